@@ -1,0 +1,236 @@
+"""Float64 CPU oracle of the HSTU layer forward -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the package's smoke check and the benchmark's CPU-baseline leg may import this
+module.  The HIP library never calls it, and it imports nothing from the library: it depends on
+numpy alone.  Inputs are the exact storage values (bf16 or fp32) upcast to float64.
+
+Sources (the pages):
+  [HSTU]   "Actions Speak Louder than Words: Trillion-Parameter Sequential Transducers for
+           Generative Recommendations" -- abstract: HSTU is an attention variant for
+           high-cardinality, non-stationary streaming data; 8192-length sequences.
+  [DLRMv4] "DLRMv4：MLPerfの推薦システム訓練ベンチマークがシーケンス化時代へ"
+           - section "モデルアーキテクチャ：HSTUが従来の特徴インタラクションスタックに取って代わる"
+             (Model architecture): inside a layer, one projection makes every internal
+             representation; pointwise attention aggregates the sequence with a bias from the
+             positional and the temporal distance of two events; a gated transformation lets the
+             aggregated features interact and takes the place of cross network and feed-forward.
+           - section "1つの訓練サンプルがHSTUでどのように処理されるか" (one training sample):
+             a time-ordered per-user event stream, candidates appended at the end and scored in
+             one forward pass, the whole sequence processed as one causal block.
+
+The pages give the structure but no formulas.  The formulas below are the plainest reading of it
+(each reading is listed with its alternatives in the design notes of this repository):
+  1. z = W1 x + b1; SiLU on all of z; U | V | Q | K are the four consecutive H*Dh slices, head-major.
+  2. s_ij = q_i . k_j + w_p[bp(i,j)] + w_t[bt(i,j)]   (no 1/sqrt(Dh) scale)
+       bp = min(|pos(i) - pos(j)|, P-1);  bt = min(bitlen(|tau_i - tau_j|), Tb-1), exact integers,
+       bitlen(0) = 0, bitlen(g) = floor(log2 g) + 1.
+     a_ij = SiLU(s_ij) on allowed pairs, 0 elsewhere.  No softmax.
+  3. O_i = c_b * sum_j a_ij v_j,  c_b = 1/n_b unless given per sequence.
+  4. y = x + W2 (LN(concat_h O) * U) + b2; LN over H*Dh, biased variance, no affine, eps given;
+     between stacked layers y <- LN(y).
+Masks: CAUSAL allows j <= i.  CAUSAL_CANDIDATES (the last m_b tokens of a sequence are candidates,
+n_h = n_b - m_b): a history row i < n_h allows j <= i; a candidate row allows every j < n_h and j = i;
+every candidate has position n_h.
+
+Functions whose result has no independent pin are marked "parity unpinned" in their docstring.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+CAUSAL = 0
+CAUSAL_CANDIDATES = 1
+
+_ROW_BLOCK = 1024
+
+
+# --------------------------------------------------------------------------- elementwise pieces
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z) = z / (1 + e^-z), float64.  e^-z may overflow to inf for z << 0,
+    which gives the correct limit -0."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def abs_diff_u64(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """|a - b| for int64 a, b as exact uint64 (the true difference always fits in 64 unsigned bits;
+    unsigned subtraction of the larger minus the smaller is exact modulo 2**64)."""
+    a, b = np.broadcast_arrays(np.asarray(a, dtype=np.int64), np.asarray(b, dtype=np.int64))
+    au, bu = a.view(np.uint64), b.view(np.uint64)
+    return np.where(a >= b, au - bu, bu - au).astype(np.uint64)
+
+
+def bitlen_u64(g: np.ndarray) -> np.ndarray:
+    """Number of significant bits of unsigned 64-bit integers (0 -> 0), by binary lifting."""
+    x = np.array(g, dtype=np.uint64, copy=True)
+    n = np.zeros(x.shape, dtype=np.int64)
+    for s in (32, 16, 8, 4, 2, 1):
+        big = x >= np.uint64(1 << s)
+        n[big] += s
+        x[big] >>= np.uint64(s)
+    return n + (x > 0)
+
+
+def position_bucket(pos_i: np.ndarray, pos_j: np.ndarray, P: int) -> np.ndarray:
+    """bp = min(|pos_i - pos_j|, P - 1) (position distance, [DLRMv4] Model architecture)."""
+    return np.minimum(np.abs(np.asarray(pos_i, np.int64) - np.asarray(pos_j, np.int64)), P - 1)
+
+
+def time_bucket(tau_i: np.ndarray, tau_j: np.ndarray, Tb: int) -> np.ndarray:
+    """bt = min(bitlen(|tau_i - tau_j|), Tb - 1): log2 buckets of the time gap, exact in integers
+    (temporal distance, [DLRMv4] Model architecture)."""
+    return np.minimum(bitlen_u64(abs_diff_u64(tau_i, tau_j)), Tb - 1)
+
+
+def positions(n: int, n_hist: int, mask: int) -> np.ndarray:
+    """Token positions inside a sequence: i for CAUSAL; min(i, n_h) for CAUSAL_CANDIDATES."""
+    i = np.arange(n, dtype=np.int64)
+    return i if mask == CAUSAL else np.minimum(i, n_hist)
+
+
+def allowed(rows: np.ndarray, n: int, n_hist: int, mask: int) -> np.ndarray:
+    """Boolean [len(rows), n]: which (i, j) pairs contribute ([DLRMv4] one training sample: one causal
+    block; candidates appended at the end see the full history)."""
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.arange(n, dtype=np.int64)[None, :]
+    if mask == CAUSAL:
+        return j <= i
+    hist_row = (i < n_hist) & (j <= i)
+    cand_row = (i >= n_hist) & ((j < n_hist) | (j == i))
+    return hist_row | cand_row
+
+
+def layer_norm(x: np.ndarray, eps: float) -> np.ndarray:
+    """Row LayerNorm over the last axis: (x - mean) / sqrt(biased var + eps), no affine."""
+    x = np.asarray(x, dtype=np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps)
+
+
+# --------------------------------------------------------------------------- attention
+def attn_sequence_head(q, k, v, tau, wp, wt, mask, n_hist, scale, rows=None):
+    """Pointwise attention for one sequence and one head.
+
+    q, k, v: [n, Dh] float64; tau: int64 [n]; wp: [P]; wt: [Tb]; returns O[rows]: [len(rows), Dh].
+    Steps 2 and 3 of the layer ([DLRMv4] Model architecture: pointwise attention with a
+    position/time-distance bias; [HSTU] abstract: attention variant, no softmax normaliser here).
+    """
+    n = q.shape[0]
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    P, Tb = len(wp), len(wt)
+    pos = positions(n, n_hist, mask)
+    out = np.zeros((len(rows), v.shape[1]), dtype=np.float64)
+    for s in range(0, len(rows), _ROW_BLOCK):
+        r = rows[s:s + _ROW_BLOCK]
+        scores = q[r] @ k.T
+        scores = scores + wp[position_bucket(pos[r][:, None], pos[None, :], P)]
+        scores = scores + wt[time_bucket(tau[r][:, None], tau[None, :], Tb)]
+        a = np.where(allowed(r, n, n_hist, mask), silu(scores), 0.0)
+        out[s:s + _ROW_BLOCK] = scale * (a @ v)
+    return out
+
+
+def _seq_params(jag, b):
+    o0, o1 = int(jag["seq_offsets"][b]), int(jag["seq_offsets"][b + 1])
+    n = o1 - o0
+    mask = int(jag.get("mask", CAUSAL))
+    m = 0
+    if mask == CAUSAL_CANDIDATES:
+        m = int(jag["num_candidates"][b])
+    n_hist = n - m
+    sc = jag.get("attn_scale")
+    scale = (1.0 / n if n else 0.0) if sc is None else float(sc[b])
+    return o0, o1, n, n_hist, mask, scale
+
+
+def attn_fwd(jag: dict, q, k, v, pos_bias, time_bias, row_sample=None):
+    """O = attention output [T, H, Dh] in float64.
+
+    jag: dict with seq_offsets int [B+1], timestamps int64 [T], mask, num_candidates [B] (candidates
+    mask only), attn_scale [B] or None.  q, k, v: [T, H, Dh]; pos_bias [R, P]; time_bias [R, Tb]
+    (R = 1 shared by all heads, or R = H, one row per head).
+    row_sample: optional dict b -> local row indices; then only those rows are computed and the
+    result is a dict (b, h) -> [rows, Dh].
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    wp = np.asarray(pos_bias, np.float64)
+    wt = np.asarray(time_bias, np.float64)
+    tau = np.asarray(jag["timestamps"], np.int64)
+    T, H, Dh = q.shape
+    B = len(jag["seq_offsets"]) - 1
+    R = wp.shape[0]
+    out = {} if row_sample is not None else np.zeros((T, H, Dh), dtype=np.float64)
+    for b in range(B):
+        o0, o1, n, n_hist, mask, scale = _seq_params(jag, b)
+        if n == 0:
+            continue
+        if row_sample is not None and b not in row_sample:
+            continue
+        for h in range(H):
+            r = 0 if R == 1 else h
+            rows = None if row_sample is None else row_sample[b]
+            o = attn_sequence_head(q[o0:o1, h], k[o0:o1, h], v[o0:o1, h], tau[o0:o1], wp[r], wt[r],
+                                   mask, n_hist, scale, rows)
+            if row_sample is None:
+                out[o0:o1, h] = o
+            else:
+                out[(b, h)] = o
+    return out
+
+
+# --------------------------------------------------------------------------- layer, stack, gather
+def projection(x, w_uvqk, b_uvqk, num_heads, head_dim):
+    """Step 1 ([DLRMv4] Model architecture: a single projection makes all internal representations):
+    SiLU(x W1^T + b1), split into U, V, Q, K, each [T, H, Dh]."""
+    x = np.asarray(x, np.float64)
+    z = x @ np.asarray(w_uvqk, np.float64).T
+    if b_uvqk is not None:
+        z = z + np.asarray(b_uvqk, np.float64)
+    z = silu(z)
+    T = x.shape[0]
+    hd = num_heads * head_dim
+    u, v, q, k = (z[:, c * hd:(c + 1) * hd].reshape(T, num_heads, head_dim) for c in range(4))
+    return u, v, q, k
+
+
+def norm_gate(o, u, eps):
+    """Step 4a ([DLRMv4] Model architecture: gated transformation): LN(concat_h O) * U, [T, H*Dh]."""
+    T = o.shape[0]
+    return layer_norm(o.reshape(T, -1), eps) * np.asarray(u, np.float64).reshape(T, -1)
+
+
+def layer_fwd(x, jag, w_uvqk, b_uvqk, w_out, b_out, pos_bias, time_bias, num_heads, head_dim,
+              ln_eps, ln_output, return_parts=False):
+    """One HSTU layer: projection, pointwise attention, norm-gate, output projection and residual
+    (plus the post-layer LayerNorm when ln_output)."""
+    x = np.asarray(x, np.float64)
+    u, v, q, k = projection(x, w_uvqk, b_uvqk, num_heads, head_dim)
+    o = attn_fwd(jag, q, k, v, pos_bias, time_bias)
+    g = norm_gate(o, u, ln_eps)
+    y = x + g @ np.asarray(w_out, np.float64).T
+    if b_out is not None:
+        y = y + np.asarray(b_out, np.float64)
+    if ln_output:
+        y = layer_norm(y, ln_eps)
+    if return_parts:
+        return y, dict(u=u, v=v, q=q, k=k, o=o, g=g)
+    return y
+
+
+def stack_fwd(x, jag, layers, num_heads, head_dim):
+    """A stack of layers; every layer but the last ends with the post-layer LayerNorm.
+    layers: list of dicts with w_uvqk, b_uvqk, w_out, b_out, pos_bias, time_bias, ln_eps."""
+    y = np.asarray(x, np.float64)
+    for li, L in enumerate(layers):
+        y = layer_fwd(y, jag, L["w_uvqk"], L.get("b_uvqk"), L["w_out"], L.get("b_out"), L["pos_bias"],
+                      L["time_bias"], num_heads, head_dim, L["ln_eps"], ln_output=li < len(layers) - 1)
+    return y
+
+
+def gather_rows(table, ids):
+    """X0[t] = E[id_t] (embedding lookup, [DLRMv4] Model architecture)."""
+    return np.asarray(table)[np.asarray(ids, np.int64)]
