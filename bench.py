@@ -1,0 +1,190 @@
+"""Benchmark of the HSTU attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--extended]
+
+A step is one hstu_attn_fwd call (QK^T, bias, SiLU, mask and AV of every allowed pair) over the
+L = 8192 workload: 8 sequences of 8192 events, 4 heads x 128, P = Tb = 256 bias buckets, causal,
+bf16 with fp32 accumulation; inputs are resident in HBM before the timed region.  The FLOP count
+covers allowed (causal, non-padded) pairs only: sum_b H * n_b (n_b + 1) / 2 * 4 * Dh.
+
+Prints one JSON line.  `roofline` compares the kernel's average duration (HIP events on the stream
+it runs on) with the MI355X dense bf16 MFMA peak; `cpu_baseline` times the float64 oracle on a
+bounded sample of the same workload on the host cores.  --extended also prints, to stderr, the
+per-config timings of the other workloads (layer, stack, candidate-masked forward).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0          # MI355X dense bf16 MFMA (no sparsity)
+HBM_PEAK_GBS = 8000.0
+METRIC = "HSTU attn fwd TFLOP/s (causal, jagged) at L=8192 bf16; % MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_L8192_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "hstu_sequential_transduction_attn_amd", "csrc", "attn_fwd.hip")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel source (else None)."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float = 12.0):
+    """Time the float64 oracle on whole 1024-row query blocks of the workload until ~budget_s."""
+    from oracle import hstu_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    j = case.jagged
+    jag = dict(seq_offsets=j.seq_offsets.astype(np.int64), timestamps=j.timestamps, mask=j.mask,
+               num_candidates=j.num_candidates, attn_scale=j.attn_scale)
+    q, k, v = case.q.values, case.k.values, case.v.values
+    flops, done, t0 = 0, [], time.perf_counter()
+    blocks = [(0, 0, r0) for r0 in range(7168, -1, -1024)]        # sequence 0, head 0, last blocks first
+    for b, h, r0 in blocks:
+        rows = {b: np.arange(r0, r0 + 1024)}
+        O.attn_fwd(jag, q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], case.rab.pos_bias, case.rab.time_bias,
+                   row_sample=rows)
+        flops += int(sum(i + 1 for i in range(r0, r0 + 1024))) * 4 * case.head_dim
+        done.append(r0)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"float64 oracle, sequence 0 head 0, query rows [{min(done)}, {max(done) + 1024}) "
+                      f"against all their causal keys ({flops:.3e} FLOP in {dt:.1f} s; BLAS matmuls on "
+                      f"{blas_threads} threads, bucket and SiLU work single-threaded)"}
+
+
+def run(args):
+    import torch
+    from hstu_sequential_transduction_attn_amd import configs as C
+    from hstu_sequential_transduction_attn_amd import _lib as ops
+
+    ops.load_library()  # fails loudly without the HIP library
+    dev = torch.device("cuda:0")
+    case = C.attn_L8192()
+    j = case.jagged
+
+    def t(x):
+        if x.dtype == "bf16":
+            return torch.from_numpy(x.bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x.values).to(dev)
+    q, k, v = t(case.q), t(case.k), t(case.v)
+    offs = torch.from_numpy(j.seq_offsets.astype(np.int32)).to(dev)
+    tau = torch.from_numpy(j.timestamps).to(dev)
+    wp = torch.from_numpy(case.rab.pos_bias).to(dev)
+    wt = torch.from_numpy(case.rab.time_bias).to(dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ops.attn_fwd(offs, tau, q, k, v, wp, wt, max_seq_len=j.max_seq_len, out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+
+    flop = case.flops()
+    tflops = flop * args.steps / wall / 1e12
+    achieved = flop / (kernel_ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "attn_L8192: hstu_attn_fwd, 8 jagged sequences x 8192 events, H=4, Dh=128, "
+                               "P=Tb=256, causal, bf16 in/out, fp32 accumulation",
+                   "global_batch": j.num_seqs, "seq_len": j.max_seq_len, "tokens": j.total_tokens,
+                   "flop_per_step": flop, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(), "kernel_ms": round(kernel_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(rec), flush=True)
+    if args.extended:
+        extended(args, dev)
+
+
+def extended(args, dev):
+    """Per-workload timings of the layer path (stderr, informational)."""
+    import torch
+    from hstu_sequential_transduction_attn_amd import configs as C
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from _util import gpu_layer_stack  # noqa: E402
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / reps * 1e3
+    for name, mk, kw in [("layer_bf16", C.layer_bf16, {}),
+                         ("stack8_bf16", C.stack8_bf16, dict(use_gather=True, residual_f32=True, act_split=True)),
+                         ("mfalcon_bf16", C.mfalcon_bf16, dict(use_gather=True, residual_f32=True))]:
+        case = mk()
+        ms = timed(lambda: gpu_layer_stack(case, **kw))
+        print(f"[extended] {name}: {ms:.2f} ms per forward (incl. host-side weight upload)", file=sys.stderr,
+              flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extended", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the attention forward of one GPU's share is the measured "
+              f"unit (--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

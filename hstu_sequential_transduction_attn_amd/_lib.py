@@ -1,0 +1,194 @@
+"""ctypes binding of libhstu (include/hstu.h): argument marshalling only.
+
+Every computation runs in the HIP library; this module turns torch tensors into device
+pointers, fills the C structs, allocates the caller-owned workspace and raises on a non-OK
+status.  It never falls back to another implementation: if the library is missing, the first
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libhstu.so")
+HEADER_PATH = os.path.join(PKG_DIR, "..", "include", "hstu.h")
+
+HSTU_F32, HSTU_BF16 = 0, 1
+MASK_CAUSAL, MASK_CAUSAL_CANDIDATES = 0, 1
+
+c_i32, c_i64, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class HstuError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name}: {detail}")
+        self.status = status
+        self.name = name
+        self.detail = detail
+
+
+class JaggedT(ctypes.Structure):
+    _fields_ = [("num_seqs", c_i32), ("total_tokens", c_i32), ("max_seq_len", c_i32),
+                ("seq_offsets", c_vp), ("timestamps", c_vp), ("num_candidates", c_vp), ("attn_scale", c_vp)]
+
+
+class AttnDescT(ctypes.Structure):
+    _fields_ = [("num_heads", c_i32), ("head_dim", c_i32), ("num_pos_buckets", c_i32), ("num_time_buckets", c_i32),
+                ("rab_rows", c_i32), ("pos_bias", c_vp), ("time_bias", c_vp), ("mask", c_i32)]
+
+
+class LayerWeightsT(ctypes.Structure):
+    _fields_ = [("d_model", c_i32), ("w_uvqk", c_vp), ("b_uvqk", c_vp), ("w_out", c_vp), ("b_out", c_vp),
+                ("ln_eps", c_f32), ("ln_output", c_i32), ("act_split", c_i32)]
+
+
+_lib = None
+
+
+def exported_functions_in_header(path: str = HEADER_PATH):
+    """Names of the functions that include/hstu.h declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hstu_[a-z0-9_]+)\s*\(", text)))
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libhstu.so and declare its signatures (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libhstu.so not found at {p}: build it with "
+                           "`python -m hstu_sequential_transduction_attn_amd.build`")
+    lib = ctypes.CDLL(p)
+    lib.hstu_abi_version.restype = ctypes.c_int
+    lib.hstu_abi_version.argtypes = []
+    lib.hstu_status_string.restype = ctypes.c_char_p
+    lib.hstu_status_string.argtypes = [ctypes.c_int]
+    lib.hstu_last_error.restype = ctypes.c_char_p
+    lib.hstu_last_error.argtypes = []
+    lib.hstu_attn_workspace_bytes.restype = c_sz
+    lib.hstu_attn_workspace_bytes.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT), ctypes.c_int]
+    lib.hstu_attn_fwd.restype = ctypes.c_int
+    lib.hstu_attn_fwd.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT), ctypes.c_int, c_vp, c_vp, c_vp,
+                                  c_vp, ctypes.c_int, c_vp, c_sz, c_vp]
+    lib.hstu_layer_workspace_bytes.restype = c_sz
+    lib.hstu_layer_workspace_bytes.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT),
+                                               ctypes.POINTER(LayerWeightsT), ctypes.c_int]
+    lib.hstu_layer_fwd.restype = ctypes.c_int
+    lib.hstu_layer_fwd.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT), ctypes.POINTER(LayerWeightsT),
+                                   ctypes.c_int, ctypes.c_int, c_vp, ctypes.c_int, c_vp, c_vp, c_sz, c_vp]
+    lib.hstu_gather_rows.restype = ctypes.c_int
+    lib.hstu_gather_rows.argtypes = [c_vp, c_i64, c_i32, ctypes.c_int, c_vp, c_i32, c_vp, c_vp]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = load_library()
+        raise HstuError(status, lib.hstu_status_string(status).decode(), lib.hstu_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return HSTU_BF16
+    if t.dtype == torch.float32:
+        return HSTU_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_jagged(seq_offsets: torch.Tensor, timestamps: torch.Tensor, max_seq_len: int,
+                num_candidates: Optional[torch.Tensor] = None, attn_scale: Optional[torch.Tensor] = None) -> JaggedT:
+    B = seq_offsets.numel() - 1
+    return JaggedT(B, timestamps.numel(), int(max_seq_len), _ptr(seq_offsets), _ptr(timestamps),
+                   _ptr(num_candidates), _ptr(attn_scale))
+
+
+def make_desc(num_heads: int, head_dim: int, pos_bias: torch.Tensor, time_bias: torch.Tensor,
+              mask: int = MASK_CAUSAL) -> AttnDescT:
+    R, P = pos_bias.shape
+    Tb = time_bias.shape[1]
+    return AttnDescT(num_heads, head_dim, P, Tb, R, _ptr(pos_bias), _ptr(time_bias), int(mask))
+
+
+def attn_fwd(seq_offsets, timestamps, q, k, v, pos_bias, time_bias, *, max_seq_len: int, mask: int = MASK_CAUSAL,
+             num_candidates=None, attn_scale=None, out_dtype: Optional[torch.dtype] = None, out=None, stream=None):
+    """O = hstu_attn_fwd(...): q, k, v [T, H, Dh] (bf16 or f32, contiguous); returns out [T, H, Dh]."""
+    lib = load_library()
+    T, H, Dh = q.shape
+    if out is None:
+        out = torch.empty((T, H, Dh), dtype=out_dtype or q.dtype, device=q.device)
+    jag = make_jagged(seq_offsets, timestamps, max_seq_len, num_candidates, attn_scale)
+    desc = make_desc(H, Dh, pos_bias, time_bias, mask)
+    dt = _dtype_code(q)
+    nws = lib.hstu_attn_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), dt)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device) if nws else None
+    _check(lib.hstu_attn_fwd(ctypes.byref(jag), ctypes.byref(desc), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                             _dtype_code(out), _ptr(ws), nws, _stream(stream)))
+    return out
+
+
+def layer_workspace_bytes(x, seq_offsets, timestamps, w_uvqk, w_out, pos_bias, time_bias, num_heads, head_dim, *,
+                          max_seq_len, ln_output=False, mask=MASK_CAUSAL, act_split=False) -> int:
+    lib = load_library()
+    jag = make_jagged(seq_offsets, timestamps, max_seq_len)
+    desc = make_desc(num_heads, head_dim, pos_bias, time_bias, mask)
+    w = LayerWeightsT(x.shape[1], _ptr(w_uvqk), None, _ptr(w_out), None, 1e-6, int(bool(ln_output)),
+                      int(bool(act_split)))
+    return int(lib.hstu_layer_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w),
+                                              _dtype_code(w_uvqk)))
+
+
+def layer_fwd(x, seq_offsets, timestamps, w_uvqk, w_out, pos_bias, time_bias, num_heads: int, head_dim: int, *,
+              max_seq_len: int, b_uvqk=None, b_out=None, ln_eps: float = 1e-6, ln_output: bool = False,
+              mask: int = MASK_CAUSAL, num_candidates=None, attn_scale=None, y_dtype: Optional[torch.dtype] = None,
+              act_split: bool = False, workspace=None, y=None, stream=None):
+    """y = hstu_layer_fwd(...): x [T, D] (fp32 or the weights' dtype); returns y [T, D] in y_dtype
+    (default: x's dtype).  The weights' dtype (bf16 or f32) sets the MFMA operand type."""
+    lib = load_library()
+    T, D = x.shape
+    if y is None:
+        y = torch.empty((T, D), dtype=y_dtype or x.dtype, device=x.device)
+    jag = make_jagged(seq_offsets, timestamps, max_seq_len, num_candidates, attn_scale)
+    desc = make_desc(num_heads, head_dim, pos_bias, time_bias, mask)
+    w = LayerWeightsT(D, _ptr(w_uvqk), _ptr(b_uvqk), _ptr(w_out), _ptr(b_out), float(ln_eps), int(bool(ln_output)),
+                      int(bool(act_split)))
+    dt = _dtype_code(w_uvqk)
+    nws = int(lib.hstu_layer_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), dt))
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device)
+    _check(lib.hstu_layer_fwd(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), dt, _dtype_code(x), _ptr(x),
+                              _dtype_code(y), _ptr(y), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return y
+
+
+def gather_rows(table: torch.Tensor, ids: torch.Tensor, out=None, stream=None):
+    """out[t] = table[ids[t]] (hstu_gather_rows)."""
+    lib = load_library()
+    rows, d = table.shape
+    T = ids.numel()
+    if out is None:
+        out = torch.empty((T, d), dtype=table.dtype, device=table.device)
+    _check(lib.hstu_gather_rows(_ptr(table), rows, d, _dtype_code(table), _ptr(ids), T, _ptr(out), _stream(stream)))
+    return out
+
+
+def abi_version() -> int:
+    return int(load_library().hstu_abi_version())

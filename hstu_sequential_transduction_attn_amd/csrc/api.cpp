@@ -1,0 +1,304 @@
+// C-ABI entry points of libhstu: argument validation, workspace layout, kernel dispatch.
+// Declarations and the contract of every entry point are in include/hstu.h.
+#include "../../include/hstu.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hstu_status_t fail(hstu_status_t st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+hstu_status_t ok() {
+  g_last_error.clear();
+  return HSTU_OK;
+}
+
+hstu_status_t from_hip(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(HSTU_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t esize(hstu_dtype_t d) { return d == HSTU_BF16 ? 2 : 4; }
+bool valid_dtype(hstu_dtype_t d) { return d == HSTU_F32 || d == HSTU_BF16; }
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+hstu_status_t check_jagged_desc(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc) {
+  if (!jag) return fail(HSTU_ERR_INVALID_ARGUMENT, "jag is NULL");
+  if (!desc) return fail(HSTU_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (jag->num_seqs < 0) return fail(HSTU_ERR_INVALID_ARGUMENT, "num_seqs = %d < 0", jag->num_seqs);
+  if (jag->total_tokens < 0) return fail(HSTU_ERR_INVALID_ARGUMENT, "total_tokens = %d < 0", jag->total_tokens);
+  if (jag->max_seq_len < 0 || jag->max_seq_len > jag->total_tokens)
+    return fail(HSTU_ERR_INVALID_ARGUMENT, "max_seq_len = %d outside [0, total_tokens = %d]", jag->max_seq_len,
+                jag->total_tokens);
+  if (jag->num_seqs > 0 && !jag->seq_offsets) return fail(HSTU_ERR_INVALID_ARGUMENT, "seq_offsets is NULL");
+  if (jag->num_seqs == 0 && jag->total_tokens != 0)
+    return fail(HSTU_ERR_INVALID_ARGUMENT, "num_seqs = 0 but total_tokens = %d", jag->total_tokens);
+  if (jag->total_tokens > 0 && !jag->timestamps) return fail(HSTU_ERR_INVALID_ARGUMENT, "timestamps is NULL");
+  if (desc->num_heads < 1) return fail(HSTU_ERR_INVALID_ARGUMENT, "num_heads = %d < 1", desc->num_heads);
+  if (desc->head_dim != 32 && desc->head_dim != 64 && desc->head_dim != 128)
+    return fail(HSTU_ERR_UNSUPPORTED, "head_dim = %d not in {32, 64, 128}", desc->head_dim);
+  if (desc->num_pos_buckets < 1 || desc->num_pos_buckets > 4096)
+    return fail(HSTU_ERR_INVALID_ARGUMENT, "num_pos_buckets = %d outside [1, 4096]", desc->num_pos_buckets);
+  if (desc->num_time_buckets < 1 || desc->num_time_buckets > 4096)
+    return fail(HSTU_ERR_INVALID_ARGUMENT, "num_time_buckets = %d outside [1, 4096]", desc->num_time_buckets);
+  if (desc->rab_rows != 1 && desc->rab_rows != desc->num_heads)
+    return fail(HSTU_ERR_INVALID_ARGUMENT, "rab_rows = %d is neither 1 nor num_heads = %d", desc->rab_rows,
+                desc->num_heads);
+  if (!desc->pos_bias || !desc->time_bias) return fail(HSTU_ERR_INVALID_ARGUMENT, "pos_bias/time_bias is NULL");
+  if (desc->mask != HSTU_MASK_CAUSAL && desc->mask != HSTU_MASK_CAUSAL_CANDIDATES)
+    return fail(HSTU_ERR_INVALID_ARGUMENT, "mask = %d is not a hstu_mask_t", (int)desc->mask);
+  if (desc->mask == HSTU_MASK_CAUSAL_CANDIDATES && jag->num_seqs > 0 && !jag->num_candidates)
+    return fail(HSTU_ERR_INVALID_ARGUMENT, "mask = CAUSAL_CANDIDATES needs num_candidates");
+  const long long hd = (long long)desc->num_heads * desc->head_dim;
+  if (hd > 4096) return fail(HSTU_ERR_UNSUPPORTED, "num_heads * head_dim = %lld > 4096", hd);
+  const long long blocks = ((long long)jag->max_seq_len + 127) / 128 * desc->num_heads * jag->num_seqs;
+  if (blocks > 0x7fffffffLL) return fail(HSTU_ERR_UNSUPPORTED, "launch too large (%lld workgroups)", blocks);
+  return HSTU_OK;
+}
+
+hstu::AttnArgs attn_args(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc) {
+  hstu::AttnArgs a{};
+  a.seq_offsets = jag->seq_offsets;
+  a.timestamps = jag->timestamps;
+  a.num_candidates = desc->mask == HSTU_MASK_CAUSAL_CANDIDATES ? jag->num_candidates : nullptr;
+  a.attn_scale = jag->attn_scale;
+  a.pos_bias = desc->pos_bias;
+  a.time_bias = desc->time_bias;
+  a.num_seqs = jag->num_seqs;
+  a.num_heads = desc->num_heads;
+  a.head_dim = desc->head_dim;
+  a.max_seq_len = jag->max_seq_len;
+  a.num_pos_buckets = desc->num_pos_buckets;
+  a.num_time_buckets = desc->num_time_buckets;
+  a.rab_rows = desc->rab_rows;
+  a.mask = desc->mask == HSTU_MASK_CAUSAL_CANDIDATES ? hstu::kCausalCandidates : hstu::kCausal;
+  return a;
+}
+
+// Layer workspace regions, each 256-byte aligned: U ([T][HD] fp32), V, Q, K ([T][HD] dtype),
+// O ([T][HD] fp32), G ([T][HD], fp32 when the gate stays fp32 for the output GEMM, else dtype),
+// Y32 ([T][D] fp32, only when ln_output).
+struct LayerWs {
+  size_t u, v, q, k, o, g, y32, total;
+  bool g_f32;
+};
+
+LayerWs layer_ws(int64_t T, int64_t HD, int64_t D, hstu_dtype_t dt, bool ln_output, bool split) {
+  LayerWs w{};
+  w.g_f32 = dt == HSTU_F32 || split;
+  const size_t part = round_up((size_t)T * HD * esize(dt), 256);
+  const size_t part32 = round_up((size_t)T * HD * 4, 256);
+  size_t off = 0;
+  w.u = off; off += part32;
+  w.v = off; off += part;
+  w.q = off; off += part;
+  w.k = off; off += part;
+  w.o = off; off += part32;
+  w.g = off; off += w.g_f32 ? part32 : part;
+  w.y32 = off; off += ln_output ? round_up((size_t)T * D * 4, 256) : 0;
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hstu_abi_version(void) { return HSTU_ABI_VERSION; }
+
+const char *hstu_status_string(hstu_status_t s) {
+  switch (s) {
+    case HSTU_OK: return "HSTU_OK";
+    case HSTU_ERR_INVALID_ARGUMENT: return "HSTU_ERR_INVALID_ARGUMENT";
+    case HSTU_ERR_UNSUPPORTED: return "HSTU_ERR_UNSUPPORTED";
+    case HSTU_ERR_WORKSPACE_TOO_SMALL: return "HSTU_ERR_WORKSPACE_TOO_SMALL";
+    case HSTU_ERR_DEVICE: return "HSTU_ERR_DEVICE";
+  }
+  return "HSTU_STATUS_UNKNOWN";
+}
+
+const char *hstu_last_error(void) { return g_last_error.c_str(); }
+
+size_t hstu_attn_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, hstu_dtype_t in_dtype) {
+  (void)jag;
+  (void)desc;
+  (void)in_dtype;
+  return 0;
+}
+
+hstu_status_t hstu_attn_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, hstu_dtype_t in_dtype,
+                            const void *q, const void *k, const void *v, void *out, hstu_dtype_t out_dtype,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  try {
+    hstu_status_t st = check_jagged_desc(jag, desc);
+    if (st != HSTU_OK) return st;
+    if (!valid_dtype(in_dtype)) return fail(HSTU_ERR_INVALID_ARGUMENT, "in_dtype = %d invalid", (int)in_dtype);
+    if (!valid_dtype(out_dtype)) return fail(HSTU_ERR_INVALID_ARGUMENT, "out_dtype = %d invalid", (int)out_dtype);
+    if (in_dtype == HSTU_F32 && out_dtype != HSTU_F32)
+      return fail(HSTU_ERR_UNSUPPORTED, "f32 inputs need an f32 output");
+    const size_t need = hstu_attn_workspace_bytes(jag, desc, in_dtype);
+    if (workspace_bytes < need)
+      return fail(HSTU_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+    if (need > 0 && !workspace) return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    const int64_t T = jag->total_tokens;
+    if (T == 0) return ok();
+    if (!q || !k || !v || !out) return fail(HSTU_ERR_INVALID_ARGUMENT, "q/k/v/out is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "q/k/v/out must be 16-byte aligned");
+    const size_t nin = (size_t)T * desc->num_heads * desc->head_dim * esize(in_dtype);
+    const size_t nout = (size_t)T * desc->num_heads * desc->head_dim * esize(out_dtype);
+    if (overlaps(out, nout, q, nin) || overlaps(out, nout, k, nin) || overlaps(out, nout, v, nin))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "out overlaps q, k or v");
+    hstu::AttnArgs a = attn_args(jag, desc);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.row_stride = (int64_t)desc->num_heads * desc->head_dim;
+    a.out_row_stride = a.row_stride;
+    a.in_dtype = in_dtype == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
+    a.out_dtype = out_dtype == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
+    return from_hip(hstu::launch_attn_fwd(a, (hipStream_t)stream), "attn_fwd launch");
+  } catch (...) {
+    return fail(HSTU_ERR_DEVICE, "unexpected C++ exception in hstu_attn_fwd");
+  }
+}
+
+size_t hstu_layer_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc,
+                                  const hstu_layer_weights_t *w, hstu_dtype_t dtype) {
+  if (!jag || !desc || !w || jag->total_tokens < 0 || desc->num_heads < 1 || desc->head_dim < 1 || w->d_model < 1)
+    return 0;
+  return layer_ws(jag->total_tokens, (int64_t)desc->num_heads * desc->head_dim, w->d_model, dtype, w->ln_output != 0,
+                  dtype == HSTU_BF16 && w->act_split != 0)
+      .total;
+}
+
+hstu_status_t hstu_layer_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, const hstu_layer_weights_t *w,
+                             hstu_dtype_t dtype, hstu_dtype_t x_dtype, const void *x, hstu_dtype_t y_dtype, void *y,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  try {
+    hstu_status_t st = check_jagged_desc(jag, desc);
+    if (st != HSTU_OK) return st;
+    if (!w) return fail(HSTU_ERR_INVALID_ARGUMENT, "weights is NULL");
+    if (!valid_dtype(dtype)) return fail(HSTU_ERR_INVALID_ARGUMENT, "dtype = %d invalid", (int)dtype);
+    if (!valid_dtype(x_dtype) || (x_dtype != dtype && x_dtype != HSTU_F32))
+      return fail(HSTU_ERR_UNSUPPORTED, "x_dtype = %d must be HSTU_F32 or dtype", (int)x_dtype);
+    if (!valid_dtype(y_dtype) || (y_dtype != dtype && y_dtype != HSTU_F32))
+      return fail(HSTU_ERR_UNSUPPORTED, "y_dtype = %d must be HSTU_F32 or dtype", (int)y_dtype);
+    const int64_t T = jag->total_tokens;
+    const int64_t D = w->d_model;
+    const int64_t HD = (int64_t)desc->num_heads * desc->head_dim;
+    if (D < 1 || D % 8 != 0 || D > 4096)
+      return fail(HSTU_ERR_UNSUPPORTED, "d_model = %lld must be a multiple of 8 in [8, 4096]", (long long)D);
+    if (!(w->ln_eps > 0.0f)) return fail(HSTU_ERR_INVALID_ARGUMENT, "ln_eps must be > 0");
+    if (!w->w_uvqk || !w->w_out) return fail(HSTU_ERR_INVALID_ARGUMENT, "w_uvqk/w_out is NULL");
+    if (!aligned16(w->w_uvqk) || !aligned16(w->w_out))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "weights must be 16-byte aligned");
+    const bool split = dtype == HSTU_BF16 && w->act_split != 0;
+    const LayerWs ws = layer_ws(T, HD, D, dtype, w->ln_output != 0, split);
+    if (workspace_bytes < ws.total)
+      return fail(HSTU_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, ws.total);
+    if (T == 0) return ok();
+    if (!x || !y) return fail(HSTU_ERR_INVALID_ARGUMENT, "x/y is NULL");
+    if (!workspace) return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if (!aligned16(x) || !aligned16(y) || !aligned16(workspace))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "x/y/workspace must be 16-byte aligned");
+    const size_t nx = (size_t)T * D * esize(x_dtype), ny = (size_t)T * D * esize(y_dtype);
+    if (overlaps(x, nx, y, ny)) return fail(HSTU_ERR_INVALID_ARGUMENT, "y overlaps x");
+    if (overlaps(workspace, ws.total, x, nx) || overlaps(workspace, ws.total, y, ny))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace overlaps x or y");
+
+    hipStream_t s = (hipStream_t)stream;
+    char *wsb = (char *)workspace;
+    const int dt = dtype == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
+    const int x_f32 = x_dtype == HSTU_F32, y_f32 = y_dtype == HSTU_F32;
+
+    hstu::GemmUvqkArgs g1{};
+    g1.x = x; g1.w = w->w_uvqk; g1.bias = w->b_uvqk;
+    g1.u = (float *)(wsb + ws.u); g1.v = wsb + ws.v; g1.q = wsb + ws.q; g1.k = wsb + ws.k;
+    g1.M = (int32_t)T; g1.K = (int32_t)D; g1.HD = (int32_t)HD;
+    g1.dtype = dt; g1.x_f32 = x_f32; g1.split = split;
+    hipError_t e = hstu::launch_gemm_uvqk(g1, s);
+    if (e != hipSuccess) return from_hip(e, "projection GEMM launch");
+
+    hstu::AttnArgs a = attn_args(jag, desc);
+    a.q = wsb + ws.q; a.k = wsb + ws.k; a.v = wsb + ws.v; a.out = wsb + ws.o;
+    a.row_stride = HD; a.out_row_stride = HD;
+    a.in_dtype = dt; a.out_dtype = hstu::kF32;
+    e = hstu::launch_attn_fwd(a, s);
+    if (e != hipSuccess) return from_hip(e, "attention launch");
+
+    hstu::NormGateArgs ng{};
+    ng.o = (const float *)(wsb + ws.o); ng.u = (const float *)(wsb + ws.u); ng.g = wsb + ws.g;
+    ng.M = (int32_t)T; ng.HD = (int32_t)HD; ng.eps = w->ln_eps; ng.dtype = dt; ng.g_f32 = ws.g_f32;
+    e = hstu::launch_norm_gate(ng, s);
+    if (e != hipSuccess) return from_hip(e, "norm-gate launch");
+
+    hstu::GemmOutArgs g2{};
+    g2.g = wsb + ws.g; g2.w = w->w_out; g2.bias = w->b_out; g2.x = x;
+    g2.y = y; g2.y32 = w->ln_output ? (float *)(wsb + ws.y32) : nullptr;
+    g2.M = (int32_t)T; g2.N = (int32_t)D; g2.K = (int32_t)HD;
+    g2.dtype = dt; g2.g_f32 = ws.g_f32; g2.split = split; g2.x_f32 = x_f32; g2.y_f32 = y_f32;
+    e = hstu::launch_gemm_out(g2, s);
+    if (e != hipSuccess) return from_hip(e, "output GEMM launch");
+
+    if (w->ln_output) {
+      hstu::RowLnArgs ln{};
+      ln.in = (const float *)(wsb + ws.y32); ln.out = y; ln.M = (int32_t)T; ln.N = (int32_t)D;
+      ln.eps = w->ln_eps; ln.out_f32 = y_f32;
+      e = hstu::launch_row_layernorm(ln, s);
+      if (e != hipSuccess) return from_hip(e, "output LayerNorm launch");
+    }
+    return ok();
+  } catch (...) {
+    return fail(HSTU_ERR_DEVICE, "unexpected C++ exception in hstu_layer_fwd");
+  }
+}
+
+hstu_status_t hstu_gather_rows(const void *table, int64_t table_rows, int32_t d, hstu_dtype_t dtype,
+                               const int64_t *ids, int32_t T, void *out, void *stream) {
+  try {
+    if (!valid_dtype(dtype)) return fail(HSTU_ERR_INVALID_ARGUMENT, "dtype = %d invalid", (int)dtype);
+    if (T < 0) return fail(HSTU_ERR_INVALID_ARGUMENT, "T = %d < 0", T);
+    if (d < 1) return fail(HSTU_ERR_INVALID_ARGUMENT, "d = %d < 1", d);
+    const int64_t row_bytes = (int64_t)d * esize(dtype);
+    if (row_bytes % 16 != 0) return fail(HSTU_ERR_UNSUPPORTED, "row of %lld bytes is not a multiple of 16",
+                                         (long long)row_bytes);
+    if (table_rows < 1) return fail(HSTU_ERR_INVALID_ARGUMENT, "table_rows = %lld < 1", (long long)table_rows);
+    if (T == 0) return ok();
+    if (!table || !ids || !out) return fail(HSTU_ERR_INVALID_ARGUMENT, "table/ids/out is NULL");
+    if (!aligned16(table) || !aligned16(out)) return fail(HSTU_ERR_INVALID_ARGUMENT, "table/out must be 16-byte aligned");
+    if (overlaps(out, (size_t)T * row_bytes, table, (size_t)table_rows * row_bytes))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "out overlaps table");
+    return from_hip(hstu::launch_gather_rows(table, table_rows, (int32_t)row_bytes, ids, T, out, (hipStream_t)stream),
+                    "gather launch");
+  } catch (...) {
+    return fail(HSTU_ERR_DEVICE, "unexpected C++ exception in hstu_gather_rows");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,420 @@
+// Jagged, causally masked pointwise attention of the HSTU layer on gfx950 (CDNA4).
+//
+//   O_i = c_b * sum_{allowed j} SiLU(q_i . k_j + w_p[bp(i,j)] + w_t[bt(i,j)]) v_j
+//   bp = min(|pos_i - pos_j|, P-1),  bt = min(bitlen(|tau_i - tau_j|), Tb-1)
+//
+// Pointwise attention with a bias from the position and the time distance of two events:
+// "DLRMv4：MLPerfの推薦システム訓練ベンチマークがシーケンス化時代へ", section "モデルアーキテクチャ".
+// One causal block per user sequence, candidates appended at the end: same page, section
+// "1つの訓練サンプルがHSTUでどのように処理されるか".  No softmax, hence no running maximum and no
+// normaliser: partial sums over key tiles simply add.
+//
+// Kernel shape.  A workgroup is 4 waves; each wave owns 32 consecutive queries of one (sequence, head),
+// so a workgroup covers 128 queries.  Key tiles of 64 rows are staged through LDS (double buffered,
+// one barrier per tile) and shared by the 4 waves.  Both contractions run on 32x32 MFMA tiles in a
+// transposed form:
+//     S^T[key][query] = K . Q^T        (A = K rows from LDS, B = Q held in registers)
+//     O^T[dh][query] += V^T . P^T      (A = V^T read with ds_read_b64_tr_b16, B = P from registers)
+// The score accumulator of the first product is already laid out as the B operand of the second:
+// lane l always holds query l%32.  K rows are stored in LDS in a permuted order so that the keys a
+// lane holds in its 16 accumulator values are two runs of 8 consecutive keys, which is exactly the
+// k-order the second MFMA expects.  V stays in its natural [key][dh] layout; the transpose read hands
+// each lane 4 consecutive keys of one dh column.
+//
+// Per (wave, key tile) the mask and the bias are classified from index ranges and from the
+// timestamp ranges of the wave's queries and the tile's keys:
+//   none    - no allowed pair: skipped;
+//   uniform - every pair allowed and one position bucket and one time bucket for the whole tile:
+//             a single bias constant, no per-element integer work;
+//   general - per-element mask, buckets and table lookups from LDS.
+#include "device_common.hpp"
+#include "kernels.h"
+
+namespace hstu {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kQW = 32;                  // queries per wave
+constexpr int kBM = kWaves * kQW;        // queries per workgroup
+constexpr int kBN = 64;                  // keys per LDS tile
+constexpr int kThreads = kWaves * kWave;
+constexpr int kTimeTab = 65;             // a 64-bit gap has bit length 0..64
+
+// Row order of K inside each 32-row block of LDS: row r holds key kperm(r) (an involution swapping
+// rows 4..7 with 8..11 and 20..23 with 24..27).  With it, accumulator element e of lane half hf holds
+// key 16*(e/8) + 8*hf + e%8.
+__device__ __forceinline__ int kperm(int r) {
+  const int g = (r >> 2) & 7;
+  const int ng = (g == 1) ? 2 : (g == 2) ? 1 : (g == 5) ? 6 : (g == 6) ? 5 : g;
+  return (r & ~31) | (ng << 2) | (r & 3);
+}
+
+template <typename T, int DH>
+struct Layout {
+  static constexpr bool kBf16 = sizeof(T) == 2;
+  static constexpr int kES = sizeof(T);
+  static constexpr int kKStride = kBf16 ? DH * 2 + 16 : (DH + 1) * 4;   // bytes per K row in LDS
+  static constexpr int kVStride = kBf16 ? DH * 2 + 32 : DH * 4;         // bytes per V row in LDS
+  static constexpr int kChunksPerRow = DH * kES / 16;
+  static constexpr int kChunksPerThread = kBN * kChunksPerRow / kThreads;
+  static constexpr int kOffK = 0;
+  static constexpr int kOffV = kOffK + kBN * kKStride;
+  static constexpr int kOffTau = (kOffV + kBN * kVStride + 15) & ~15;
+  static constexpr int kOffStat = kOffTau + kBN * 8;
+  static constexpr int kStageBytes = kOffStat + 16;
+  static constexpr int kKPL = kBf16 ? 8 : 1;                 // operand values per lane per MFMA
+  static constexpr int kKStep = kBf16 ? 16 : 2;              // k per MFMA
+  static constexpr int kQSteps = DH / kKStep;                // MFMAs per 32x32 score block
+  static constexpr int kDB = DH / 32;                        // 32-row dh blocks of O^T
+  static_assert(kChunksPerThread >= 1 && kBN * kChunksPerRow % kThreads == 0, "staging split");
+};
+
+template <typename T> struct QFrag;
+template <> struct QFrag<__bf16> { using type = bf16x8; };
+template <> struct QFrag<float> { using type = float; };
+
+__device__ __forceinline__ int64_t shfl_xor_i64(int64_t v, int m) {
+  return __shfl_xor(v, m, kWave);
+}
+
+template <typename T, int DH, typename TO>
+// Two waves per SIMD (<= 256 registers per lane) so that one wave's MFMAs overlap the other's VALU work.
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
+  using L = Layout<T, DH>;
+  using Frag = typename QFrag<T>::type;
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  HSTU_LDS char *smem = (HSTU_LDS char *)smem_raw;
+
+  // ---- work item: query block major (longest first), then (sequence, head)
+  const int HB = p.num_heads * p.num_seqs;
+  const int item = blockIdx.x;
+  const int qblk = n_qblocks - 1 - item / HB;
+  const int b = (item % HB) / p.num_heads;
+  const int h = (item % HB) % p.num_heads;
+  const int o0 = p.seq_offsets[b];
+  const int n = p.seq_offsets[b + 1] - o0;
+  const int q0 = qblk * kBM;
+  if (q0 >= n) return;  // uniform over the workgroup
+  const bool cand = p.mask == kCausalCandidates;
+  const int nh = cand ? n - p.num_candidates[b] : n;
+  const float cb = p.attn_scale ? p.attn_scale[b] : 1.0f / (float)n;
+  const int P = p.num_pos_buckets;
+  const int Tb = p.num_time_buckets;
+  const int rr = p.rab_rows == 1 ? 0 : h;
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+
+  // ---- bias tables into LDS (after the two pipeline stages)
+  HSTU_LDS float *wp_lds = (HSTU_LDS float *)(smem + 2 * L::kStageBytes);
+  HSTU_LDS float *wt_lds = wp_lds + P;
+  for (int i = tid; i < P; i += kThreads) wp_lds[i] = p.pos_bias[(int64_t)rr * P + i];
+  const int nt_tab = imin(Tb, kTimeTab);
+  for (int i = tid; i < nt_tab; i += kThreads) wt_lds[i] = p.time_bias[(int64_t)rr * Tb + i];
+
+  // ---- this wave's queries
+  const int qa = q0 + wave * kQW;                 // first query of the wave
+  const int ql = imin(qa + kQW - 1, n - 1);       // last valid query of the wave
+  const bool wave_active = qa < n;
+  const int my_q = qa + l32;
+  const bool my_valid = my_q < n;
+  const int64_t my_tau = my_valid ? p.timestamps[o0 + my_q] : 0;
+  const int my_pos = cand ? imin(my_q, nh) : my_q;
+
+  int64_t wmin = my_valid ? my_tau : INT64_MAX;
+  int64_t wmax = my_valid ? my_tau : INT64_MIN;
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) {
+    const int64_t a = shfl_xor_i64(wmin, m), c = shfl_xor_i64(wmax, m);
+    wmin = a < wmin ? a : wmin;
+    wmax = c > wmax ? c : wmax;
+  }
+
+  // Q fragments (B operand of S^T = K Q^T): lane holds query l32, dh = kKStep*s + kKPL*half + [0, kKPL)
+  Frag qf[L::kQSteps];
+  {
+    const T *qrow = (const T *)p.q + (int64_t)(o0 + (my_valid ? my_q : 0)) * p.row_stride + h * DH;
+#pragma unroll
+    for (int s = 0; s < L::kQSteps; ++s) {
+      if constexpr (L::kBf16) {
+        bf16x8 v = *(const bf16x8 *)(qrow + s * 16 + half * 8);
+        if (!my_valid) v = bf16x8{};
+        qf[s] = v;
+      } else {
+        qf[s] = my_valid ? qrow[s * 2 + half] : 0.0f;
+      }
+    }
+  }
+
+  // ---- key tiles needed by the workgroup: [0, r1_end) and, for candidate rows, their own tiles
+  const int blast = imin(q0 + kBM - 1, n - 1);
+  const int r1_end = (imin(blast + 1, nh) + kBN - 1) / kBN;
+  int r2_begin = 0, r2_end = 0;
+  if (blast >= nh) {
+    r2_begin = imax(imax(q0, nh) / kBN, r1_end);
+    r2_end = blast / kBN + 1;
+  }
+  auto next_tile = [&](int t) -> int {
+    ++t;
+    if (t < r1_end) return t;
+    if (t < r2_begin) t = r2_begin;
+    return t < r2_end ? t : -1;
+  };
+  int tile = r1_end > 0 ? 0 : (r2_begin < r2_end ? r2_begin : -1);
+
+  // ---- staging of one key tile: global -> registers -> LDS
+  u32x4 kreg[L::kChunksPerThread], vreg[L::kChunksPerThread];
+  int64_t treg = 0;
+  auto load_tile = [&](int t) {
+    const int k0 = t * kBN;
+#pragma unroll
+    for (int c = 0; c < L::kChunksPerThread; ++c) {
+      const int chunk = tid + c * kThreads;
+      const int row = chunk / L::kChunksPerRow, col = chunk % L::kChunksPerRow;
+      const bool ok = k0 + row < n;
+      const int64_t off = (int64_t)(o0 + (ok ? k0 + row : 0)) * p.row_stride * L::kES + (int64_t)h * DH * L::kES +
+                          col * 16;
+      u32x4 kv = *(const u32x4 *)((const char *)p.k + off);
+      u32x4 vv = *(const u32x4 *)((const char *)p.v + off);
+      kreg[c] = ok ? kv : u32x4{0u, 0u, 0u, 0u};
+      vreg[c] = ok ? vv : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tid < kBN) treg = (k0 + tid < n) ? p.timestamps[o0 + k0 + tid] : 0;
+  };
+  auto store_tile = [&](int t, int stage) {
+    HSTU_LDS char *base = smem + stage * L::kStageBytes;
+    const int k0 = t * kBN;
+#pragma unroll
+    for (int c = 0; c < L::kChunksPerThread; ++c) {
+      const int chunk = tid + c * kThreads;
+      const int row = chunk / L::kChunksPerRow, col = chunk % L::kChunksPerRow;
+      HSTU_LDS char *kdst = base + L::kOffK + kperm(row) * L::kKStride + col * 16;
+      if constexpr (L::kBf16) {
+        *(HSTU_LDS u32x4 *)kdst = kreg[c];
+      } else {
+        HSTU_LDS uint32_t *d = (HSTU_LDS uint32_t *)kdst;
+        d[0] = kreg[c].x; d[1] = kreg[c].y; d[2] = kreg[c].z; d[3] = kreg[c].w;
+      }
+      *(HSTU_LDS u32x4 *)(base + L::kOffV + row * L::kVStride + col * 16) = vreg[c];
+    }
+    if (tid < kBN) {
+      HSTU_LDS int64_t *tl = (HSTU_LDS int64_t *)(base + L::kOffTau);
+      tl[tid] = treg;
+      const bool ok = k0 + tid < n;
+      int64_t mn = ok ? treg : INT64_MAX, mx = ok ? treg : INT64_MIN;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const int64_t a = shfl_xor_i64(mn, m), c = shfl_xor_i64(mx, m);
+        mn = a < mn ? a : mn;
+        mx = c > mx ? c : mx;
+      }
+      if (tid == 0) {
+        HSTU_LDS int64_t *st = (HSTU_LDS int64_t *)(base + L::kOffStat);
+        st[0] = mn;
+        st[1] = mx;
+      }
+    }
+  };
+
+  floatx16 oacc[L::kDB];
+#pragma unroll
+  for (int d = 0; d < L::kDB; ++d) oacc[d] = floatx16{};
+
+  int stage = 0;
+  if (tile >= 0) {
+    load_tile(tile);
+    store_tile(tile, 0);
+  }
+  __syncthreads();
+
+  while (tile >= 0) {
+    const int nxt = next_tile(tile);
+    if (nxt >= 0) load_tile(nxt);
+    HSTU_LDS char *base = smem + stage * L::kStageBytes;
+    const int k0 = tile * kBN;
+
+    // ---- classify this tile for this wave
+    const bool none = !wave_active || k0 > ql || (k0 >= nh && (k0 + kBN - 1 < imax(qa, nh)));
+    if (!none) {
+      const bool all = (k0 + kBN - 1 <= qa) && (k0 + kBN - 1 < nh);
+      bool uniform = false;
+      float cbias = 0.0f;
+      if (all && imin(qa, nh) - (k0 + kBN - 1) >= P - 1) {
+        const HSTU_LDS int64_t *st = (const HSTU_LDS int64_t *)(base + L::kOffStat);
+        const int64_t kmin = st[0], kmax = st[1];
+        uint64_t lo, hi;
+        if (wmin >= kmax) {
+          lo = (uint64_t)wmin - (uint64_t)kmax;
+          hi = (uint64_t)wmax - (uint64_t)kmin;
+        } else if (kmin >= wmax) {
+          lo = (uint64_t)kmin - (uint64_t)wmax;
+          hi = (uint64_t)kmax - (uint64_t)wmin;
+        } else {
+          lo = 0;
+          const uint64_t h1 = (uint64_t)wmax - (uint64_t)kmin, h2 = (uint64_t)kmax - (uint64_t)wmin;
+          hi = h1 > h2 ? h1 : h2;
+        }
+        const int blo = imin(lo == 0 ? 0 : 64 - __clzll((long long)lo), Tb - 1);
+        const int bhi = imin(hi == 0 ? 0 : 64 - __clzll((long long)hi), Tb - 1);
+        if (blo == bhi) {
+          uniform = true;
+          cbias = wp_lds[P - 1] + wt_lds[blo];
+        }
+      }
+
+      const HSTU_LDS char *lK = base + L::kOffK;
+      const HSTU_LDS char *lV = base + L::kOffV;
+      const HSTU_LDS int64_t *lT = (const HSTU_LDS int64_t *)(base + L::kOffTau);
+
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        // S^T block: 32 keys x 32 queries
+        floatx16 s = floatx16{};
+#pragma unroll
+        for (int st = 0; st < L::kQSteps; ++st) {
+          Frag kf;
+          if constexpr (L::kBf16) {
+            kf = *(const HSTU_LDS bf16x8 *)(lK + (32 * kb + l32) * L::kKStride + (16 * st + 8 * half) * 2);
+          } else {
+            kf = *(const HSTU_LDS float *)(lK + (32 * kb + l32) * L::kKStride + (2 * st + half) * 4);
+          }
+          s = mfma32(kf, qf[st], s);
+        }
+        // pointwise: element e holds key j = k0 + 32*kb + 16*(e/8) + 8*half + e%8
+        float a[16];
+        if (uniform) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) a[e] = silu_f32(s[e] + cbias);
+        } else {
+          const bool masked = !all;
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const int jl0 = 32 * kb + 16 * g + 8 * half;     // local key of element 8*g
+#pragma unroll
+            for (int e8 = 0; e8 < 8; ++e8) {
+              const int e = 8 * g + e8;
+              const int j = k0 + jl0 + e8;
+              const int64_t tj = lT[jl0 + e8];
+              const int pj = cand ? imin(j, nh) : j;
+              const int dp = my_pos >= pj ? my_pos - pj : pj - my_pos;
+              const int bp = imin(dp, P - 1);
+              const int bt = imin(bitlen_absdiff(my_tau, tj), Tb - 1);
+              const float sv = s[e] + wp_lds[bp] + wt_lds[bt];
+              bool ok = true;
+              if (masked) {
+                ok = j < n && (my_q < nh ? j <= my_q : (j < nh || j == my_q));
+              }
+              a[e] = ok ? silu_f32(sv) : 0.0f;
+            }
+          }
+        }
+        // O^T += V^T P^T over these 32 keys
+        if constexpr (L::kBf16) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            bf16x8 pf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pf[e] = f32_to_bf16(a[8 * s2 + e]);
+            const int g16 = lane >> 4, i16 = lane & 15;
+            const int krow = 32 * kb + 16 * s2 + 8 * half + (i16 >> 2);
+#pragma unroll
+            for (int db = 0; db < L::kDB; ++db) {
+              const int col = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
+              const HSTU_LDS shortx4 *a0 = (const HSTU_LDS shortx4 *)(lV + krow * L::kVStride + col * 2);
+              const HSTU_LDS shortx4 *a1 = (const HSTU_LDS shortx4 *)(lV + (krow + 4) * L::kVStride + col * 2);
+              const shortx4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HSTU_LDS shortx4 *)a0);
+              const shortx4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HSTU_LDS shortx4 *)a1);
+              bf16x8 vf;
+              const bf16x4 w0 = __builtin_bit_cast(bf16x4, v0), w1 = __builtin_bit_cast(bf16x4, v1);
+              vf[0] = w0[0]; vf[1] = w0[1]; vf[2] = w0[2]; vf[3] = w0[3];
+              vf[4] = w1[0]; vf[5] = w1[1]; vf[6] = w1[2]; vf[7] = w1[3];
+              oacc[db] = mfma32(vf, pf, oacc[db]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int krow = 32 * kb + 16 * (e / 8) + 8 * half + (e % 8);
+#pragma unroll
+            for (int db = 0; db < L::kDB; ++db) {
+              const float vf = *(const HSTU_LDS float *)(lV + krow * L::kVStride + (32 * db + l32) * 4);
+              oacc[db] = mfma32(vf, a[e], oacc[db]);
+            }
+          }
+        }
+      }
+    }
+
+    if (nxt >= 0) store_tile(nxt, stage ^ 1);
+    __syncthreads();
+    stage ^= 1;
+    tile = nxt;
+  }
+
+  // ---- epilogue: O^T element e of dh block db is dh = 32*db + 8*(e/4) + 4*half + e%4
+  if (my_valid) {
+    TO *orow = (TO *)p.out + (int64_t)(o0 + my_q) * p.out_row_stride + h * DH;
+#pragma unroll
+    for (int db = 0; db < L::kDB; ++db) {
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int dh = 32 * db + 8 * e4 + 4 * half;
+        if constexpr (sizeof(TO) == 4) {
+          floatx4 w;
+          w[0] = oacc[db][4 * e4 + 0] * cb; w[1] = oacc[db][4 * e4 + 1] * cb;
+          w[2] = oacc[db][4 * e4 + 2] * cb; w[3] = oacc[db][4 * e4 + 3] * cb;
+          *(floatx4 *)(orow + dh) = w;
+        } else {
+          bf16x4 w;
+          w[0] = f32_to_bf16(oacc[db][4 * e4 + 0] * cb); w[1] = f32_to_bf16(oacc[db][4 * e4 + 1] * cb);
+          w[2] = f32_to_bf16(oacc[db][4 * e4 + 2] * cb); w[3] = f32_to_bf16(oacc[db][4 * e4 + 3] * cb);
+          *(bf16x4 *)(orow + dh) = w;
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int DH, typename TO>
+hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
+  using L = Layout<T, DH>;
+  const int n_qblocks = (a.max_seq_len + kBM - 1) / kBM;
+  const long long grid = (long long)n_qblocks * a.num_heads * a.num_seqs;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const size_t lds = 2 * L::kStageBytes + (size_t)(a.num_pos_buckets + kTimeTab) * sizeof(float);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_kernel<T, DH, TO>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((attn_fwd_kernel<T, DH, TO>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a, n_qblocks);
+  return hipGetLastError();
+}
+
+template <typename T, typename TO>
+hipError_t launch_dh(const AttnArgs &a, hipStream_t stream) {
+  switch (a.head_dim) {
+    case 32: return launch_typed<T, 32, TO>(a, stream);
+    case 64: return launch_typed<T, 64, TO>(a, stream);
+    case 128: return launch_typed<T, 128, TO>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream) {
+  if (a.in_dtype == kBF16) {
+    return a.out_dtype == kBF16 ? launch_dh<__bf16, __bf16>(a, stream) : launch_dh<__bf16, float>(a, stream);
+  }
+  return launch_dh<float, float>(a, stream);
+}
+
+}  // namespace hstu

@@ -1,0 +1,61 @@
+// Device-side helpers shared by the gfx950 kernels of libhstu: vector types, MFMA wrappers,
+// bf16 conversion, LDS pointer qualifiers.  CDNA4 only (wave64, MFMA, LDS transpose reads).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hstu {
+
+#define HSTU_LDS __attribute__((address_space(3)))
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(__bf16 x) { return (float)x; }
+
+// Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ __bf16 f32_to_bf16(float x) { return (__bf16)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<__bf16>(__bf16 x) { return (float)x; }
+
+// 32x32 MFMA over one k-step.  bf16: k = 16 per instruction, 8 values per lane; f32: k = 2, 1 value.
+// Operand layouts (lane l): A[m][k] at lane m + 32*(k/KPL), B[k][n] at lane n + 32*(k/KPL);
+// D[m][n] at lane n + 32*((m/4)%2), element 4*(m/8) + m%4.
+__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx16 mfma32(float a, float b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// SiLU(s) = s * sigmoid(s) = s / (1 + 2^(-s*log2(e))), with the hardware exp2 and reciprocal.
+// For s << 0 the exponential overflows to +inf and the reciprocal gives 0, the right limit.
+__device__ __forceinline__ float silu_f32(float s) {
+  const float e = __builtin_amdgcn_exp2f(s * -1.4426950408889634f);
+  return s * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Number of significant bits of |a - b| for int64 a, b (exact; the difference fits in uint64).
+__device__ __forceinline__ int bitlen_absdiff(int64_t a, int64_t b) {
+  const uint64_t d = a >= b ? (uint64_t)a - (uint64_t)b : (uint64_t)b - (uint64_t)a;
+  return d == 0 ? 0 : 64 - __clzll((long long)d);
+}
+
+__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+__device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
+
+}  // namespace hstu

@@ -1,0 +1,84 @@
+// Internal launch interface between the C-ABI host code (api.cpp) and the HIP kernels.
+// Host-side validation happens in api.cpp; every launcher here assumes valid arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hstu {
+
+enum Dtype : int { kF32 = 0, kBF16 = 1 };
+enum Mask : int { kCausal = 0, kCausalCandidates = 1 };
+
+// Pointwise attention over a jagged batch.
+struct AttnArgs {
+  const void *q, *k, *v;          // [T][row_stride] elements, head h at column h*Dh
+  void *out;                      // [T][out_row_stride] elements, head h at column h*Dh
+  int64_t row_stride;             // elements between tokens in q/k/v
+  int64_t out_row_stride;         // elements between tokens in out
+  const int32_t *seq_offsets;     // [B+1]
+  const int64_t *timestamps;      // [T]
+  const int32_t *num_candidates;  // [B] or null
+  const float *attn_scale;        // [B] or null
+  const float *pos_bias;          // [R][P]
+  const float *time_bias;         // [R][Tb]
+  int32_t num_seqs, num_heads, head_dim, max_seq_len;
+  int32_t num_pos_buckets, num_time_buckets, rab_rows;
+  int32_t mask;
+  int32_t in_dtype, out_dtype;
+};
+
+hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream);
+
+// C[M][N] = epilogue(A[M][K] * B[N][K]^T): bf16 or f32 weights (MFMA operand type `dtype`), fp32
+// accumulation.  With bf16 weights the activation A may be fp32 (x_f32 / g_f32): rounded to bf16, or with
+// split = 1 entered as a bf16 hi + lo pair (two MFMA passes).
+struct GemmUvqkArgs {
+  const void *x;                  // [M][K], fp32 if x_f32 else dtype
+  const void *w;                  // [4*HD][K] dtype
+  const void *bias;               // [4*HD] dtype or null
+  float *u;                       // [M][HD] fp32
+  void *v, *q, *k;                // each [M][HD] dtype
+  int32_t M, K, HD;
+  int32_t dtype, x_f32, split;
+};
+hipError_t launch_gemm_uvqk(const GemmUvqkArgs &a, hipStream_t stream);
+
+// Gate: g = LN(o) * u over each H*Dh row (LN: biased variance, no affine).
+struct NormGateArgs {
+  const float *o;                 // [M][HD] fp32 attention output
+  const float *u;                 // [M][HD] fp32
+  void *g;                        // [M][HD]: fp32 if g_f32 else dtype
+  int32_t M, HD;
+  float eps;
+  int32_t dtype, g_f32;
+};
+hipError_t launch_norm_gate(const NormGateArgs &a, hipStream_t stream);
+
+// Output projection: y = x + g W2^T + b2 (into y, or fp32 into y32 when a LayerNorm follows).
+struct GemmOutArgs {
+  const void *g;                  // [M][K] (K = HD): fp32 if g_f32 else dtype
+  const void *w;                  // [N][K] dtype (N = D)
+  const void *bias;               // [N] dtype or null
+  const void *x;                  // [M][N] residual: fp32 if x_f32 else dtype
+  void *y;                        // [M][N]: fp32 if y_f32 else dtype (unused when y32 is set)
+  float *y32;                     // [M][N] fp32 pre-LayerNorm result, or null
+  int32_t M, N, K;
+  int32_t dtype, g_f32, split, x_f32, y_f32;
+};
+hipError_t launch_gemm_out(const GemmOutArgs &a, hipStream_t stream);
+
+struct RowLnArgs {
+  const float *in;                // [M][N] fp32
+  void *out;                      // [M][N]: fp32 if out_f32 else bf16
+  int32_t M, N;
+  float eps;
+  int32_t out_f32;
+};
+hipError_t launch_row_layernorm(const RowLnArgs &a, hipStream_t stream);
+
+hipError_t launch_gather_rows(const void *table, int64_t table_rows, int32_t row_bytes, const int64_t *ids,
+                              int32_t T, void *out, hipStream_t stream);
+
+}  // namespace hstu

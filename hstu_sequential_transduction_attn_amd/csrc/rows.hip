@@ -1,0 +1,174 @@
+// Row-wise, HBM-bound kernels of the HSTU layer on gfx950.
+//
+//  * norm_gate:      g_t = LN(o_t) * u_t over the H*Dh row of each token (the gated transformation:
+//                    "DLRMv4：MLPerfの推薦システム訓練ベンチマークがシーケンス化時代へ", section
+//                    "モデルアーキテクチャ").  LayerNorm with biased variance, no affine.
+//  * row_layernorm:  y_t = LN(y32_t) between stacked layers.
+//  * gather_rows:    x_t = E[id_t], the embedding lookup that stages the first layer's input.
+//
+// One wave per row; each lane keeps its slice of the row in registers, so the row is read from HBM
+// exactly once and the statistics take two passes over registers (mean, then centred squares).
+#include "device_common.hpp"
+#include "kernels.h"
+
+namespace hstu {
+namespace {
+
+constexpr int kRowsPerBlock = 4;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Each lane owns columns lane*4 + 256*c for c < N/256 (+ tail): 16-byte fp32 loads.
+template <typename TO, int MAXC>
+__global__ void __launch_bounds__(256) norm_gate_kernel(const float *__restrict__ o, const float *__restrict__ u,
+                                                        TO *__restrict__ g, int M, int N, float eps) {
+  const int row = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (row >= M) return;
+  const float *orow = o + (int64_t)row * N;
+  float x[MAXC][4];
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int col = 256 * c + 4 * lane;
+    if (col < N) {
+      const floatx4 v = *(const floatx4 *)(orow + col);
+      x[c][0] = v[0]; x[c][1] = v[1]; x[c][2] = v[2]; x[c][3] = v[3];
+      s += v[0] + v[1] + v[2] + v[3];
+    } else {
+      x[c][0] = x[c][1] = x[c][2] = x[c][3] = 0.0f;
+    }
+  }
+  const float mean = wave_sum(s) / (float)N;
+  float q = 0.0f;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int col = 256 * c + 4 * lane;
+    if (col < N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float d = x[c][i] - mean;
+        q += d * d;
+      }
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)N + eps);
+  const float *urow = u + (int64_t)row * N;
+  TO *grow = g + (int64_t)row * N;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int col = 256 * c + 4 * lane;
+    if (col < N) {
+      const floatx4 uv = *(const floatx4 *)(urow + col);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) grow[col + i] = from_f32<TO>((x[c][i] - mean) * rstd * uv[i]);
+    }
+  }
+}
+
+template <typename TO, int MAXC>
+__global__ void __launch_bounds__(256) row_ln_kernel(const float *__restrict__ in, TO *__restrict__ out, int M, int N,
+                                                     float eps) {
+  const int row = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (row >= M) return;
+  const float *irow = in + (int64_t)row * N;
+  float x[MAXC][4];
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int col = 256 * c + 4 * lane;
+    if (col < N) {
+      const floatx4 v = *(const floatx4 *)(irow + col);
+      x[c][0] = v[0]; x[c][1] = v[1]; x[c][2] = v[2]; x[c][3] = v[3];
+      s += v[0] + v[1] + v[2] + v[3];
+    } else {
+      x[c][0] = x[c][1] = x[c][2] = x[c][3] = 0.0f;
+    }
+  }
+  const float mean = wave_sum(s) / (float)N;
+  float q = 0.0f;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int col = 256 * c + 4 * lane;
+    if (col < N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float d = x[c][i] - mean;
+        q += d * d;
+      }
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)N + eps);
+  TO *orow = out + (int64_t)row * N;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int col = 256 * c + 4 * lane;
+    if (col < N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) orow[col + i] = from_f32<TO>((x[c][i] - mean) * rstd);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) gather_kernel(const u32x4 *__restrict__ table, const int64_t *__restrict__ ids,
+                                                     u32x4 *__restrict__ out, int T, int chunks_per_row) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)T * chunks_per_row;
+  if (i >= total) return;
+  const int64_t t = i / chunks_per_row;
+  const int c = (int)(i % chunks_per_row);
+  out[i] = table[ids[t] * chunks_per_row + c];
+}
+
+// Row width is bounded by 256 * MAXC (checked on the host: width <= 4096, width % 4 == 0).
+template <typename TO>
+hipError_t launch_ng(const NormGateArgs &a, hipStream_t s) {
+  const dim3 grid((a.M + kRowsPerBlock - 1) / kRowsPerBlock);
+  const float *o = a.o;
+  const float *u = a.u;
+  TO *g = (TO *)a.g;
+  if (a.HD <= 256) hipLaunchKernelGGL((norm_gate_kernel<TO, 1>), grid, dim3(256), 0, s, o, u, g, a.M, a.HD, a.eps);
+  else if (a.HD <= 1024) hipLaunchKernelGGL((norm_gate_kernel<TO, 4>), grid, dim3(256), 0, s, o, u, g, a.M, a.HD, a.eps);
+  else hipLaunchKernelGGL((norm_gate_kernel<TO, 16>), grid, dim3(256), 0, s, o, u, g, a.M, a.HD, a.eps);
+  return hipGetLastError();
+}
+
+template <typename TO>
+hipError_t launch_ln(const RowLnArgs &a, hipStream_t s) {
+  const dim3 grid((a.M + kRowsPerBlock - 1) / kRowsPerBlock);
+  TO *out = (TO *)a.out;
+  if (a.N <= 256) hipLaunchKernelGGL((row_ln_kernel<TO, 1>), grid, dim3(256), 0, s, a.in, out, a.M, a.N, a.eps);
+  else if (a.N <= 1024) hipLaunchKernelGGL((row_ln_kernel<TO, 4>), grid, dim3(256), 0, s, a.in, out, a.M, a.N, a.eps);
+  else hipLaunchKernelGGL((row_ln_kernel<TO, 16>), grid, dim3(256), 0, s, a.in, out, a.M, a.N, a.eps);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_norm_gate(const NormGateArgs &a, hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  return (a.dtype == kBF16 && !a.g_f32) ? launch_ng<__bf16>(a, s) : launch_ng<float>(a, s);
+}
+
+hipError_t launch_row_layernorm(const RowLnArgs &a, hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  return a.out_f32 ? launch_ln<float>(a, s) : launch_ln<__bf16>(a, s);
+}
+
+hipError_t launch_gather_rows(const void *table, int64_t table_rows, int32_t row_bytes, const int64_t *ids, int32_t T,
+                              void *out, hipStream_t s) {
+  (void)table_rows;
+  if (T == 0) return hipSuccess;
+  const int cpr = row_bytes / 16;
+  const int64_t total = (int64_t)T * cpr;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  hipLaunchKernelGGL(gather_kernel, grid, dim3(256), 0, s, (const u32x4 *)table, ids, (u32x4 *)out, T, cpr);
+  return hipGetLastError();
+}
+
+}  // namespace hstu

@@ -1,0 +1,166 @@
+/*
+ * hstu.h -- C ABI of libhstu, the MI355X (gfx950) HSTU layer forward.
+ *
+ * What it computes.  The HSTU layer as the pages describe it: "DLRMv4：MLPerfの推薦システム訓練
+ * ベンチマークがシーケンス化時代へ", section "モデルアーキテクチャ：HSTUが従来の特徴インタラクション
+ * スタックに取って代わる" -- one projection makes every internal representation of the layer,
+ * pointwise attention aggregates the sequence with a bias from the positional and temporal distance
+ * of two events, and a gated transformation lets the aggregated features interact.  Section
+ * "1つの訓練サンプルがHSTUでどのように処理されるか" of the same page: a time-ordered per-user event
+ * sequence, candidates appended at the end, the whole sequence processed as one causal block.
+ * "Actions Speak Louder than Words: Trillion-Parameter Sequential Transducers for Generative
+ * Recommendations", abstract: HSTU, an attention variant for high-cardinality, non-stationary
+ * streaming data, at sequence length 8192.
+ *
+ * Formulas (the pages fix the structure, not the algebra; these are the readings implemented):
+ *   projection  z_t = W1 x_t + b1;  U|V|Q|K = SiLU(z_t) split into four H*Dh slices, head-major
+ *   scores      s_ij = q_i . k_j + pos_bias[r][bp] + time_bias[r][bt]     (no 1/sqrt(Dh))
+ *               bp = min(|pos_i - pos_j|, P-1), bt = min(bitlen(|tau_i - tau_j|), Tb-1) (exact int64)
+ *   attention   O_i = c_b * sum_{allowed j} SiLU(s_ij) v_j,  c_b = attn_scale[b] or 1/n_b   (no softmax)
+ *   gate        g_t = LN(concat_h O_t) * U_t     (LN over H*Dh, biased variance, no affine)
+ *   output      y_t = x_t + W2 g_t + b2;  if ln_output: y_t = LN(y_t)
+ * Masks: HSTU_MASK_CAUSAL allows j <= i.  HSTU_MASK_CAUSAL_CANDIDATES: the last m_b tokens of
+ * sequence b are candidates (n_h = n_b - m_b); history rows allow j <= i; a candidate row allows
+ * every j < n_h and j = i (never another candidate); candidates take position n_h.
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked (device) are device addresses owned by the caller; the library keeps none of
+ *    them after the call returns and never allocates or frees device memory.  Scratch memory comes
+ *    from the caller's `workspace`, sized by the matching *_workspace_bytes() call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All work is enqueued on
+ *    it; calls return before the work completes; nothing is synchronised and nothing is copied
+ *    between host and device, so the calls can be captured in a HIP graph.
+ *  - Everything the host can check is checked before any launch (null pointers, sizes, supported
+ *    head_dim / dtype pairs, workspace size, 16-byte alignment).  A failure returns a status and
+ *    leaves a message for hstu_last_error(); no C++ exception crosses the ABI; a failed launch
+ *    returns HSTU_ERR_DEVICE with the HIP error text.
+ *  - Device-resident content is the caller's contract and is not validated on the hot path:
+ *    offsets must be non-decreasing from 0 to total_tokens, 0 <= num_candidates[b] <= n_b,
+ *    and ids must be < table_rows.
+ *  - Outputs are bitwise deterministic for identical inputs on one device (no float atomics).
+ */
+#ifndef HSTU_H_
+#define HSTU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HSTU_ABI_VERSION 1
+
+typedef enum {
+  HSTU_OK = 0,
+  HSTU_ERR_INVALID_ARGUMENT = 1,
+  HSTU_ERR_UNSUPPORTED = 2,
+  HSTU_ERR_WORKSPACE_TOO_SMALL = 3,
+  HSTU_ERR_DEVICE = 4
+} hstu_status_t;
+
+typedef enum { HSTU_F32 = 0, HSTU_BF16 = 1 } hstu_dtype_t;
+
+typedef enum { HSTU_MASK_CAUSAL = 0, HSTU_MASK_CAUSAL_CANDIDATES = 1 } hstu_mask_t;
+
+/* The jagged batch: B per-user event sequences packed back to back (T tokens in total). */
+typedef struct {
+  int32_t num_seqs;              /* B >= 0 (host)                                                  */
+  int32_t total_tokens;          /* T = seq_offsets[B] (host); sizes the launch, never read back   */
+  int32_t max_seq_len;           /* >= max_b n_b (host); sizes the launch, never read back         */
+  const int32_t *seq_offsets;    /* [B+1] (device): 0 = o_0 <= o_1 <= ... <= o_B = T               */
+  const int64_t *timestamps;     /* [T] (device): any int64 (seconds in the shipped workloads)     */
+  const int32_t *num_candidates; /* [B] (device): m_b, required iff mask == CAUSAL_CANDIDATES       */
+  const float *attn_scale;       /* [B] (device) c_b, or NULL for c_b = 1/n_b                      */
+} hstu_jagged_t;
+
+/* The pointwise attention and its relative-attention bias (rab) tables. */
+typedef struct {
+  int32_t num_heads;             /* H >= 1                                                         */
+  int32_t head_dim;              /* Dh in {32, 64, 128}                                            */
+  int32_t num_pos_buckets;       /* P in [1, 4096]                                                 */
+  int32_t num_time_buckets;      /* Tb in [1, 4096]                                                */
+  int32_t rab_rows;              /* R = 1 (one table pair shared by all heads) or R = H            */
+  const float *pos_bias;         /* [R][P] fp32 (device)                                           */
+  const float *time_bias;        /* [R][Tb] fp32 (device)                                          */
+  hstu_mask_t mask;
+} hstu_attn_desc_t;
+
+/* Weights and numerics options of one layer; weight element type is the call's `dtype`. */
+typedef struct {
+  int32_t d_model;               /* D, a multiple of 8 in [8, 4096]                                */
+  const void *w_uvqk;            /* [4*H*Dh][D] (device): rows U | V | Q | K, head-major in each  */
+  const void *b_uvqk;            /* [4*H*Dh] (device) or NULL                                      */
+  const void *w_out;             /* [D][H*Dh] (device)                                             */
+  const void *b_out;             /* [D] (device) or NULL                                           */
+  float ln_eps;                  /* > 0; used by the gate's LayerNorm and the output LayerNorm    */
+  int32_t ln_output;             /* 1: y = LN(x + branch) (between stacked layers); 0: y = x + branch */
+  int32_t act_split;             /* bf16 only.  0: fp32 activations (x, and the gate g) are rounded
+                                    to bf16 before the GEMMs.  1: they enter both GEMMs as a bf16
+                                    hi + lo pair (two MFMA passes, ~16 significant bits), so long
+                                    stacks keep fp32-activation accuracy.  Ignored for f32.        */
+} hstu_layer_weights_t;
+
+/* ABI version of the loaded library (HSTU_ABI_VERSION). */
+int hstu_abi_version(void);
+
+/* Text of a status code (static storage). */
+const char *hstu_status_string(hstu_status_t status);
+
+/* Detail of the last non-OK return on the calling thread (thread-local storage; "" if none). */
+const char *hstu_last_error(void);
+
+/*
+ * Workspace needed by hstu_attn_fwd for this batch shape (bytes; 0 is possible).  Depends only on
+ * the host fields of `jag` and `desc`.
+ */
+size_t hstu_attn_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc,
+                                 hstu_dtype_t in_dtype);
+
+/*
+ * Pointwise attention forward (steps 2-3 of the layer; the causal-jagged kernel):
+ *   out[t][h][:] = c_b * sum_{allowed j} SiLU(q_t . k_j + rab) v_j   for every token t of every sequence.
+ * q, k, v: [T][H][Dh] row-major (device), dtype in_dtype (HSTU_BF16 or HSTU_F32).
+ * out:     [T][H][Dh] row-major (device), out_dtype = HSTU_F32 or in_dtype; may not alias q, k, v.
+ * bf16 inputs: QK^T and AV on bf16 MFMA with fp32 accumulation; SiLU(s) is rounded to bf16 as the
+ * AV operand.  f32 inputs: fp32 MFMA throughout.
+ * Returns HSTU_ERR_UNSUPPORTED for a head_dim outside {32, 64, 128}.
+ */
+hstu_status_t hstu_attn_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, hstu_dtype_t in_dtype,
+                            const void *q, const void *k, const void *v, void *out, hstu_dtype_t out_dtype,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace needed by hstu_layer_fwd (bytes). */
+size_t hstu_layer_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc,
+                                  const hstu_layer_weights_t *w, hstu_dtype_t dtype);
+
+/*
+ * One HSTU layer forward (steps 1-4):  y = [LN](x + W2 (LN(O) * U) + b2).
+ * dtype:   element type of the weights and of the MFMA operands (HSTU_BF16: bf16 MFMA with fp32
+ *          accumulation; HSTU_F32: fp32 throughout).
+ * x:       [T][D] (device), element type x_dtype in {HSTU_F32, dtype}.
+ * y:       [T][D] (device), element type y_dtype in {HSTU_F32, dtype}; may not overlap x.
+ *          An fp32 residual stream between stacked bf16 layers (x_dtype = y_dtype = HSTU_F32) avoids
+ *          rounding the activations to bf16 at every layer boundary.
+ * Inside: the projection GEMM fuses bias, SiLU and the U|V|Q|K split into its epilogue (U is kept in
+ * fp32, V, Q, K in dtype); the attention writes O in fp32; the gate applies LN(O) * U in fp32; the output
+ * GEMM adds bias and residual in fp32 and rounds once (or hands the fp32 sum to the output LayerNorm).
+ */
+hstu_status_t hstu_layer_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc,
+                             const hstu_layer_weights_t *w, hstu_dtype_t dtype, hstu_dtype_t x_dtype,
+                             const void *x, hstu_dtype_t y_dtype, void *y, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * Embedding gather (input staging before the first layer):  out[t][:] = table[ids[t]][:].
+ * table: [table_rows][d] (device); ids: [T] int64 (device), each in [0, table_rows);
+ * out: [T][d] (device).  Element type `dtype`; d * element size must be a multiple of 16 bytes.
+ */
+hstu_status_t hstu_gather_rows(const void *table, int64_t table_rows, int32_t d, hstu_dtype_t dtype,
+                               const int64_t *ids, int32_t T, void *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_H_ */

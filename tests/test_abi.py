@@ -1,0 +1,137 @@
+"""The C-ABI library on the host: it loads, exports every function include/hstu.h declares, and rejects
+invalid arguments with the documented status before anything reaches the GPU.
+
+No call here launches a kernel: every case fails validation (or has zero tokens) first, so these
+tests run without a GPU.  Pointers are fake device addresses that are never dereferenced.
+"""
+import ctypes
+import os
+
+import pytest
+
+from hstu_sequential_transduction_attn_amd import _lib as L
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libhstu.so not built")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL, DEVICE = 0, 1, 2, 3, 4
+P16 = 0x7F0000000000  # a 16-byte aligned fake device address
+
+
+def _lib():
+    return L.load_library()
+
+
+def _jag(B=2, T=100, max_len=60, cand=False):
+    return L.JaggedT(B, T, max_len, P16, P16 + 0x1000, P16 + 0x2000 if cand else None, None)
+
+
+def _desc(H=4, Dh=128, P=32, Tb=32, R=1, mask=0):
+    return L.AttnDescT(H, Dh, P, Tb, R, P16 + 0x3000, P16 + 0x4000, mask)
+
+
+def _attn(jag, desc, in_dt=L.HSTU_BF16, out_dt=L.HSTU_BF16, q=P16 + 0x10000, k=P16 + 0x20000000,
+          v=P16 + 0x40000000, out=P16 + 0x60000000, ws=None, nws=0):
+    lib = _lib()
+    st = lib.hstu_attn_fwd(ctypes.byref(jag) if jag else None, ctypes.byref(desc) if desc else None, in_dt, q, k, v,
+                           out, out_dt, ws, nws, None)
+    return st, lib.hstu_last_error().decode()
+
+
+def test_exports_every_declared_symbol():
+    names = L.exported_functions_in_header()
+    assert len(names) == 8
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    lib = _lib()
+    assert lib.hstu_abi_version() == 1
+    assert lib.hstu_status_string(OK) == b"HSTU_OK"
+    assert lib.hstu_status_string(WS_SMALL) == b"HSTU_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.hstu_status_string(99) == b"HSTU_STATUS_UNKNOWN"
+
+
+def test_attn_argument_errors():
+    assert _attn(None, _desc())[0] == INVALID
+    assert _attn(_jag(), None)[0] == INVALID
+    st, msg = _attn(_jag(), _desc(Dh=48))
+    assert st == UNSUPPORTED and "head_dim" in msg
+    assert _attn(_jag(), _desc(H=0))[0] == INVALID
+    assert _attn(_jag(), _desc(P=0))[0] == INVALID
+    assert _attn(_jag(), _desc(Tb=5000))[0] == INVALID
+    assert _attn(_jag(), _desc(R=3))[0] == INVALID
+    assert _attn(_jag(), _desc(mask=7))[0] == INVALID
+    st, msg = _attn(_jag(cand=False), _desc(mask=1))
+    assert st == INVALID and "num_candidates" in msg
+    assert _attn(_jag(B=-1), _desc())[0] == INVALID
+    assert _attn(_jag(max_len=101), _desc())[0] == INVALID           # max_seq_len > total_tokens
+    assert _attn(_jag(B=0, T=5, max_len=0), _desc())[0] == INVALID
+    assert _attn(_jag(), _desc(), in_dt=L.HSTU_F32, out_dt=L.HSTU_BF16)[0] == UNSUPPORTED
+    assert _attn(_jag(), _desc(), in_dt=7)[0] == INVALID
+    assert _attn(_jag(), _desc(), q=None)[0] == INVALID
+    st, msg = _attn(_jag(), _desc(), q=P16 + 2)
+    assert st == INVALID and "aligned" in msg
+    st, msg = _attn(_jag(), _desc(), out=P16 + 0x10000 + 64)             # out overlaps q
+    assert st == INVALID and "overlaps" in msg
+    jag = L.JaggedT(2, 100, 60, None, P16, None, None)
+    assert _attn(jag, _desc())[0] == INVALID                              # seq_offsets NULL
+    assert _attn(_jag(), L.AttnDescT(4, 128, 32, 32, 1, None, P16, 0))[0] == INVALID
+
+
+def test_attn_zero_tokens_is_a_no_op():
+    st, msg = _attn(L.JaggedT(3, 0, 0, P16, None, None, None), _desc(), q=None, k=None, v=None, out=None)
+    assert st == OK and msg == ""
+
+
+def test_layer_argument_errors():
+    lib = _lib()
+    jag, desc = _jag(), _desc()
+
+    def call(w, dt=L.HSTU_BF16, x=P16 + 0x100000, y=P16 + 0x200000, ws=P16 + 0x10000000, nws=1 << 40,
+             x_dt=L.HSTU_BF16, y_dt=L.HSTU_BF16):
+        st = lib.hstu_layer_fwd(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w) if w else None, dt, x_dt, x,
+                                y_dt, y, ws, nws, None)
+        return st, lib.hstu_last_error().decode()
+
+    good = dict(d_model=512, w_uvqk=P16 + 0x300000, b_uvqk=None, w_out=P16 + 0x400000, b_out=None, ln_eps=1e-6,
+                ln_output=0, act_split=0)
+    mk = lambda **kw: L.LayerWeightsT(**{**good, **kw})
+    assert call(None)[0] == INVALID
+    assert call(mk(d_model=12))[0] == UNSUPPORTED
+    assert call(mk(ln_eps=0.0))[0] == INVALID
+    assert call(mk(w_out=None))[0] == INVALID
+    assert call(mk(), x=P16 + 0x100000, y=P16 + 0x100000 + 16)[0] == INVALID   # y overlaps x
+    assert call(mk(), dt=L.HSTU_F32, x_dt=L.HSTU_BF16)[0] == UNSUPPORTED        # bf16 x with f32 weights
+    assert call(mk(), y_dt=5)[0] == UNSUPPORTED
+    need = lib.hstu_layer_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(mk()), L.HSTU_BF16)
+    assert need > 0
+    st, msg = call(mk(), nws=need - 1)
+    assert st == WS_SMALL and str(need) in msg
+    need_ln = lib.hstu_layer_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(mk(ln_output=1)),
+                                             L.HSTU_BF16)
+    assert need_ln > need
+    need_split = lib.hstu_layer_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(mk(act_split=1)),
+                                                L.HSTU_BF16)
+    assert need_split > need                 # the gate stays fp32 for the split output GEMM
+
+
+def test_gather_argument_errors():
+    lib = _lib()
+
+    def call(d=512, dt=L.HSTU_BF16, T=10, rows=100, table=P16, ids=P16 + 0x100000, out=P16 + 0x200000):
+        return lib.hstu_gather_rows(table, rows, d, dt, ids, T, out, None)
+    assert call(d=12) == UNSUPPORTED          # 24-byte rows
+    assert call(T=-1) == INVALID
+    assert call(rows=0) == INVALID
+    assert call(table=None) == INVALID
+    assert call(out=P16 + 8) == INVALID
+    assert call(T=0, table=None, ids=None, out=None) == OK
+    assert call(out=P16 + 512) == INVALID     # out overlaps table
+
+
+def test_python_binding_raises_with_message():
+    with pytest.raises(L.HstuError) as ei:
+        L._check(UNSUPPORTED)
+    assert ei.value.name == "HSTU_ERR_UNSUPPORTED"
