@@ -101,13 +101,13 @@ hstu::AttnArgs attn_args(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc)
 
 // Layer workspace regions, each 256-byte aligned: U ([T][HD] fp32), V, Q, K ([T][HD] dtype),
 // O ([T][HD] fp32), G ([T][HD], fp32 when the gate stays fp32 for the output GEMM, else dtype),
-// Y32 ([T][D] fp32, only when ln_output).
+// Y32 ([T][D] fp32, only when ln_output), timestamp ranges of the attention.
 struct LayerWs {
-  size_t u, v, q, k, o, g, y32, total;
+  size_t u, v, q, k, o, g, y32, stats, total;
   bool g_f32;
 };
 
-LayerWs layer_ws(int64_t T, int64_t HD, int64_t D, hstu_dtype_t dt, bool ln_output, bool split) {
+LayerWs layer_ws(int64_t T, int64_t B, int64_t HD, int64_t D, hstu_dtype_t dt, bool ln_output, bool split) {
   LayerWs w{};
   w.g_f32 = dt == HSTU_F32 || split;
   const size_t part = round_up((size_t)T * HD * esize(dt), 256);
@@ -120,6 +120,7 @@ LayerWs layer_ws(int64_t T, int64_t HD, int64_t D, hstu_dtype_t dt, bool ln_outp
   w.o = off; off += part32;
   w.g = off; off += w.g_f32 ? part32 : part;
   w.y32 = off; off += ln_output ? round_up((size_t)T * D * 4, 256) : 0;
+  w.stats = off; off += round_up(hstu::attn_tau_stats_bytes(T, B), 256);
   w.total = off;
   return w;
 }
@@ -144,10 +145,10 @@ const char *hstu_status_string(hstu_status_t s) {
 const char *hstu_last_error(void) { return g_last_error.c_str(); }
 
 size_t hstu_attn_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, hstu_dtype_t in_dtype) {
-  (void)jag;
   (void)desc;
   (void)in_dtype;
-  return 0;
+  if (!jag || jag->total_tokens <= 0 || jag->num_seqs < 0) return 0;
+  return round_up(hstu::attn_tau_stats_bytes(jag->total_tokens, jag->num_seqs), 256);
 }
 
 hstu_status_t hstu_attn_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, hstu_dtype_t in_dtype,
@@ -163,9 +164,10 @@ hstu_status_t hstu_attn_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *de
     const size_t need = hstu_attn_workspace_bytes(jag, desc, in_dtype);
     if (workspace_bytes < need)
       return fail(HSTU_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
-    if (need > 0 && !workspace) return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace is NULL");
     const int64_t T = jag->total_tokens;
     if (T == 0) return ok();
+    if (!workspace) return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if (!aligned16(workspace)) return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
     if (!q || !k || !v || !out) return fail(HSTU_ERR_INVALID_ARGUMENT, "q/k/v/out is NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
       return fail(HSTU_ERR_INVALID_ARGUMENT, "q/k/v/out must be 16-byte aligned");
@@ -173,6 +175,9 @@ hstu_status_t hstu_attn_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *de
     const size_t nout = (size_t)T * desc->num_heads * desc->head_dim * esize(out_dtype);
     if (overlaps(out, nout, q, nin) || overlaps(out, nout, k, nin) || overlaps(out, nout, v, nin))
       return fail(HSTU_ERR_INVALID_ARGUMENT, "out overlaps q, k or v");
+    if (overlaps(workspace, need, out, nout) || overlaps(workspace, need, q, nin) || overlaps(workspace, need, k, nin) ||
+        overlaps(workspace, need, v, nin))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace overlaps q, k, v or out");
     hstu::AttnArgs a = attn_args(jag, desc);
     a.q = q;
     a.k = k;
@@ -182,6 +187,7 @@ hstu_status_t hstu_attn_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *de
     a.out_row_stride = a.row_stride;
     a.in_dtype = in_dtype == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
     a.out_dtype = out_dtype == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
+    a.tau_stats = (int64_t *)workspace;
     return from_hip(hstu::launch_attn_fwd(a, (hipStream_t)stream), "attn_fwd launch");
   } catch (...) {
     return fail(HSTU_ERR_DEVICE, "unexpected C++ exception in hstu_attn_fwd");
@@ -192,7 +198,8 @@ size_t hstu_layer_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc
                                   const hstu_layer_weights_t *w, hstu_dtype_t dtype) {
   if (!jag || !desc || !w || jag->total_tokens < 0 || desc->num_heads < 1 || desc->head_dim < 1 || w->d_model < 1)
     return 0;
-  return layer_ws(jag->total_tokens, (int64_t)desc->num_heads * desc->head_dim, w->d_model, dtype, w->ln_output != 0,
+  return layer_ws(jag->total_tokens, jag->num_seqs, (int64_t)desc->num_heads * desc->head_dim, w->d_model, dtype,
+                  w->ln_output != 0,
                   dtype == HSTU_BF16 && w->act_split != 0)
       .total;
 }
@@ -219,7 +226,7 @@ hstu_status_t hstu_layer_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
     if (!aligned16(w->w_uvqk) || !aligned16(w->w_out))
       return fail(HSTU_ERR_INVALID_ARGUMENT, "weights must be 16-byte aligned");
     const bool split = dtype == HSTU_BF16 && w->act_split != 0;
-    const LayerWs ws = layer_ws(T, HD, D, dtype, w->ln_output != 0, split);
+    const LayerWs ws = layer_ws(T, jag->num_seqs, HD, D, dtype, w->ln_output != 0, split);
     if (workspace_bytes < ws.total)
       return fail(HSTU_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, ws.total);
     if (T == 0) return ok();
@@ -249,6 +256,7 @@ hstu_status_t hstu_layer_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
     a.q = wsb + ws.q; a.k = wsb + ws.k; a.v = wsb + ws.v; a.out = wsb + ws.o;
     a.row_stride = HD; a.out_row_stride = HD;
     a.in_dtype = dt; a.out_dtype = hstu::kF32;
+    a.tau_stats = (int64_t *)(wsb + ws.stats);
     e = hstu::launch_attn_fwd(a, s);
     if (e != hipSuccess) return from_hip(e, "attention launch");
 

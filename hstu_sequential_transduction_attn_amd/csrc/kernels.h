@@ -27,8 +27,11 @@ struct AttnArgs {
   int32_t num_pos_buckets, num_time_buckets, rab_rows;
   int32_t mask;
   int32_t in_dtype, out_dtype;
+  int64_t *tau_stats;             // workspace: attn_tau_stats_bytes() of per-32-token timestamp ranges
 };
 
+// Workspace bytes of the per-32-token timestamp ranges the attention kernel classifies tiles with.
+size_t attn_tau_stats_bytes(int64_t total_tokens, int64_t num_seqs);
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream);
 
 // C[M][N] = epilogue(A[M][K] * B[N][K]^T): bf16 or f32 weights (MFMA operand type `dtype`), fp32

@@ -30,7 +30,7 @@ def _desc(H=4, Dh=128, P=32, Tb=32, R=1, mask=0):
 
 
 def _attn(jag, desc, in_dt=L.HSTU_BF16, out_dt=L.HSTU_BF16, q=P16 + 0x10000, k=P16 + 0x20000000,
-          v=P16 + 0x40000000, out=P16 + 0x60000000, ws=None, nws=0):
+          v=P16 + 0x40000000, out=P16 + 0x60000000, ws=P16 + 0x80000000, nws=1 << 20):
     lib = _lib()
     st = lib.hstu_attn_fwd(ctypes.byref(jag) if jag else None, ctypes.byref(desc) if desc else None, in_dt, q, k, v,
                            out, out_dt, ws, nws, None)
@@ -81,8 +81,21 @@ def test_attn_argument_errors():
 
 
 def test_attn_zero_tokens_is_a_no_op():
-    st, msg = _attn(L.JaggedT(3, 0, 0, P16, None, None, None), _desc(), q=None, k=None, v=None, out=None)
+    jag = L.JaggedT(3, 0, 0, P16, None, None, None)
+    assert _lib().hstu_attn_workspace_bytes(ctypes.byref(jag), ctypes.byref(_desc()), L.HSTU_BF16) == 0
+    st, msg = _attn(jag, _desc(), q=None, k=None, v=None, out=None, ws=None, nws=0)
     assert st == OK and msg == ""
+
+
+def test_attn_workspace_checks():
+    jag = _jag(B=3, T=1000, max_len=600)
+    need = _lib().hstu_attn_workspace_bytes(ctypes.byref(jag), ctypes.byref(_desc()), L.HSTU_BF16)
+    assert need >= ((1000 >> 5) + 3 + 1) * 16 and need % 256 == 0
+    st, msg = _attn(jag, _desc(), nws=need - 1)
+    assert st == WS_SMALL and str(need) in msg
+    assert _attn(jag, _desc(), ws=None, nws=need)[0] == INVALID
+    assert _attn(jag, _desc(), ws=P16 + 8, nws=need)[0] == INVALID                # misaligned
+    assert _attn(jag, _desc(), ws=P16 + 0x10000 + 256, nws=need)[0] == INVALID    # overlaps q
 
 
 def test_layer_argument_errors():
