@@ -10,19 +10,28 @@
 // normaliser: partial sums over key tiles simply add.
 //
 // Kernel shape.  A workgroup is 4 waves; each wave owns 32 consecutive queries of one (sequence, head),
-// so a workgroup covers 128 queries.  Key tiles of 64 rows are staged through LDS (double buffered,
-// one barrier per tile) and shared by the 4 waves.  Both contractions run on 32x32 MFMA tiles in a
-// transposed form:
+// so a workgroup covers 128 queries and shares every key tile among its 4 waves.  Two workgroups share
+// a CU (two waves per SIMD, from different workgroups, so that their MFMA and VALU phases drift apart
+// instead of running in lock-step behind one barrier).  Key tiles of 64 rows (K, V and their
+// timestamps) go global -> LDS with direct-to-LDS loads (global_load_lds_dwordx4: no registers, no
+// VALU) into a ring of LDS stages, issued ahead; one barrier per tile.  Both contractions run on 32x32 MFMA tiles in a transposed form:
 //     S^T[key][query] = K . Q^T        (A = K rows from LDS, B = Q held in registers)
 //     O^T[dh][query] += V^T . P^T      (A = V^T read with ds_read_b64_tr_b16, B = P from registers)
 // The score accumulator of the first product is already laid out as the B operand of the second:
-// lane l always holds query l%32.  K rows are stored in LDS in a permuted order so that the keys a
-// lane holds in its 16 accumulator values are two runs of 8 consecutive keys, which is exactly the
-// k-order the second MFMA expects.  V stays in its natural [key][dh] layout; the transpose read hands
-// each lane 4 consecutive keys of one dh column.
+// lane l always holds query l%32.  The first product reads its K rows in a permuted order (row m of the
+// MFMA is key kperm(m)) so that the keys a lane holds in its 16 accumulator values are two runs of 8
+// consecutive keys, which is exactly the k-order the second MFMA expects.  The transpose read hands each
+// lane 4 consecutive keys of one dh column of V.
 //
-// Bias and mask.  Per (wave, key tile) the work is classified from index ranges and from timestamp
-// ranges (per-32-token minimum and maximum, computed by a small prologue kernel):
+// LDS tile layout.  A K or V tile is stored column-group-major: the row's bytes are cut into 64-byte
+// groups, and group g of key r sits at ((g * 64 + r) * 64).  One 1 KB direct-to-LDS load fills 16 rows of
+// one group (four lanes per 64-byte line of the source); the V transpose reads of 16 lanes cover 4 rows x
+// 32 bytes in distinct banks; in K, the four 16-byte pieces of a group are XOR-permuted by bits 2..3 of
+// the row, so that the 16 rows one K-operand read touches land in 16 distinct bank groups.  All operand
+// addresses are one or two per-lane registers plus immediate offsets.
+//
+// Bias and mask.  Per (wave, key tile) the work is classified, in scalar registers, from index ranges
+// and from timestamp ranges (per-32-token minimum and maximum, computed by a small prologue kernel):
 //   none      - no allowed pair: skipped;
 //   uniform   - every pair allowed, one position bucket and one time bucket: a single bias constant;
 //   two       - every pair allowed, one position bucket, the time bucket is one of two adjacent
@@ -38,13 +47,21 @@
 namespace hstu {
 namespace {
 
-constexpr int kWaves = 4;
+#ifndef HSTU_ATTN_WAVES
+#define HSTU_ATTN_WAVES 4
+#endif
+#ifndef HSTU_ATTN_RING_KB
+#define HSTU_ATTN_RING_KB 68
+#endif
+constexpr int kWaves = HSTU_ATTN_WAVES;
 constexpr int kQW = 32;                  // queries per wave
 constexpr int kBM = kWaves * kQW;        // queries per workgroup
 constexpr int kBN = 64;                  // keys per LDS tile
 constexpr int kThreads = kWaves * kWave;
 constexpr int kTimeTab = 65;             // a 64-bit gap has bit length 0..64
 constexpr int kChunk = 32;               // tokens per timestamp-range chunk
+constexpr int kRingBudget = HSTU_ATTN_RING_KB * 1024;  // LDS for the stage ring (bias tables: <= 16.6 KB more)
+constexpr int kTauLanes = 128 / kWaves;  // lanes per wave that load the tile's 64 timestamps (4 bytes each)
 
 enum Mode : int { kUniform = 0, kTwo = 1, kGen32 = 2, kGen64 = 3 };
 
@@ -61,21 +78,32 @@ template <typename T, int DH>
 struct Layout {
   static constexpr bool kBf16 = sizeof(T) == 2;
   static constexpr int kES = sizeof(T);
-  static constexpr int kKStride = kBf16 ? DH * 2 + 16 : (DH + 1) * 4;   // bytes per K row in LDS
-  static constexpr int kVStride = kBf16 ? DH * 2 + 32 : DH * 4;         // bytes per V row in LDS
-  static constexpr int kChunksPerRow = DH * kES / 16;
-  static constexpr int kChunksPerThread = kBN * kChunksPerRow / kThreads;
+  static constexpr int kRB = DH * kES;                 // bytes of one K or V row
+  static constexpr int kCPR = kRB / 16;                // 16-byte chunks per row
+  static constexpr int kTileBytes = kBN * kRB;
   static constexpr int kOffK = 0;
-  static constexpr int kOffV = kOffK + kBN * kKStride;
-  static constexpr int kOffTauLo = (kOffV + kBN * kVStride + 15) & ~15;
-  static constexpr int kOffTauHi = kOffTauLo + kBN * 4;
-  static constexpr int kStageBytes = kOffTauHi + kBN * 4;
+  static constexpr int kOffV = kTileBytes;
+  static constexpr int kOffTau = 2 * kTileBytes;       // kBN int64 timestamps
+  static constexpr int kStageBytes = 2 * kTileBytes + kBN * 8;
+  static constexpr int kFit = kRingBudget / kStageBytes;
+  static constexpr int kStages = kFit >= 4 ? 4 : (kFit >= 2 ? kFit : 2);   // at least double-buffered
+  static constexpr int kInstPerOperand = kBN * kCPR / kWave;          // 1 KB wave loads per K or V tile
+  static constexpr int kInstPerWave = 2 * kInstPerOperand / kWaves;   // K and V loads per wave per tile
+  static constexpr int kLoadsPerTile = kInstPerWave + 1;              // + the timestamp load
   static constexpr int kKPL = kBf16 ? 8 : 1;                 // operand values per lane per MFMA
   static constexpr int kKStep = kBf16 ? 16 : 2;              // k per MFMA
   static constexpr int kQSteps = DH / kKStep;                // MFMAs per 32x32 score block
   static constexpr int kDB = DH / 32;                        // 32-row dh blocks of O^T
-  static_assert(kChunksPerThread >= 1 && kBN * kChunksPerRow % kThreads == 0, "staging split");
+  static_assert(kStages >= 2, "ring");
+  static_assert(kInstPerWave >= 1 && 2 * kInstPerOperand % kWaves == 0, "staging split");
   static_assert(kStageBytes % 16 == 0, "stage alignment");
+  static constexpr int kG = kRB / 64;                                  // 64-byte column groups per row
+  static_assert(kRB % 64 == 0, "rows of whole 64-byte groups");
+  // LDS byte offset of byte b of row r in a V tile, and in a K tile (16-byte pieces XOR-permuted)
+  __device__ static int v_at(int r, int b) { return (((b >> 6) * 64 + r) << 6) + (b & 63); }
+  __device__ static int k_at(int r, int b) {
+    return (((b >> 6) * 64 + r) << 6) + ((((b >> 4) & 3) ^ ((r >> 2) & 3)) << 4) + (b & 15);
+  }
 };
 
 // The O^T accumulators of one wave: N blocks of 32 dh rows x 32 queries.
@@ -91,6 +119,25 @@ template <> struct QFrag<float> { using type = float; };
 __device__ __forceinline__ int bitlen_u64(uint64_t d) { return d == 0 ? 0 : 64 - __clzll((long long)d); }
 __device__ __forceinline__ int bitlen_u32(uint32_t d) { return 32 - __clz((int)d); }  // __clz(0) = 32
 
+// 16 bytes (or 4 bytes) from global memory at base + lane_off straight into LDS at lds_base + 16 * lane
+// (4 * lane); base is a wave-uniform 64-bit address, lane_off a 32-bit per-lane offset.  Issued as inline
+// assembly so that the waits for these loads are exactly the explicit vmcnt waits of the ring: a wait the
+// compiler inserted itself before LDS reads would not know that they read another stage.
+__device__ __forceinline__ void dma16(const void *base, uint32_t lane_off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(lds_base), "v"(lane_off), "s"(base)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const void *base, uint32_t lane_off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" : : "s"(lds_base), "v"(lane_off), "s"(base)
+               : "memory");
+}
+// s_waitcnt with only the vector-memory counter constrained (expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // Per-wave constants of the score pointwise work for one tile.
 struct TileCtx {
   int k0;              // first key of the tile (sequence-local)
@@ -104,7 +151,7 @@ struct TileCtx {
   uint32_t thr;        // two-bucket mode: |dt| >= thr selects bias_hi
   float cbias, bias_lo, bias_hi;
   const HSTU_LDS float *wp, *wt;
-  const HSTU_LDS uint32_t *tlo, *thi;   // the tile's timestamps, low and high words
+  const HSTU_LDS int64_t *tau;   // the tile's timestamps
 };
 
 // SiLU(score + bias) for the 16 scores of one 32-key block kb; element e holds key
@@ -119,13 +166,10 @@ __device__ __forceinline__ void pointwise(const floatx16 &s, float (&a)[16], con
     for (int g = 0; g < 2; ++g) {
       const int jl0 = 32 * kb + 16 * g + 8 * half;   // tile-local key of element 8*g
       uint32_t lo[8], hi[8];
-      {
-        const u32x4 l0 = *(const HSTU_LDS u32x4 *)(c.tlo + jl0), l1 = *(const HSTU_LDS u32x4 *)(c.tlo + jl0 + 4);
-        lo[0] = l0.x; lo[1] = l0.y; lo[2] = l0.z; lo[3] = l0.w; lo[4] = l1.x; lo[5] = l1.y; lo[6] = l1.z; lo[7] = l1.w;
-      }
-      if constexpr (MODE == kGen64) {
-        const u32x4 h0 = *(const HSTU_LDS u32x4 *)(c.thi + jl0), h1 = *(const HSTU_LDS u32x4 *)(c.thi + jl0 + 4);
-        hi[0] = h0.x; hi[1] = h0.y; hi[2] = h0.z; hi[3] = h0.w; hi[4] = h1.x; hi[5] = h1.y; hi[6] = h1.z; hi[7] = h1.w;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 w = *(const HSTU_LDS u32x4 *)(c.tau + jl0 + 2 * q);
+        lo[2 * q] = w.x; hi[2 * q] = w.y; lo[2 * q + 1] = w.z; hi[2 * q + 1] = w.w;
       }
 #pragma unroll
       for (int e8 = 0; e8 < 8; ++e8) {
@@ -166,14 +210,15 @@ template <typename T, int DH>
 __device__ __forceinline__ void score_block(floatx16 &s, const HSTU_LDS char *lK, int kb, int l32, int half,
                                             const typename QFrag<T>::type (&qf)[Layout<T, DH>::kQSteps]) {
   using L = Layout<T, DH>;
+  const int r = 32 * kb + kperm(l32);   // MFMA row l32 takes key kperm(l32) of this 32-key block
   s = floatx16{};
 #pragma unroll
   for (int st = 0; st < L::kQSteps; ++st) {
     if constexpr (L::kBf16) {
-      const bf16x8 kf = *(const HSTU_LDS bf16x8 *)(lK + (32 * kb + l32) * L::kKStride + (16 * st + 8 * half) * 2);
+      const bf16x8 kf = *(const HSTU_LDS bf16x8 *)(lK + L::k_at(r, (16 * st + 8 * half) * 2));
       s = mfma32(kf, qf[st], s);
     } else {
-      const float kf = *(const HSTU_LDS float *)(lK + (32 * kb + l32) * L::kKStride + (2 * st + half) * 4);
+      const float kf = *(const HSTU_LDS float *)(lK + L::k_at(r, (2 * st + half) * 4));
       s = mfma32(kf, qf[st], s);
     }
   }
@@ -191,14 +236,12 @@ __device__ __forceinline__ void av_block(OAcc<Layout<T, DH>::kDB> &oacc, const f
 #pragma unroll
       for (int e = 0; e < 8; ++e) pf[e] = f32_to_bf16(a[8 * s2 + e]);
       const int g16 = lane >> 4, i16 = lane & 15;
-      const int krow = 32 * kb + 16 * s2 + 8 * half + (i16 >> 2);
+      const int r0 = 32 * kb + 16 * s2 + 8 * half + (i16 >> 2);
 #pragma unroll
       for (int db = 0; db < L::kDB; ++db) {
-        const int col = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
-        const shortx4 v0 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((HSTU_LDS shortx4 *)(lV + krow * L::kVStride + col * 2));
-        const shortx4 v1 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((HSTU_LDS shortx4 *)(lV + (krow + 4) * L::kVStride + col * 2));
+        const int b = (32 * db + 16 * (g16 & 1) + 4 * (i16 & 3)) * 2;
+        const shortx4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HSTU_LDS shortx4 *)(lV + L::v_at(r0, b)));
+        const shortx4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HSTU_LDS shortx4 *)(lV + L::v_at(r0 + 4, b)));
         const bf16x4 w0 = __builtin_bit_cast(bf16x4, v0), w1 = __builtin_bit_cast(bf16x4, v1);
         bf16x8 vf;
         vf[0] = w0[0]; vf[1] = w0[1]; vf[2] = w0[2]; vf[3] = w0[3];
@@ -209,10 +252,10 @@ __device__ __forceinline__ void av_block(OAcc<Layout<T, DH>::kDB> &oacc, const f
   } else {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int krow = 32 * kb + 16 * (e / 8) + 8 * half + (e % 8);
+      const int r = 32 * kb + 16 * (e / 8) + 8 * half + (e % 8);
 #pragma unroll
       for (int db = 0; db < L::kDB; ++db) {
-        const float vf = *(const HSTU_LDS float *)(lV + krow * L::kVStride + (32 * db + l32) * 4);
+        const float vf = *(const HSTU_LDS float *)(lV + L::v_at(r, (32 * db + l32) * 4));
         oacc.d[db] = mfma32(vf, a[e], oacc.d[db]);
       }
     }
@@ -267,6 +310,7 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   using Frag = typename QFrag<T>::type;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   HSTU_LDS char *smem = (HSTU_LDS char *)smem_raw;
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
   // ---- work item: query block major (longest first), then (sequence, head)
   const int HB = p.num_heads * p.num_seqs;
@@ -287,15 +331,15 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   const int64_t *cstats = p.tau_stats + 2 * (int64_t)((o0 >> 5) + b);   // chunk c at cstats[2c], [2c+1]
 
   const int tid = threadIdx.x;
-  // wave index as a scalar: everything derived from it (query range, tile classes) stays wave-uniform,
-  // so the per-tile class selects one body with a scalar branch instead of predicating all of them
-  const int wave = tid / kWave;
+  // wave index in a scalar register: the query range and the tile classes derived from it are
+  // wave-uniform, so each tile runs exactly one class body, selected by a scalar branch
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  // ---- bias tables into LDS (after the two pipeline stages)
-  HSTU_LDS float *wp_lds = (HSTU_LDS float *)(smem + 2 * L::kStageBytes);
+  // ---- bias tables into LDS (after the stage ring)
+  HSTU_LDS float *wp_lds = (HSTU_LDS float *)(smem + L::kStages * L::kStageBytes);
   HSTU_LDS float *wt_lds = wp_lds + P;
   for (int i = tid; i < P; i += kThreads) wp_lds[i] = p.pos_bias[(int64_t)rr * P + i];
   const int nt_tab = imin(Tb, kTimeTab);
@@ -335,51 +379,52 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
     r2_begin = imax(imax(q0, nh) / kBN, r1_end);
     r2_end = blast / kBN + 1;
   }
-  auto next_tile = [&](int t) -> int {
-    ++t;
-    if (t < r1_end) return t;
-    if (t < r2_begin) t = r2_begin;
-    return t < r2_end ? t : -1;
-  };
-  int tile = r1_end > 0 ? 0 : (r2_begin < r2_end ? r2_begin : -1);
+  const int ntiles = r1_end + imax(r2_end - r2_begin, 0);
+  auto tile_of = [&](int i) -> int { return i < r1_end ? i : r2_begin + (i - r1_end); };
 
-  // ---- staging of one key tile: global -> registers -> LDS
-  u32x4 kreg[L::kChunksPerThread], vreg[L::kChunksPerThread];
-  int64_t treg = 0;
-  auto load_tile = [&](int t) {
-    const int k0 = t * kBN;
+  // ---- direct-to-LDS staging.  Per tile, wave w issues kInstPerWave 1 KB loads: instruction iota fills
+  // block blk = iota % kInstPerOperand of operand iota / kInstPerOperand (K, then V): column group blk / 4,
+  // rows 16 * (blk % 4) .. +15, lane l taking row l / 4 of the block and 16-byte piece l % 4 of the group
+  // (K: the piece whose XOR-permuted position is l % 4).  The per-lane part of every source address is
+  // one register per operand; rows past the end of the sequence load its last row instead (finite data
+  // that the mask discards).  Timestamps: lanes 0..kTauLanes-1 of every wave load 4 bytes each.
+  const int64_t rsb = p.row_stride * L::kES;                  // bytes between tokens
+  const int lane_row = lane >> 2;
+  const uint32_t v_lane_off = (uint32_t)(lane_row * rsb + (lane & 3) * 16 + h * L::kRB);
+  const uint32_t k_lane_off = (uint32_t)(lane_row * rsb + ((lane & 3) ^ ((lane >> 4) & 3)) * 16 + h * L::kRB);
+  const uint32_t tau_lane_off = 4u * (uint32_t)(kTauLanes * wave + (lane % kTauLanes));
+  const char *kbase = (const char *)p.k, *vbase = (const char *)p.v;
+  auto issue_tile = [&](int i, int stage) {
+    const int k0 = tile_of(i) * kBN;
+    const uint32_t sbase = smem_addr + stage * L::kStageBytes;
+    const bool tail = k0 + kBN > n;
 #pragma unroll
-    for (int c = 0; c < L::kChunksPerThread; ++c) {
-      const int chunk = tid + c * kThreads;
-      const int row = chunk / L::kChunksPerRow, col = chunk % L::kChunksPerRow;
-      const bool ok = k0 + row < n;
-      const int64_t off = (int64_t)(o0 + (ok ? k0 + row : 0)) * p.row_stride * L::kES + (int64_t)h * DH * L::kES +
-                          col * 16;
-      const u32x4 kv = *(const u32x4 *)((const char *)p.k + off);
-      const u32x4 vv = *(const u32x4 *)((const char *)p.v + off);
-      kreg[c] = ok ? kv : u32x4{0u, 0u, 0u, 0u};
-      vreg[c] = ok ? vv : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (tid < kBN) treg = (k0 + tid < n) ? p.timestamps[o0 + k0 + tid] : 0;
-  };
-  auto store_tile = [&](int stage) {
-    HSTU_LDS char *base = smem + stage * L::kStageBytes;
-#pragma unroll
-    for (int c = 0; c < L::kChunksPerThread; ++c) {
-      const int chunk = tid + c * kThreads;
-      const int row = chunk / L::kChunksPerRow, col = chunk % L::kChunksPerRow;
-      HSTU_LDS char *kdst = base + L::kOffK + kperm(row) * L::kKStride + col * 16;
-      if constexpr (L::kBf16) {
-        *(HSTU_LDS u32x4 *)kdst = kreg[c];
+    for (int j = 0; j < L::kInstPerWave; ++j) {
+      const int iota = wave * L::kInstPerWave + j;
+      const bool is_v = iota >= L::kInstPerOperand;
+      const int blk = iota % L::kInstPerOperand;
+      const int row0 = k0 + 16 * (blk & 3);                   // first key of this instruction
+      const int64_t col = 64 * (blk >> 2);                    // byte offset of its column group
+      const uint32_t lane_off = is_v ? v_lane_off : k_lane_off;
+      const uint32_t lds = sbase + (is_v ? L::kOffV : L::kOffK) + blk * 1024;
+      if (!tail) {
+        dma16((is_v ? vbase : kbase) + (int64_t)(o0 + row0) * rsb + col, lane_off, lds);
       } else {
-        HSTU_LDS uint32_t *d = (HSTU_LDS uint32_t *)kdst;
-        d[0] = kreg[c].x; d[1] = kreg[c].y; d[2] = kreg[c].z; d[3] = kreg[c].w;
+        // clamp the instruction's base row as well, so that the per-lane offset stays non-negative
+        const int base_row = imin(row0, n - 1);
+        const int key = imin(row0 + lane_row, n - 1);
+        dma16((is_v ? vbase : kbase) + (int64_t)(o0 + base_row) * rsb + col,
+              (uint32_t)((key - base_row) * rsb) + (lane_off - (uint32_t)(lane_row * rsb)), lds);
       }
-      *(HSTU_LDS u32x4 *)(base + L::kOffV + row * L::kVStride + col * 16) = vreg[c];
     }
-    if (tid < kBN) {
-      ((HSTU_LDS uint32_t *)(base + L::kOffTauLo))[tid] = (uint32_t)(uint64_t)treg;
-      ((HSTU_LDS uint32_t *)(base + L::kOffTauHi))[tid] = (uint32_t)((uint64_t)treg >> 32);
+    {
+      const char *src = (const char *)(p.timestamps + o0 + k0);
+      uint32_t off = tau_lane_off;
+      if (tail) {
+        const int d = kTauLanes * wave + (lane % kTauLanes);
+        off = 8u * (uint32_t)(imin(k0 + (d >> 1), n - 1) - k0) + 4u * (uint32_t)(d & 1);
+      }
+      if (lane < kTauLanes) dma4(src, off, sbase + L::kOffTau + 4 * kTauLanes * wave);
     }
   };
 
@@ -399,18 +444,23 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   c.wp = wp_lds;
   c.wt = wt_lds;
 
-  int stage = 0;
-  if (tile >= 0) {
-    load_tile(tile);
-    store_tile(0);
-  }
-  __syncthreads();
+  constexpr int kAhead = L::kStages - 1;      // tiles in flight beyond the one being computed
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i)
+    if (i < ntiles) issue_tile(i, i);
 
-  while (tile >= 0) {
-    const int nxt = next_tile(tile);
-    if (nxt >= 0) load_tile(nxt);
+  for (int i = 0; i < ntiles; ++i) {
+    // tile i has landed once at most (tiles issued after it) x (loads per tile) loads are outstanding
+    const int after = imin(kAhead - 1, ntiles - 1 - i);
+    if (after >= 2) wait_vmcnt<2 * L::kLoadsPerTile>();
+    else if (after == 1) wait_vmcnt<L::kLoadsPerTile>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // tile i visible to all waves; every wave is done with tile i - 1
+    if (i + kAhead < ntiles) issue_tile(i + kAhead, (i + kAhead) % L::kStages);
+
+    const int stage = i % L::kStages;
     const HSTU_LDS char *base = smem + stage * L::kStageBytes;
-    const int k0 = tile * kBN;
+    const int k0 = tile_of(i) * kBN;
 
     const bool none = !wave_active || k0 > ql || (k0 >= nh && (k0 + kBN - 1 < imax(qa, nh)));
     if (!none) {
@@ -426,8 +476,7 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
       const int64_t tmax = wmax > kmax ? wmax : kmax;
       const uint64_t span = (uint64_t)tmax - (uint64_t)tmin;
       c.k0 = k0;
-      c.tlo = (const HSTU_LDS uint32_t *)(base + L::kOffTauLo);
-      c.thi = (const HSTU_LDS uint32_t *)(base + L::kOffTauHi);
+      c.tau = (const HSTU_LDS int64_t *)(base + L::kOffTau);
       c.base_lo = (uint32_t)(uint64_t)tmin;
       c.qoff = (uint32_t)(uint64_t)my_tau - c.base_lo;
       const HSTU_LDS char *lK = base + L::kOffK;
@@ -470,11 +519,6 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
         else tile_body<T, DH, kGen64, true>(oacc, qf, lK, lV, c, lane);
       }
     }
-
-    if (nxt >= 0) store_tile(stage ^ 1);
-    __syncthreads();
-    stage ^= 1;
-    tile = nxt;
   }
 
   // ---- epilogue: O^T element e of dh block db is dh = 32*db + 8*(e/4) + 4*half + e%4
@@ -508,7 +552,7 @@ hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
   const long long grid = (long long)n_qblocks * a.num_heads * a.num_seqs;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const size_t lds = 2 * L::kStageBytes + (size_t)(a.num_pos_buckets + kTimeTab) * sizeof(float);
+  const size_t lds = (size_t)L::kStages * L::kStageBytes + (size_t)(a.num_pos_buckets + kTimeTab) * sizeof(float);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_kernel<T, DH, TO>,
