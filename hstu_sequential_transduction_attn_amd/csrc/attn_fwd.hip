@@ -14,7 +14,11 @@
 // a CU (two waves per SIMD, from different workgroups, so that their MFMA and VALU phases drift apart
 // instead of running in lock-step behind one barrier).  Key tiles of 64 rows (K, V and their
 // timestamps) go global -> LDS with direct-to-LDS loads (global_load_lds_dwordx4: no registers, no
-// VALU) into a ring of LDS stages, issued ahead; one barrier per tile.  Both contractions run on 32x32 MFMA tiles in a transposed form:
+// VALU) into a two-stage LDS ring; one barrier per tile.  Wave w loads rows 16w..16w+15 of every K and
+// V column group and the timestamps of those 16 keys, so its per-lane source offsets are three
+// registers per tile, clamped at the end of the sequence without a branch.
+//
+// Both contractions run on 32x32 MFMA tiles in a transposed form:
 //     S^T[key][query] = K . Q^T        (A = K rows from LDS, B = Q held in registers)
 //     O^T[dh][query] += V^T . P^T      (A = V^T read with ds_read_b64_tr_b16, B = P from registers)
 // The score accumulator of the first product is already laid out as the B operand of the second:
@@ -27,11 +31,16 @@
 // groups, and group g of key r sits at ((g * 64 + r) * 64).  One 1 KB direct-to-LDS load fills 16 rows of
 // one group (four lanes per 64-byte line of the source); the V transpose reads of 16 lanes cover 4 rows x
 // 32 bytes in distinct banks; in K, the four 16-byte pieces of a group are XOR-permuted by bits 2..3 of
-// the row, so that the 16 rows one K-operand read touches land in 16 distinct bank groups.  All operand
-// addresses are one or two per-lane registers plus immediate offsets.
+// the row, so that the 16 rows one K-operand read touches land in 16 distinct bank groups.
 //
-// Bias and mask.  Per (wave, key tile) the work is classified, in scalar registers, from index ranges
-// and from timestamp ranges (per-32-token minimum and maximum, computed by a small prologue kernel):
+// SiLU with the exponent scale folded in.  With u = -log2(e) * x, SiLU(x) = x / (1 + 2^u) =
+// -ln(2) * u / (1 + 2^u).  The kernel forms u = fma(s, -log2 e, c1) directly (c1 = -log2(e) * bias for
+// a tile with a single bias, else 0 with the bias already added to s), accumulates u / (1 + 2^u) and
+// applies -ln(2) once, with c_b, to the output: one FMA, exp2, add, reciprocal and multiply per score.
+//
+// Bias and mask.  Per (wave, key tile) the work is classified from index ranges and from timestamp
+// ranges (per-32-token minimum and maximum, computed by a small prologue kernel).  Each wave classifies
+// 64 of its tiles at a time, one per lane, and reads a tile's class with readlane:
 //   none      - no allowed pair: skipped;
 //   uniform   - every pair allowed, one position bucket and one time bucket: a single bias constant;
 //   two       - every pair allowed, one position bucket, the time bucket is one of two adjacent
@@ -39,71 +48,63 @@
 //               (v_sad_u32), one compare and one select per score;
 //   general   - per-score mask and bucket lookups in LDS (32-bit offsets when the span allows,
 //               exact 64-bit differences otherwise).
-// Each class has its own branch-free body; the two score blocks of a tile are ordered so that one
-// block's SiLU work overlaps the other's MFMAs.
+// All classes share one tile body: the MFMA code and the SiLU are common, and the classes other than
+// uniform add their per-score bias (and the mask) to the score accumulators in place, in a branch of
+// their own, so that the output accumulators never change registers between classes.
 #include "device_common.hpp"
 #include "kernels.h"
 
 namespace hstu {
 namespace {
 
-#ifndef HSTU_ATTN_WAVES
-#define HSTU_ATTN_WAVES 4
-#endif
-#ifndef HSTU_ATTN_RING_KB
-#define HSTU_ATTN_RING_KB 68
-#endif
-constexpr int kWaves = HSTU_ATTN_WAVES;
+constexpr int kWaves = 4;
 constexpr int kQW = 32;                  // queries per wave
 constexpr int kBM = kWaves * kQW;        // queries per workgroup
 constexpr int kBN = 64;                  // keys per LDS tile
 constexpr int kThreads = kWaves * kWave;
 constexpr int kTimeTab = 65;             // a 64-bit gap has bit length 0..64
 constexpr int kChunk = 32;               // tokens per timestamp-range chunk
-constexpr int kRingBudget = HSTU_ATTN_RING_KB * 1024;  // LDS for the stage ring (bias tables: <= 16.6 KB more)
-constexpr int kTauLanes = 128 / kWaves;  // lanes per wave that load the tile's 64 timestamps (4 bytes each)
+constexpr int kRingBudget = 68 * 1024;   // LDS for the stage ring: two workgroups per CU
+constexpr float kNegLog2e = -1.4426950408889634f;
+constexpr float kNegLn2 = -0.6931471805599453f;
+static_assert(kWaves * 16 == kBN, "each wave stages 16 rows of a tile");
 
-enum Mode : int { kUniform = 0, kTwo = 1, kGen32 = 2, kGen64 = 3 };
+// Tile classes.  A class code is body | (low time bucket << 8).
+enum Body : int { kNone = 0, kUniform = 1, kTwo = 2, kGen32 = 3, kGen64 = 4, kGen32M = 5, kGen64M = 6 };
 
 // Row order of K inside each 32-row block of LDS: row r holds key kperm(r) (an involution swapping
-// rows 4..7 with 8..11 and 20..23 with 24..27).  With it, accumulator element e of lane half hf holds
+// rows 4..7 with 8..11 and 20..23 with 24..27, i.e. bits 2 and 3 of r).  With it, accumulator element e of lane half hf holds
 // key 16*(e/8) + 8*hf + e%8.
-__device__ __forceinline__ int kperm(int r) {
-  const int g = (r >> 2) & 7;
-  const int ng = (g == 1) ? 2 : (g == 2) ? 1 : (g == 5) ? 6 : (g == 6) ? 5 : g;
-  return (r & ~31) | (ng << 2) | (r & 3);
-}
+__device__ __forceinline__ int kperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 template <typename T, int DH>
 struct Layout {
   static constexpr bool kBf16 = sizeof(T) == 2;
   static constexpr int kES = sizeof(T);
   static constexpr int kRB = DH * kES;                 // bytes of one K or V row
-  static constexpr int kCPR = kRB / 16;                // 16-byte chunks per row
+  static constexpr int kG = kRB / 64;                  // 64-byte column groups per row
   static constexpr int kTileBytes = kBN * kRB;
   static constexpr int kOffK = 0;
   static constexpr int kOffV = kTileBytes;
-  static constexpr int kOffTau = 2 * kTileBytes;       // kBN int64 timestamps
-  static constexpr int kStageBytes = 2 * kTileBytes + kBN * 8;
+  static constexpr int kOffTau = 2 * kTileBytes;       // wave w's 16 timestamps at 256*w (+128 B unused)
+  static constexpr int kStageBytes = 2 * kTileBytes + kWaves * 256;
   static constexpr int kFit = kRingBudget / kStageBytes;
   static constexpr int kStages = kFit >= 4 ? 4 : (kFit >= 2 ? kFit : 2);   // at least double-buffered
-  static constexpr int kInstPerOperand = kBN * kCPR / kWave;          // 1 KB wave loads per K or V tile
-  static constexpr int kInstPerWave = 2 * kInstPerOperand / kWaves;   // K and V loads per wave per tile
-  static constexpr int kLoadsPerTile = kInstPerWave + 1;              // + the timestamp load
-  static constexpr int kKPL = kBf16 ? 8 : 1;                 // operand values per lane per MFMA
-  static constexpr int kKStep = kBf16 ? 16 : 2;              // k per MFMA
-  static constexpr int kQSteps = DH / kKStep;                // MFMAs per 32x32 score block
-  static constexpr int kDB = DH / 32;                        // 32-row dh blocks of O^T
+  static constexpr int kLoadsPerTile = 2 * kG + 1;     // per wave: K and V column groups, timestamps
+  static constexpr int kKPL = kBf16 ? 8 : 1;           // operand values per lane per MFMA
+  static constexpr int kKStep = kBf16 ? 16 : 2;        // k per MFMA
+  static constexpr int kQSteps = DH / kKStep;          // MFMAs per 32x32 score block
+  static constexpr int kDB = DH / 32;                  // 32-row dh blocks of O^T
   static_assert(kStages >= 2, "ring");
-  static_assert(kInstPerWave >= 1 && 2 * kInstPerOperand % kWaves == 0, "staging split");
-  static_assert(kStageBytes % 16 == 0, "stage alignment");
-  static constexpr int kG = kRB / 64;                                  // 64-byte column groups per row
   static_assert(kRB % 64 == 0, "rows of whole 64-byte groups");
+  static_assert(kStageBytes % 16 == 0, "stage alignment");
   // LDS byte offset of byte b of row r in a V tile, and in a K tile (16-byte pieces XOR-permuted)
   __device__ static int v_at(int r, int b) { return (((b >> 6) * 64 + r) << 6) + (b & 63); }
   __device__ static int k_at(int r, int b) {
     return (((b >> 6) * 64 + r) << 6) + ((((b >> 4) & 3) ^ ((r >> 2) & 3)) << 4) + (b & 15);
   }
+  // LDS byte offset (from the stage) of the timestamp of tile-local key j
+  __device__ static int tau_at(int j) { return kOffTau + 256 * (j >> 4) + 8 * (j & 15); }
 };
 
 // The O^T accumulators of one wave: N blocks of 32 dh rows x 32 queries.
@@ -116,20 +117,33 @@ template <typename T> struct QFrag;
 template <> struct QFrag<__bf16> { using type = bf16x8; };
 template <> struct QFrag<float> { using type = float; };
 
-__device__ __forceinline__ int bitlen_u64(uint64_t d) { return d == 0 ? 0 : 64 - __clzll((long long)d); }
 __device__ __forceinline__ int bitlen_u32(uint32_t d) { return 32 - __clz((int)d); }  // __clz(0) = 32
 
-// 16 bytes (or 4 bytes) from global memory at base + lane_off straight into LDS at lds_base + 16 * lane
-// (4 * lane); base is a wave-uniform 64-bit address, lane_off a 32-bit per-lane offset.  Issued as inline
-// assembly so that the waits for these loads are exactly the explicit vmcnt waits of the ring: a wait the
-// compiler inserted itself before LDS reads would not know that they read another stage.
-__device__ __forceinline__ void dma16(const void *base, uint32_t lane_off, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(lds_base), "v"(lane_off), "s"(base)
+// 16 bytes (or 4 bytes) from global memory at base + lane_off + IMM straight into LDS at
+// m0 + IMM + 16 * lane (4 * lane): the immediate offset moves both addresses.  base is a wave-uniform
+// 64-bit address, lane_off a 32-bit per-lane offset.  Issued as inline assembly so that the waits for
+// these loads are exactly the explicit vmcnt waits of the ring (a wait the compiler inserted itself
+// before LDS reads would not know that they read another stage); the s_nop is the one wait state an
+// LDS DMA needs after an SALU write of M0.
+template <int IMM>
+__device__ __forceinline__ void dma16(const void *base, uint32_t lane_off, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3"
+               : : "s"(m0), "v"(lane_off), "s"(base), "i"(IMM) : "memory");
+}
+__device__ __forceinline__ void dma4(const void *base, uint32_t lane_off, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" : : "s"(m0), "v"(lane_off), "s"(base)
                : "memory");
 }
-__device__ __forceinline__ void dma4(const void *base, uint32_t lane_off, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" : : "s"(lds_base), "v"(lane_off), "s"(base)
-               : "memory");
+// Column groups G..NG-1 of one row group of K and V: LDS group g sits at m + 4096*g; the immediate 64*g
+// selects the source column group and is taken back out of M0.
+template <int G, int NG>
+__device__ __forceinline__ void dma_groups(const char *kb, const char *vb, uint32_t koff, uint32_t voff, uint32_t mk,
+                                           uint32_t mv) {
+  if constexpr (G < NG) {
+    dma16<64 * G>(kb, koff, mk + (uint32_t)G * (4096u - 64u));
+    dma16<64 * G>(vb, voff, mv + (uint32_t)G * (4096u - 64u));
+    dma_groups<G + 1, NG>(kb, vb, koff, voff, mk, mv);
+  }
 }
 // s_waitcnt with only the vector-memory counter constrained (expcnt and lgkmcnt left at their maxima)
 template <int N>
@@ -138,71 +152,89 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+__device__ __forceinline__ int readlane_i(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
 // Per-wave constants of the score pointwise work for one tile.
 struct TileCtx {
   int k0;              // first key of the tile (sequence-local)
   int my_q, my_pos;    // this lane's query and its position
-  int n, nh;           // sequence length, history length
-  bool cand;
+  int pos_lim;         // position of key j is min(j, pos_lim): n_h with candidates, else n
+  int key_lim;         // allowed keys of this lane's query: j <= key_lim, or j == my_q
+  int nh;              // history length
   int P, Tb;
   int64_t my_tau;
   uint32_t qoff;       // (uint32)(my_tau - base) for the 32-bit modes
   uint32_t base_lo;    // low word of the tile's timestamp base
   uint32_t thr;        // two-bucket mode: |dt| >= thr selects bias_hi
-  float cbias, bias_lo, bias_hi;
-  const HSTU_LDS float *wp, *wt;
-  const HSTU_LDS int64_t *tau;   // the tile's timestamps
+  float c1;            // -log2(e) * bias of a uniform tile, 0 otherwise
+  float bias_lo, bias_hi;          // two-bucket mode: the two biases
+  const HSTU_LDS float *wp, *wt;   // bias tables
+  const HSTU_LDS char *stage;      // the tile's LDS stage
 };
 
-// SiLU(score + bias) for the 16 scores of one 32-key block kb; element e holds key
-// k0 + 32*kb + 16*(e/8) + 8*half + e%8.
-template <int MODE, bool MASKED>
-__device__ __forceinline__ void pointwise(const floatx16 &s, float (&a)[16], const TileCtx &c, int kb, int half) {
-  if constexpr (MODE == kUniform) {
+// Score of a pair outside the mask: SiLU of it is exactly 0 in silu_block (u = 1.4e30 is finite, 2^u
+// overflows to +inf, the reciprocal of 1 + inf is 0 and u * 0 = 0), and adding a finite q.k keeps it there.
+constexpr float kMaskedScore = -1.0e30f;
+
+// Per-score bias and mask of a non-uniform tile, added to the 16 scores of 32-key block kb in place;
+// element e holds key k0 + 32*kb + 16*(e/8) + 8*half + e%8.
+template <typename T, int DH, int MODE>
+__device__ __forceinline__ void adjust_block(floatx16 &s, const TileCtx &c, int kb, int half) {
+  using L = Layout<T, DH>;
+  constexpr bool kMasked = MODE == kGen32M || MODE == kGen64M;
+  constexpr bool k64 = MODE == kGen64 || MODE == kGen64M;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) a[e] = silu_f32(s[e] + c.cbias);
-  } else {
+  for (int g = 0; g < 2; ++g) {
+    const int jl0 = 32 * kb + 16 * g + 8 * half;   // tile-local key of element 8*g
+    uint32_t lo[8], hi[8];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int jl0 = 32 * kb + 16 * g + 8 * half;   // tile-local key of element 8*g
-      uint32_t lo[8], hi[8];
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 w = *(const HSTU_LDS u32x4 *)(c.stage + L::tau_at(jl0 + 2 * q));
+      lo[2 * q] = w.x; hi[2 * q] = w.y; lo[2 * q + 1] = w.z; hi[2 * q + 1] = w.w;
+    }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4 w = *(const HSTU_LDS u32x4 *)(c.tau + jl0 + 2 * q);
-        lo[2 * q] = w.x; hi[2 * q] = w.y; lo[2 * q + 1] = w.z; hi[2 * q + 1] = w.w;
+    for (int e8 = 0; e8 < 8; ++e8) {
+      const int e = 8 * g + e8;
+      float bias;
+      if constexpr (MODE == kTwo) {
+        const uint32_t d = __usad(c.qoff, lo[e8] - c.base_lo, 0u);
+        bias = d >= c.thr ? c.bias_hi : c.bias_lo;
+      } else {
+        const int j = c.k0 + jl0 + e8;
+        const int pj = imin(j, c.pos_lim);
+        const uint32_t dp = __usad((uint32_t)c.my_pos, (uint32_t)pj, 0u);
+        const int bp = (int)(dp < (uint32_t)(c.P - 1) ? dp : (uint32_t)(c.P - 1));
+        int bt;
+        if constexpr (!k64) {
+          bt = bitlen_u32(__usad(c.qoff, lo[e8] - c.base_lo, 0u));
+        } else {
+          const int64_t tj = (int64_t)(((uint64_t)hi[e8] << 32) | lo[e8]);
+          bt = bitlen_absdiff(c.my_tau, tj);
+        }
+        bt = imin(bt, c.Tb - 1);
+        bias = c.wp[bp] + c.wt[bt];
       }
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) {
-        const int e = 8 * g + e8;
-        float bias;
-        if constexpr (MODE == kTwo) {
-          const uint32_t d = __usad(c.qoff, lo[e8] - c.base_lo, 0u);
-          bias = d >= c.thr ? c.bias_hi : c.bias_lo;
-        } else {
-          const int j = c.k0 + jl0 + e8;
-          const int pj = c.cand ? imin(j, c.nh) : j;
-          const uint32_t dp = __usad((uint32_t)c.my_pos, (uint32_t)pj, 0u);
-          const int bp = (int)(dp < (uint32_t)(c.P - 1) ? dp : (uint32_t)(c.P - 1));
-          int bt;
-          if constexpr (MODE == kGen32) {
-            bt = bitlen_u32(__usad(c.qoff, lo[e8] - c.base_lo, 0u));
-          } else {
-            const int64_t tj = (int64_t)(((uint64_t)hi[e8] << 32) | lo[e8]);
-            bt = bitlen_absdiff(c.my_tau, tj);
-          }
-          bt = imin(bt, c.Tb - 1);
-          bias = c.wp[bp] + c.wt[bt];
-        }
-        const float v = silu_f32(s[e] + bias);
-        if constexpr (MASKED) {
-          const int j = c.k0 + jl0 + e8;
-          const bool ok = j < c.n && (c.my_q < c.nh ? j <= c.my_q : (j < c.nh || j == c.my_q));
-          a[e] = ok ? v : 0.0f;
-        } else {
-          a[e] = v;
-        }
+      if constexpr (kMasked) {
+        const int j = c.k0 + jl0 + e8;
+        const bool ok = (j <= c.key_lim) | (j == c.my_q);
+        s[e] = ok ? s[e] + bias : kMaskedScore;
+      } else {
+        s[e] = s[e] + bias;
       }
     }
+  }
+}
+
+// u / (1 + 2^u) for u = -log2(e) * (score + bias) of the 16 scores of one block (the bias is c1 for a
+// uniform tile, already inside the scores otherwise).
+__device__ __forceinline__ void silu_block(const floatx16 &s, float (&a)[16], float c1) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float u = __builtin_fmaf(s[e], kNegLog2e, c1);
+    a[e] = u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u));
   }
 }
 
@@ -262,21 +294,38 @@ __device__ __forceinline__ void av_block(OAcc<Layout<T, DH>::kDB> &oacc, const f
   }
 }
 
-// One key tile for one wave: both score blocks, then pointwise and AV for each.
-template <typename T, int DH, int MODE, bool MASKED>
+// One key tile for one wave: both score blocks; for a non-uniform tile the per-score bias and mask
+// patched into them in place (so that every class shares the MFMA code and the accumulators stay in
+// the same registers); then SiLU and AV for each block.
+template <typename T, int DH>
 __device__ __forceinline__ void tile_body(OAcc<Layout<T, DH>::kDB> &oacc,
                                           const typename QFrag<T>::type (&qf)[Layout<T, DH>::kQSteps],
-                                          const HSTU_LDS char *lK, const HSTU_LDS char *lV, const TileCtx &c,
-                                          int lane) {
+                                          const TileCtx &c, int body, int lane) {
+  using L = Layout<T, DH>;
   const int l32 = lane & 31, half = lane >> 5;
+  const HSTU_LDS char *lK = c.stage + L::kOffK;
+  const HSTU_LDS char *lV = c.stage + L::kOffV;
   floatx16 s0, s1;
   score_block<T, DH>(s0, lK, 0, l32, half, qf);
   score_block<T, DH>(s1, lK, 1, l32, half, qf);
-  float a[16];
-  pointwise<MODE, MASKED>(s0, a, c, 0, half);
-  av_block<T, DH>(oacc, a, lV, 0, lane);
-  pointwise<MODE, MASKED>(s1, a, c, 1, half);
-  av_block<T, DH>(oacc, a, lV, 1, lane);
+  if (body != kUniform) {
+    if (body == kTwo) {
+      adjust_block<T, DH, kTwo>(s0, c, 0, half); adjust_block<T, DH, kTwo>(s1, c, 1, half);
+    } else if (body == kGen32) {
+      adjust_block<T, DH, kGen32>(s0, c, 0, half); adjust_block<T, DH, kGen32>(s1, c, 1, half);
+    } else if (body == kGen32M) {
+      adjust_block<T, DH, kGen32M>(s0, c, 0, half); adjust_block<T, DH, kGen32M>(s1, c, 1, half);
+    } else if (body == kGen64) {
+      adjust_block<T, DH, kGen64>(s0, c, 0, half); adjust_block<T, DH, kGen64>(s1, c, 1, half);
+    } else {
+      adjust_block<T, DH, kGen64M>(s0, c, 0, half); adjust_block<T, DH, kGen64M>(s1, c, 1, half);
+    }
+  }
+  float a0[16], a1[16];
+  silu_block(s0, a0, c.c1);
+  av_block<T, DH>(oacc, a0, lV, 0, lane);
+  silu_block(s1, a1, c.c1);
+  av_block<T, DH>(oacc, a1, lV, 1, lane);
 }
 
 // Timestamp minimum and maximum of every 32-token chunk of every sequence.  Chunk c of sequence b is
@@ -382,50 +431,85 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   const int ntiles = r1_end + imax(r2_end - r2_begin, 0);
   auto tile_of = [&](int i) -> int { return i < r1_end ? i : r2_begin + (i - r1_end); };
 
-  // ---- direct-to-LDS staging.  Per tile, wave w issues kInstPerWave 1 KB loads: instruction iota fills
-  // block blk = iota % kInstPerOperand of operand iota / kInstPerOperand (K, then V): column group blk / 4,
-  // rows 16 * (blk % 4) .. +15, lane l taking row l / 4 of the block and 16-byte piece l % 4 of the group
-  // (K: the piece whose XOR-permuted position is l % 4).  The per-lane part of every source address is
-  // one register per operand; rows past the end of the sequence load its last row instead (finite data
-  // that the mask discards).  Timestamps: lanes 0..kTauLanes-1 of every wave load 4 bytes each.
-  const int64_t rsb = p.row_stride * L::kES;                  // bytes between tokens
-  const int lane_row = lane >> 2;
-  const uint32_t v_lane_off = (uint32_t)(lane_row * rsb + (lane & 3) * 16 + h * L::kRB);
-  const uint32_t k_lane_off = (uint32_t)(lane_row * rsb + ((lane & 3) ^ ((lane >> 4) & 3)) * 16 + h * L::kRB);
-  const uint32_t tau_lane_off = 4u * (uint32_t)(kTauLanes * wave + (lane % kTauLanes));
+  // ---- direct-to-LDS staging.  Per tile, wave w loads rows 16w..16w+15 of each 64-byte column group g
+  // of K and of V (1 KB each: lane l takes row 16w + l/4 and 16-byte piece l%4 of the group; in K, the
+  // piece whose XOR-permuted position is l%4) and the 16 timestamps of those rows (lanes 32..63 repeat
+  // lanes 0..31 into an unused half of the wave's 256-byte slot).  Rows past the end of the sequence
+  // load its last row instead (finite data that the mask discards).
+  const uint32_t rsb = (uint32_t)(p.row_stride * L::kES);        // bytes between tokens (<= 16 KB)
+  const int lr16 = 16 * wave + (lane >> 2);                      // tile-local row this lane loads
+  const uint32_t k_add = (uint32_t)(h * L::kRB) + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+  const uint32_t v_add = (uint32_t)(h * L::kRB) + 16u * (uint32_t)(lane & 3);
+  const int tr16 = 16 * wave + ((lane & 31) >> 1);               // tile-local key of this lane's tau word
+  const uint32_t t_add = 4u * (uint32_t)(lane & 1);
   const char *kbase = (const char *)p.k, *vbase = (const char *)p.v;
   auto issue_tile = [&](int i, int stage) {
     const int k0 = tile_of(i) * kBN;
-    const uint32_t sbase = smem_addr + stage * L::kStageBytes;
-    const bool tail = k0 + kBN > n;
-#pragma unroll
-    for (int j = 0; j < L::kInstPerWave; ++j) {
-      const int iota = wave * L::kInstPerWave + j;
-      const bool is_v = iota >= L::kInstPerOperand;
-      const int blk = iota % L::kInstPerOperand;
-      const int row0 = k0 + 16 * (blk & 3);                   // first key of this instruction
-      const int64_t col = 64 * (blk >> 2);                    // byte offset of its column group
-      const uint32_t lane_off = is_v ? v_lane_off : k_lane_off;
-      const uint32_t lds = sbase + (is_v ? L::kOffV : L::kOffK) + blk * 1024;
-      if (!tail) {
-        dma16((is_v ? vbase : kbase) + (int64_t)(o0 + row0) * rsb + col, lane_off, lds);
-      } else {
-        // clamp the instruction's base row as well, so that the per-lane offset stays non-negative
-        const int base_row = imin(row0, n - 1);
-        const int key = imin(row0 + lane_row, n - 1);
-        dma16((is_v ? vbase : kbase) + (int64_t)(o0 + base_row) * rsb + col,
-              (uint32_t)((key - base_row) * rsb) + (lane_off - (uint32_t)(lane_row * rsb)), lds);
+    const int lim = n - 1 - k0;                                  // >= 0: every tile starts inside the sequence
+    const uint32_t r = (uint32_t)imin(lr16, lim);
+    const uint32_t koff = __umul24(r, rsb) + k_add;
+    const uint32_t voff = __umul24(r, rsb) + v_add;
+    const uint32_t toff = 8u * (uint32_t)imin(tr16, lim) + t_add;
+    const int64_t row0 = (int64_t)(o0 + k0) * rsb;
+    const uint32_t sb = smem_addr + stage * L::kStageBytes;
+    dma_groups<0, L::kG>(kbase + row0, vbase + row0, koff, voff, sb + L::kOffK + wave * 1024,
+                         sb + L::kOffV + wave * 1024);
+    dma4((const char *)(p.timestamps + o0 + k0), toff, sb + L::kOffTau + 256 * wave);
+  };
+
+  // ---- tile classes, one tile per lane, 64 tiles at a time (vector code, once per 64 tiles)
+  int cls_code = 0;
+  float cls_lo = 0.0f, cls_hi = 0.0f;
+  uint32_t cls_base = 0;
+  auto classify = [&](int t0) {
+    const int t = t0 + lane;
+    int code = kNone;
+    float clo = 0.0f, chi = 0.0f;
+    uint32_t base = 0;
+    if (t < ntiles && wave_active) {
+      const int k0 = tile_of(t) * kBN;
+      const bool none = k0 > ql || (k0 >= nh && k0 + kBN - 1 < imax(qa, nh));
+      if (!none) {
+        const int c0 = k0 >> 5;
+        int64_t kmin = cstats[2 * c0], kmax = cstats[2 * c0 + 1];
+        if (k0 + kChunk < n) {
+          const int64_t a = cstats[2 * c0 + 2], bb = cstats[2 * c0 + 3];
+          kmin = a < kmin ? a : kmin;
+          kmax = bb > kmax ? bb : kmax;
+        }
+        const int64_t tmin = wmin < kmin ? wmin : kmin;
+        const int64_t tmax = wmax > kmax ? wmax : kmax;
+        const uint64_t span = (uint64_t)tmax - (uint64_t)tmin;
+        base = (uint32_t)(uint64_t)tmin;
+        const bool all = (k0 + kBN - 1 <= qa) && (k0 + kBN - 1 < nh);
+        code = span < (1ull << 32) ? (all ? kGen32 : kGen32M) : (all ? kGen64 : kGen64M);
+        if (all && imin(qa, nh) - (k0 + kBN - 1) >= P - 1) {
+          uint64_t lo, hi;
+          if (wmin >= kmax) {
+            lo = (uint64_t)wmin - (uint64_t)kmax;
+            hi = (uint64_t)wmax - (uint64_t)kmin;
+          } else if (kmin >= wmax) {
+            lo = (uint64_t)kmin - (uint64_t)wmax;
+            hi = (uint64_t)kmax - (uint64_t)wmin;
+          } else {
+            lo = 0;
+            hi = span;
+          }
+          const int blo = imin(lo == 0 ? 0 : 64 - __clzll((long long)lo), Tb - 1);
+          const int bhi = imin(hi == 0 ? 0 : 64 - __clzll((long long)hi), Tb - 1);
+          const float wpc = wp_lds[P - 1];
+          if (blo == bhi) {
+            code = kUniform;
+            clo = kNegLog2e * (wpc + wt_lds[blo]);
+          } else if (bhi == blo + 1 && span < (1ull << 32)) {
+            code = kTwo | (blo << 8);      // threshold 2^blo: |dt| >= 2^blo has bit length > blo
+            clo = wpc + wt_lds[blo];
+            chi = wpc + wt_lds[bhi];
+          }
+        }
       }
     }
-    {
-      const char *src = (const char *)(p.timestamps + o0 + k0);
-      uint32_t off = tau_lane_off;
-      if (tail) {
-        const int d = kTauLanes * wave + (lane % kTauLanes);
-        off = 8u * (uint32_t)(imin(k0 + (d >> 1), n - 1) - k0) + 4u * (uint32_t)(d & 1);
-      }
-      if (lane < kTauLanes) dma4(src, off, sbase + L::kOffTau + 4 * kTauLanes * wave);
-    }
+    cls_code = code; cls_lo = clo; cls_hi = chi; cls_base = base;
   };
 
   OAcc<L::kDB> oacc;
@@ -435,9 +519,11 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   TileCtx c;
   c.my_q = my_q;
   c.my_pos = cand ? imin(my_q, nh) : my_q;
-  c.n = n;
+  c.pos_lim = cand ? nh : n;
+  // a history query sees keys 0..my_q, a candidate the whole history and itself (every allowed key is
+  // < n for a query < n; lanes past the end are never stored)
+  c.key_lim = my_q < nh ? my_q : nh - 1;
   c.nh = nh;
-  c.cand = cand;
   c.P = P;
   c.Tb = Tb;
   c.my_tau = my_tau;
@@ -448,8 +534,10 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
 #pragma unroll
   for (int i = 0; i < kAhead; ++i)
     if (i < ntiles) issue_tile(i, i);
+  __syncthreads();                            // bias tables visible to the classification
 
   for (int i = 0; i < ntiles; ++i) {
+    if ((i & 63) == 0) classify(i);
     // tile i has landed once at most (tiles issued after it) x (loads per tile) loads are outstanding
     const int after = imin(kAhead - 1, ntiles - 1 - i);
     if (after >= 2) wait_vmcnt<2 * L::kLoadsPerTile>();
@@ -458,70 +546,26 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
     __syncthreads();  // tile i visible to all waves; every wave is done with tile i - 1
     if (i + kAhead < ntiles) issue_tile(i + kAhead, (i + kAhead) % L::kStages);
 
-    const int stage = i % L::kStages;
-    const HSTU_LDS char *base = smem + stage * L::kStageBytes;
-    const int k0 = tile_of(i) * kBN;
-
-    const bool none = !wave_active || k0 > ql || (k0 >= nh && (k0 + kBN - 1 < imax(qa, nh)));
-    if (!none) {
-      // timestamp range of the tile's valid keys
-      const int c0 = k0 >> 5;
-      int64_t kmin = cstats[2 * c0], kmax = cstats[2 * c0 + 1];
-      if (k0 + kChunk < n) {
-        const int64_t a = cstats[2 * c0 + 2], bb = cstats[2 * c0 + 3];
-        kmin = a < kmin ? a : kmin;
-        kmax = bb > kmax ? bb : kmax;
-      }
-      const int64_t tmin = wmin < kmin ? wmin : kmin;
-      const int64_t tmax = wmax > kmax ? wmax : kmax;
-      const uint64_t span = (uint64_t)tmax - (uint64_t)tmin;
-      c.k0 = k0;
-      c.tau = (const HSTU_LDS int64_t *)(base + L::kOffTau);
-      c.base_lo = (uint32_t)(uint64_t)tmin;
+    const int li = i & 63;
+    const int code = readlane_i(cls_code, li);
+    const int body = code & 7;
+    if (body != kNone) {
+      c.k0 = tile_of(i) * kBN;
+      c.stage = smem + (i % L::kStages) * L::kStageBytes;
+      const float lo_v = readlane_f(cls_lo, li);
+      c.c1 = body == kUniform ? lo_v : 0.0f;
+      c.bias_lo = lo_v;
+      c.bias_hi = readlane_f(cls_hi, li);
+      c.thr = 1u << ((code >> 8) & 31);
+      c.base_lo = (uint32_t)readlane_i((int)cls_base, li);
       c.qoff = (uint32_t)(uint64_t)my_tau - c.base_lo;
-      const HSTU_LDS char *lK = base + L::kOffK;
-      const HSTU_LDS char *lV = base + L::kOffV;
-
-      const bool all = (k0 + kBN - 1 <= qa) && (k0 + kBN - 1 < nh);
-      int mode = span < (1ull << 32) ? kGen32 : kGen64;
-      if (all && imin(qa, nh) - (k0 + kBN - 1) >= P - 1) {
-        uint64_t lo, hi;
-        if (wmin >= kmax) {
-          lo = (uint64_t)wmin - (uint64_t)kmax;
-          hi = (uint64_t)wmax - (uint64_t)kmin;
-        } else if (kmin >= wmax) {
-          lo = (uint64_t)kmin - (uint64_t)wmax;
-          hi = (uint64_t)kmax - (uint64_t)wmin;
-        } else {
-          lo = 0;
-          hi = span;
-        }
-        const int blo = imin(bitlen_u64(lo), Tb - 1);
-        const int bhi = imin(bitlen_u64(hi), Tb - 1);
-        const float wpc = wp_lds[P - 1];
-        if (blo == bhi) {
-          mode = kUniform;
-          c.cbias = wpc + wt_lds[blo];
-        } else if (bhi == blo + 1 && span < (1ull << 32)) {
-          mode = kTwo;
-          c.thr = 1u << (bhi - 1);
-          c.bias_lo = wpc + wt_lds[blo];
-          c.bias_hi = wpc + wt_lds[bhi];
-        }
-      }
-      if (all) {
-        if (mode == kUniform) tile_body<T, DH, kUniform, false>(oacc, qf, lK, lV, c, lane);
-        else if (mode == kTwo) tile_body<T, DH, kTwo, false>(oacc, qf, lK, lV, c, lane);
-        else if (mode == kGen32) tile_body<T, DH, kGen32, false>(oacc, qf, lK, lV, c, lane);
-        else tile_body<T, DH, kGen64, false>(oacc, qf, lK, lV, c, lane);
-      } else {
-        if (mode == kGen32) tile_body<T, DH, kGen32, true>(oacc, qf, lK, lV, c, lane);
-        else tile_body<T, DH, kGen64, true>(oacc, qf, lK, lV, c, lane);
-      }
+      tile_body<T, DH>(oacc, qf, c, body, lane);
     }
   }
 
-  // ---- epilogue: O^T element e of dh block db is dh = 32*db + 8*(e/4) + 4*half + e%4
+  // ---- epilogue: O^T element e of dh block db is dh = 32*db + 8*(e/4) + 4*half + e%4; the sums carry
+  // the factor -log2(e) of the folded SiLU, removed here together with c_b
+  const float scale = cb * kNegLn2;
   if (my_valid) {
     TO *orow = (TO *)p.out + (int64_t)(o0 + my_q) * p.out_row_stride + h * DH;
 #pragma unroll
@@ -531,13 +575,13 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
         const int dh = 32 * db + 8 * e4 + 4 * half;
         if constexpr (sizeof(TO) == 4) {
           floatx4 w;
-          w[0] = oacc.d[db][4 * e4 + 0] * cb; w[1] = oacc.d[db][4 * e4 + 1] * cb;
-          w[2] = oacc.d[db][4 * e4 + 2] * cb; w[3] = oacc.d[db][4 * e4 + 3] * cb;
+          w[0] = oacc.d[db][4 * e4 + 0] * scale; w[1] = oacc.d[db][4 * e4 + 1] * scale;
+          w[2] = oacc.d[db][4 * e4 + 2] * scale; w[3] = oacc.d[db][4 * e4 + 3] * scale;
           *(floatx4 *)(orow + dh) = w;
         } else {
           bf16x4 w;
-          w[0] = f32_to_bf16(oacc.d[db][4 * e4 + 0] * cb); w[1] = f32_to_bf16(oacc.d[db][4 * e4 + 1] * cb);
-          w[2] = f32_to_bf16(oacc.d[db][4 * e4 + 2] * cb); w[3] = f32_to_bf16(oacc.d[db][4 * e4 + 3] * cb);
+          w[0] = f32_to_bf16(oacc.d[db][4 * e4 + 0] * scale); w[1] = f32_to_bf16(oacc.d[db][4 * e4 + 1] * scale);
+          w[2] = f32_to_bf16(oacc.d[db][4 * e4 + 2] * scale); w[3] = f32_to_bf16(oacc.d[db][4 * e4 + 3] * scale);
           *(bf16x4 *)(orow + dh) = w;
         }
       }
