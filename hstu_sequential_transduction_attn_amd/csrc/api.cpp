@@ -100,16 +100,14 @@ hstu::AttnArgs attn_args(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc)
 }
 
 // Layer workspace regions, each 256-byte aligned: U ([T][HD] fp32), V, Q, K ([T][HD] dtype),
-// O ([T][HD] fp32), G ([T][HD], fp32 when the gate stays fp32 for the output GEMM, else dtype),
-// Y32 ([T][D] fp32, only when ln_output), timestamp ranges of the attention.
+// O ([T][HD] fp32), per-(token, head) statistics of O ([T][H][2] fp32), Y32 ([T][D] fp32, only when
+// ln_output), timestamp ranges of the attention.
 struct LayerWs {
-  size_t u, v, q, k, o, g, y32, stats, total;
-  bool g_f32;
+  size_t u, v, q, k, o, ostat, y32, stats, total;
 };
 
-LayerWs layer_ws(int64_t T, int64_t B, int64_t HD, int64_t D, hstu_dtype_t dt, bool ln_output, bool split) {
+LayerWs layer_ws(int64_t T, int64_t B, int64_t H, int64_t HD, int64_t D, hstu_dtype_t dt, bool ln_output) {
   LayerWs w{};
-  w.g_f32 = dt == HSTU_F32 || split;
   const size_t part = round_up((size_t)T * HD * esize(dt), 256);
   const size_t part32 = round_up((size_t)T * HD * 4, 256);
   size_t off = 0;
@@ -118,7 +116,7 @@ LayerWs layer_ws(int64_t T, int64_t B, int64_t HD, int64_t D, hstu_dtype_t dt, b
   w.q = off; off += part;
   w.k = off; off += part;
   w.o = off; off += part32;
-  w.g = off; off += w.g_f32 ? part32 : part;
+  w.ostat = off; off += round_up((size_t)T * H * 8, 256);
   w.y32 = off; off += ln_output ? round_up((size_t)T * D * 4, 256) : 0;
   w.stats = off; off += round_up(hstu::attn_tau_stats_bytes(T, B), 256);
   w.total = off;
@@ -198,9 +196,8 @@ size_t hstu_layer_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc
                                   const hstu_layer_weights_t *w, hstu_dtype_t dtype) {
   if (!jag || !desc || !w || jag->total_tokens < 0 || desc->num_heads < 1 || desc->head_dim < 1 || w->d_model < 1)
     return 0;
-  return layer_ws(jag->total_tokens, jag->num_seqs, (int64_t)desc->num_heads * desc->head_dim, w->d_model, dtype,
-                  w->ln_output != 0,
-                  dtype == HSTU_BF16 && w->act_split != 0)
+  return layer_ws(jag->total_tokens, jag->num_seqs, desc->num_heads, (int64_t)desc->num_heads * desc->head_dim,
+                  w->d_model, dtype, w->ln_output != 0)
       .total;
 }
 
@@ -226,7 +223,7 @@ hstu_status_t hstu_layer_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
     if (!aligned16(w->w_uvqk) || !aligned16(w->w_out))
       return fail(HSTU_ERR_INVALID_ARGUMENT, "weights must be 16-byte aligned");
     const bool split = dtype == HSTU_BF16 && w->act_split != 0;
-    const LayerWs ws = layer_ws(T, jag->num_seqs, HD, D, dtype, w->ln_output != 0, split);
+    const LayerWs ws = layer_ws(T, jag->num_seqs, desc->num_heads, HD, D, dtype, w->ln_output != 0);
     if (workspace_bytes < ws.total)
       return fail(HSTU_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, ws.total);
     if (T == 0) return ok();
@@ -257,20 +254,18 @@ hstu_status_t hstu_layer_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
     a.row_stride = HD; a.out_row_stride = HD;
     a.in_dtype = dt; a.out_dtype = hstu::kF32;
     a.tau_stats = (int64_t *)(wsb + ws.stats);
+    a.row_stats = (float *)(wsb + ws.ostat);
     e = hstu::launch_attn_fwd(a, s);
     if (e != hipSuccess) return from_hip(e, "attention launch");
 
-    hstu::NormGateArgs ng{};
-    ng.o = (const float *)(wsb + ws.o); ng.u = (const float *)(wsb + ws.u); ng.g = wsb + ws.g;
-    ng.M = (int32_t)T; ng.HD = (int32_t)HD; ng.eps = w->ln_eps; ng.dtype = dt; ng.g_f32 = ws.g_f32;
-    e = hstu::launch_norm_gate(ng, s);
-    if (e != hipSuccess) return from_hip(e, "norm-gate launch");
-
     hstu::GemmOutArgs g2{};
-    g2.g = wsb + ws.g; g2.w = w->w_out; g2.bias = w->b_out; g2.x = x;
+    g2.o = (const float *)(wsb + ws.o); g2.u = (const float *)(wsb + ws.u);
+    g2.row_stats = (const float *)(wsb + ws.ostat);
+    g2.heads = desc->num_heads; g2.head_dim = desc->head_dim; g2.eps = w->ln_eps;
+    g2.w = w->w_out; g2.bias = w->b_out; g2.x = x;
     g2.y = y; g2.y32 = w->ln_output ? (float *)(wsb + ws.y32) : nullptr;
     g2.M = (int32_t)T; g2.N = (int32_t)D; g2.K = (int32_t)HD;
-    g2.dtype = dt; g2.g_f32 = ws.g_f32; g2.split = split; g2.x_f32 = x_f32; g2.y_f32 = y_f32;
+    g2.dtype = dt; g2.split = split; g2.x_f32 = x_f32; g2.y_f32 = y_f32;
     e = hstu::launch_gemm_out(g2, s);
     if (e != hipSuccess) return from_hip(e, "output GEMM launch");
 

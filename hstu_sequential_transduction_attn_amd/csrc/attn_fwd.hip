@@ -566,6 +566,32 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   // ---- epilogue: O^T element e of dh block db is dh = 32*db + 8*(e/4) + 4*half + e%4; the sums carry
   // the factor -log2(e) of the folded SiLU, removed here together with c_b
   const float scale = cb * kNegLn2;
+  if (p.row_stats) {
+    // mean and sum of squared deviations of the stored head row: each lane holds 16*kDB of its query's
+    // values, lane ^ 32 the others; the two halves combine exactly (equal counts)
+    constexpr float kN = 16.0f * L::kDB;
+    float sum = 0.0f;
+#pragma unroll
+    for (int db = 0; db < L::kDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sum += oacc.d[db][e] * scale;
+    const float mean_l = sum / kN;
+    float m2_l = 0.0f;
+#pragma unroll
+    for (int db = 0; db < L::kDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float d = oacc.d[db][e] * scale - mean_l;
+        m2_l += d * d;
+      }
+    const float mean_o = __shfl_xor(mean_l, 32, kWave), m2_o = __shfl_xor(m2_l, 32, kWave);
+    const float dm = mean_l - mean_o;
+    if (my_valid && half == 0) {
+      float *st = p.row_stats + 2 * ((int64_t)(o0 + my_q) * p.num_heads + h);
+      st[0] = 0.5f * (mean_l + mean_o);
+      st[1] = m2_l + m2_o + dm * dm * (0.5f * kN);
+    }
+  }
   if (my_valid) {
     TO *orow = (TO *)p.out + (int64_t)(o0 + my_q) * p.out_row_stride + h * DH;
 #pragma unroll

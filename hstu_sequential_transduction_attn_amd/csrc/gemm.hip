@@ -5,7 +5,10 @@
 //    訓練ベンチマークがシーケンス化時代へ", section "モデルアーキテクチャ").  U, used only by the
 //    elementwise gate, is kept in fp32; V, Q, K are stored in the MFMA operand type.
 //  * output:      y = x + G W2^T + b2 (residual added in fp32, one rounding), or the fp32 sum for a
-//    following LayerNorm pass.
+//    following LayerNorm pass, with the gate G = LN(O) * U (the gated transformation of the same
+//    section) computed while the A operand is loaded: the rows' LayerNorm statistics are combined
+//    from the per-head partial statistics the attention kernel stored next to O, and each A element
+//    is (o - mean) * rstd * u.  G is never stored.
 //
 // Both operands are K-contiguous (row-major activations, torch-Linear [out][in] weights), which is the
 // native operand form of the 32x32 MFMAs.  Workgroup tile 128x128, k-tile 32, 4 waves in a 2x2 grid,
@@ -51,7 +54,7 @@ template <> struct Frag<__bf16> { using type = bf16x8; };
 template <> struct Frag<float> { using type = float; };
 
 struct GemmParams {
-  const void *a;       // [M][K] (TA)
+  const void *a;       // [M][K] (TA); with the fused gate: O, fp32
   const void *b;       // [N][K] (TM)
   const void *bias;    // [N] (TM) or null
   const void *resid;   // [M][N] residual (output epilogue), fp32 if resid_f32 else TM
@@ -59,6 +62,10 @@ struct GemmParams {
   float *out32;        // output epilogue: fp32 result (pre-LayerNorm) or null
   int M, N, K, HD;
   int resid_f32, y_f32;
+  const float *gate_u;     // fused gate: U [M][K] fp32
+  const float *row_stats;  // fused gate: [M][heads][2] per-head mean and sum of squared deviations of O
+  int heads, head_dim;
+  float eps;
 };
 
 // Staging registers of one 16-byte LDS chunk of A: the global source is 16 bytes (TA == TM) or
@@ -74,16 +81,42 @@ struct AChunk<__bf16, float> {
   floatx4 lo, hi;  // 8 consecutive fp32 values
 };
 
-template <typename TM, typename TA, int SPLIT, int EPI>
+template <typename TM, typename TA, int SPLIT, int EPI, bool GATE>
 __global__ void __launch_bounds__(kThreads) gemm_kernel(const GemmParams p) {
   using L = GLayout<TM, TA, SPLIT>;
   using F = typename Frag<TM>::type;
+  static_assert(!GATE || sizeof(TA) == 4, "the fused gate reads fp32 O and U");
   __shared__ __attribute__((aligned(16))) char smem_raw[2 * L::kStageBytes];
+  __shared__ float row_norm[GATE ? 2 * kBM : 2];   // fused gate: (mean, rstd) of the tile's rows
   HSTU_LDS char *smem = (HSTU_LDS char *)smem_raw;
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, l32 = lane & 31, half = lane >> 5;
   const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+
+  if constexpr (GATE) {
+    // LayerNorm statistics of the row from its heads' (mean, M2): equal counts per head, so the row
+    // mean is the mean of the head means and M2 = sum(M2_h + Dh (mean_h - mean)^2)
+    if (tid < kBM) {
+      const int m = m0 + tid;
+      float mean = 0.0f, rstd = 0.0f;
+      if (m < p.M) {
+        const float *st = p.row_stats + (int64_t)m * p.heads * 2;
+        float s = 0.0f;
+        for (int hh = 0; hh < p.heads; ++hh) s += st[2 * hh];
+        mean = s / (float)p.heads;
+        float m2 = 0.0f;
+        for (int hh = 0; hh < p.heads; ++hh) {
+          const float d = st[2 * hh] - mean;
+          m2 += st[2 * hh + 1] + (float)p.head_dim * d * d;
+        }
+        rstd = 1.0f / sqrtf(m2 / (float)(p.heads * p.head_dim) + p.eps);
+      }
+      row_norm[2 * tid] = mean;
+      row_norm[2 * tid + 1] = rstd;
+    }
+    __syncthreads();
+  }
 
   AChunk<TM, TA> areg[L::kCPT];
   u32x4 breg[L::kCPT];
@@ -97,8 +130,22 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(const GemmParams p) {
       {
         const int m = m0 + row;
         const bool ok = kok && m < p.M;
-        const TA *src = (const TA *)p.a + (int64_t)(ok ? m : 0) * p.K + (ok ? kk : 0);
-        if constexpr (L::kConvA) {
+        const int64_t aoff = (int64_t)(ok ? m : 0) * p.K + (ok ? kk : 0);
+        const TA *src = (const TA *)p.a + aoff;
+        if constexpr (GATE) {
+          // g = (o - mean) * rstd * u for the chunk's 8 (bf16 operand) or 4 (fp32 operand) columns
+          const float mean = row_norm[2 * row], rstd = row_norm[2 * row + 1];
+          const float *usrc = p.gate_u + aoff;
+          floatx4 g0 = (*(const floatx4 *)src - mean) * rstd * *(const floatx4 *)usrc;
+          if constexpr (L::kConvA) {
+            floatx4 g1 = (*(const floatx4 *)(src + 4) - mean) * rstd * *(const floatx4 *)(usrc + 4);
+            areg[c].lo = ok ? g0 : floatx4{};
+            areg[c].hi = ok ? g1 : floatx4{};
+          } else {
+            if (!ok) g0 = floatx4{};
+            areg[c].v = __builtin_bit_cast(u32x4, g0);
+          }
+        } else if constexpr (L::kConvA) {
           const floatx4 a0 = *(const floatx4 *)src, a1 = *(const floatx4 *)(src + 4);
           areg[c].lo = ok ? a0 : floatx4{};
           areg[c].hi = ok ? a1 : floatx4{};
@@ -231,19 +278,21 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(const GemmParams p) {
   }
 }
 
-template <typename TM, typename TA, int SPLIT, int EPI>
+template <typename TM, typename TA, int SPLIT, int EPI, bool GATE>
 hipError_t launch(const GemmParams &p, hipStream_t s) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
   dim3 grid((p.N + kBN - 1) / kBN, (p.M + kBM - 1) / kBM);
-  hipLaunchKernelGGL((gemm_kernel<TM, TA, SPLIT, EPI>), grid, dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((gemm_kernel<TM, TA, SPLIT, EPI, GATE>), grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
-template <int EPI>
+template <int EPI, bool GATE>
 hipError_t dispatch(const GemmParams &p, int dtype, int a_f32, int split, hipStream_t s) {
-  if (dtype == kF32) return launch<float, float, 1, EPI>(p, s);
-  if (!a_f32) return launch<__bf16, __bf16, 1, EPI>(p, s);
-  return split ? launch<__bf16, float, 2, EPI>(p, s) : launch<__bf16, float, 1, EPI>(p, s);
+  if (dtype == kF32) return launch<float, float, 1, EPI, GATE>(p, s);
+  if constexpr (!GATE) {
+    if (!a_f32) return launch<__bf16, __bf16, 1, EPI, false>(p, s);
+  }
+  return split ? launch<__bf16, float, 2, EPI, GATE>(p, s) : launch<__bf16, float, 1, EPI, GATE>(p, s);
 }
 
 }  // namespace
@@ -253,16 +302,17 @@ hipError_t launch_gemm_uvqk(const GemmUvqkArgs &a, hipStream_t s) {
   p.a = a.x; p.b = a.w; p.bias = a.bias; p.resid = nullptr;
   p.out0 = a.u; p.out1 = a.v; p.out2 = a.q; p.out3 = a.k; p.out32 = nullptr;
   p.M = a.M; p.N = 4 * a.HD; p.K = a.K; p.HD = a.HD;
-  return dispatch<kEpiUvqk>(p, a.dtype, a.x_f32, a.split, s);
+  return dispatch<kEpiUvqk, false>(p, a.dtype, a.x_f32, a.split, s);
 }
 
 hipError_t launch_gemm_out(const GemmOutArgs &a, hipStream_t s) {
   GemmParams p{};
-  p.a = a.g; p.b = a.w; p.bias = a.bias; p.resid = a.x;
+  p.a = a.o; p.b = a.w; p.bias = a.bias; p.resid = a.x;
   p.out0 = a.y; p.out1 = p.out2 = p.out3 = nullptr; p.out32 = a.y32;
   p.M = a.M; p.N = a.N; p.K = a.K; p.HD = 0;
   p.resid_f32 = a.x_f32; p.y_f32 = a.y_f32;
-  return dispatch<kEpiOut>(p, a.dtype, a.g_f32, a.split, s);
+  p.gate_u = a.u; p.row_stats = a.row_stats; p.heads = a.heads; p.head_dim = a.head_dim; p.eps = a.eps;
+  return dispatch<kEpiOut, true>(p, a.dtype, 1, a.split, s);
 }
 
 }  // namespace hstu

@@ -28,6 +28,8 @@ struct AttnArgs {
   int32_t mask;
   int32_t in_dtype, out_dtype;
   int64_t *tau_stats;             // workspace: attn_tau_stats_bytes() of per-32-token timestamp ranges
+  float *row_stats;               // [T][H][2] mean and sum of squared deviations of each stored head row
+                                  // (fp32 output only; the gate of the output projection uses them), or null
 };
 
 // Workspace bytes of the per-32-token timestamp ranges the attention kernel classifies tiles with.
@@ -48,27 +50,24 @@ struct GemmUvqkArgs {
 };
 hipError_t launch_gemm_uvqk(const GemmUvqkArgs &a, hipStream_t stream);
 
-// Gate: g = LN(o) * u over each H*Dh row (LN: biased variance, no affine).
-struct NormGateArgs {
-  const float *o;                 // [M][HD] fp32 attention output
-  const float *u;                 // [M][HD] fp32
-  void *g;                        // [M][HD]: fp32 if g_f32 else dtype
-  int32_t M, HD;
-  float eps;
-  int32_t dtype, g_f32;
-};
-hipError_t launch_norm_gate(const NormGateArgs &a, hipStream_t stream);
-
-// Output projection: y = x + g W2^T + b2 (into y, or fp32 into y32 when a LayerNorm follows).
+// Output projection with the gate fused into its A operand:
+//   A[m][k] = (o[m][k] - mean_m) * rstd_m * u[m][k],   y = x + A W2^T + b2
+// (LayerNorm over the whole H*Dh row of o, biased variance, no affine).  mean_m and rstd_m are
+// combined from the per-head statistics the attention kernel wrote next to o.  y goes to y, or in fp32
+// to y32 when a LayerNorm follows.
 struct GemmOutArgs {
-  const void *g;                  // [M][K] (K = HD): fp32 if g_f32 else dtype
+  const float *o;                 // [M][K] fp32 attention output (K = H*Dh)
+  const float *u;                 // [M][K] fp32
+  const float *row_stats;         // [M][H][2] per-head mean and sum of squared deviations of o
+  int32_t heads, head_dim;
+  float eps;
   const void *w;                  // [N][K] dtype (N = D)
   const void *bias;               // [N] dtype or null
   const void *x;                  // [M][N] residual: fp32 if x_f32 else dtype
   void *y;                        // [M][N]: fp32 if y_f32 else dtype (unused when y32 is set)
   float *y32;                     // [M][N] fp32 pre-LayerNorm result, or null
   int32_t M, N, K;
-  int32_t dtype, g_f32, split, x_f32, y_f32;
+  int32_t dtype, split, x_f32, y_f32;
 };
 hipError_t launch_gemm_out(const GemmOutArgs &a, hipStream_t stream);
 

@@ -1,9 +1,6 @@
 // Row-wise, HBM-bound kernels of the HSTU layer on gfx950.
 //
-//  * norm_gate:      g_t = LN(o_t) * u_t over the H*Dh row of each token (the gated transformation:
-//                    "DLRMv4：MLPerfの推薦システム訓練ベンチマークがシーケンス化時代へ", section
-//                    "モデルアーキテクチャ").  LayerNorm with biased variance, no affine.
-//  * row_layernorm:  y_t = LN(y32_t) between stacked layers.
+//  * row_layernorm:  y_t = LN(y32_t) between stacked layers (LayerNorm with biased variance, no affine).
 //  * gather_rows:    x_t = E[id_t], the embedding lookup that stages the first layer's input.
 //
 // One wave per row; each lane keeps its slice of the row in registers, so the row is read from HBM
@@ -20,54 +17,6 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
   return v;
-}
-
-// Each lane owns columns lane*4 + 256*c for c < N/256 (+ tail): 16-byte fp32 loads.
-template <typename TO, int MAXC>
-__global__ void __launch_bounds__(256) norm_gate_kernel(const float *__restrict__ o, const float *__restrict__ u,
-                                                        TO *__restrict__ g, int M, int N, float eps) {
-  const int row = blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  if (row >= M) return;
-  const float *orow = o + (int64_t)row * N;
-  float x[MAXC][4];
-  float s = 0.0f;
-#pragma unroll
-  for (int c = 0; c < MAXC; ++c) {
-    const int col = 256 * c + 4 * lane;
-    if (col < N) {
-      const floatx4 v = *(const floatx4 *)(orow + col);
-      x[c][0] = v[0]; x[c][1] = v[1]; x[c][2] = v[2]; x[c][3] = v[3];
-      s += v[0] + v[1] + v[2] + v[3];
-    } else {
-      x[c][0] = x[c][1] = x[c][2] = x[c][3] = 0.0f;
-    }
-  }
-  const float mean = wave_sum(s) / (float)N;
-  float q = 0.0f;
-#pragma unroll
-  for (int c = 0; c < MAXC; ++c) {
-    const int col = 256 * c + 4 * lane;
-    if (col < N) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float d = x[c][i] - mean;
-        q += d * d;
-      }
-    }
-  }
-  const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)N + eps);
-  const float *urow = u + (int64_t)row * N;
-  TO *grow = g + (int64_t)row * N;
-#pragma unroll
-  for (int c = 0; c < MAXC; ++c) {
-    const int col = 256 * c + 4 * lane;
-    if (col < N) {
-      const floatx4 uv = *(const floatx4 *)(urow + col);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) grow[col + i] = from_f32<TO>((x[c][i] - mean) * rstd * uv[i]);
-    }
-  }
 }
 
 template <typename TO, int MAXC>
@@ -127,18 +76,6 @@ __global__ void __launch_bounds__(256) gather_kernel(const u32x4 *__restrict__ t
 
 // Row width is bounded by 256 * MAXC (checked on the host: width <= 4096, width % 4 == 0).
 template <typename TO>
-hipError_t launch_ng(const NormGateArgs &a, hipStream_t s) {
-  const dim3 grid((a.M + kRowsPerBlock - 1) / kRowsPerBlock);
-  const float *o = a.o;
-  const float *u = a.u;
-  TO *g = (TO *)a.g;
-  if (a.HD <= 256) hipLaunchKernelGGL((norm_gate_kernel<TO, 1>), grid, dim3(256), 0, s, o, u, g, a.M, a.HD, a.eps);
-  else if (a.HD <= 1024) hipLaunchKernelGGL((norm_gate_kernel<TO, 4>), grid, dim3(256), 0, s, o, u, g, a.M, a.HD, a.eps);
-  else hipLaunchKernelGGL((norm_gate_kernel<TO, 16>), grid, dim3(256), 0, s, o, u, g, a.M, a.HD, a.eps);
-  return hipGetLastError();
-}
-
-template <typename TO>
 hipError_t launch_ln(const RowLnArgs &a, hipStream_t s) {
   const dim3 grid((a.M + kRowsPerBlock - 1) / kRowsPerBlock);
   TO *out = (TO *)a.out;
@@ -149,11 +86,6 @@ hipError_t launch_ln(const RowLnArgs &a, hipStream_t s) {
 }
 
 }  // namespace
-
-hipError_t launch_norm_gate(const NormGateArgs &a, hipStream_t s) {
-  if (a.M == 0) return hipSuccess;
-  return (a.dtype == kBF16 && !a.g_f32) ? launch_ng<__bf16>(a, s) : launch_ng<float>(a, s);
-}
 
 hipError_t launch_row_layernorm(const RowLnArgs &a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;

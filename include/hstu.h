@@ -143,8 +143,10 @@ size_t hstu_layer_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc
  *          An fp32 residual stream between stacked bf16 layers (x_dtype = y_dtype = HSTU_F32) avoids
  *          rounding the activations to bf16 at every layer boundary.
  * Inside: the projection GEMM fuses bias, SiLU and the U|V|Q|K split into its epilogue (U is kept in
- * fp32, V, Q, K in dtype); the attention writes O in fp32; the gate applies LN(O) * U in fp32; the output
- * GEMM adds bias and residual in fp32 and rounds once (or hands the fp32 sum to the output LayerNorm).
+ * fp32, V, Q, K in dtype); the attention writes O in fp32 together with each head row's mean and sum
+ * of squared deviations; the output GEMM computes the gate LN(O) * U in fp32 while it loads its A
+ * operand (the gate is never stored), adds bias and residual in fp32 and rounds once (or hands the
+ * fp32 sum to the output LayerNorm).
  */
 hstu_status_t hstu_layer_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc,
                              const hstu_layer_weights_t *w, hstu_dtype_t dtype, hstu_dtype_t x_dtype,
