@@ -154,27 +154,71 @@ def run(args):
 
 
 def extended(args, dev):
-    """Per-workload timings of the layer path (stderr, informational)."""
+    """Layer workloads (stderr, informational): layer_bf16, stack8_bf16 and mfalcon_bf16 with every input
+    and weight resident on the device; one forward = gather (when the workload stages its input from an
+    embedding table) + every layer.  Timed with HIP events on the stream the kernels run on."""
     import torch
     from hstu_sequential_transduction_attn_amd import configs as C
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from _util import gpu_layer_stack  # noqa: E402
+    from hstu_sequential_transduction_attn_amd import inputs as I
+    from hstu_sequential_transduction_attn_amd import _lib as ops
 
-    def timed(fn, reps=3):
-        fn()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            fn()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / reps * 1e3
-    for name, mk, kw in [("layer_bf16", C.layer_bf16, {}),
-                         ("stack8_bf16", C.stack8_bf16, dict(use_gather=True, residual_f32=True, act_split=True)),
-                         ("mfalcon_bf16", C.mfalcon_bf16, dict(use_gather=True, residual_f32=True))]:
+    def t(x, dtype=None):
+        if isinstance(x, I.Tensor):
+            if x.dtype == "bf16":
+                return torch.from_numpy(np.ascontiguousarray(x.bits).view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(x.values)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    for name, mk, residual_f32, act_split in [("layer_bf16", C.layer_bf16, False, False),
+                                              ("stack8_bf16", C.stack8_bf16, True, True),
+                                              ("mfalcon_bf16", C.mfalcon_bf16, True, False)]:
         case = mk()
-        ms = timed(lambda: gpu_layer_stack(case, **kw))
-        print(f"[extended] {name}: {ms:.2f} ms per forward (incl. host-side weight upload)", file=sys.stderr,
-              flush=True)
+        j = case.jagged
+        offs, tau = t(j.seq_offsets.astype(np.int32)), t(j.timestamps.astype(np.int64))
+        ncand = None if j.num_candidates is None else t(j.num_candidates.astype(np.int32))
+        layers = [dict(w1=t(L.w_uvqk), w2=t(L.w_out), wp=t(L.rab.pos_bias), wt=t(L.rab.time_bias), eps=L.ln_eps)
+                  for L in case.layers]
+        if case.table_rows:
+            table = torch.zeros((case.table_rows, case.d_model), dtype=torch.bfloat16, device=dev)
+            table.index_copy_(0, t(case.table_touched.astype(np.int64)), t(case.table_values))
+            ids = t(case.ids.astype(np.int64))
+            x0 = None
+        else:
+            table = ids = None
+            x0 = t(case.x)
+        H, Dh = case.num_heads, case.head_dim
+        probe = x0 if x0 is not None else torch.empty((j.total_tokens, case.d_model), dtype=torch.bfloat16, device=dev)
+        nws = ops.layer_workspace_bytes(probe, offs, tau, layers[0]["w1"], layers[0]["w2"], layers[0]["wp"],
+                                        layers[0]["wt"], H, Dh, max_seq_len=j.max_seq_len, ln_output=True,
+                                        mask=j.mask, act_split=act_split)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        ydt = torch.float32 if residual_f32 else None
+
+        def forward():
+            x = ops.gather_rows(table, ids) if table is not None else x0
+            for li, L in enumerate(layers):
+                x = ops.layer_fwd(x, offs, tau, L["w1"], L["w2"], L["wp"], L["wt"], H, Dh,
+                                  max_seq_len=j.max_seq_len, ln_eps=L["eps"], ln_output=li < len(layers) - 1,
+                                  mask=j.mask, num_candidates=ncand, y_dtype=ydt, act_split=act_split, workspace=ws)
+            return x
+        stream = torch.cuda.current_stream()
+        for _ in range(2):
+            forward()
+        torch.cuda.synchronize()
+        reps = 5
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            forward()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        T, D, HD = j.total_tokens, case.d_model, H * Dh
+        pairs = I.allowed_pairs(j)
+        flop = len(layers) * (2 * T * D * 4 * HD + pairs * H * 4 * Dh + 2 * T * HD * D)
+        print(f"[extended] {name}: {ms:.3f} ms per forward ({len(layers)} layers, T={T}, D={D}, H={H}x{Dh}); "
+              f"{flop:.3e} algorithmic FLOP -> {flop / ms / 1e9:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        del table, ws
 
 
 def main():
