@@ -119,21 +119,6 @@ template <> struct QFrag<float> { using type = float; };
 
 __device__ __forceinline__ int bitlen_u32(uint32_t d) { return 32 - __clz((int)d); }  // __clz(0) = 32
 
-// 16 bytes (or 4 bytes) from global memory at base + lane_off + IMM straight into LDS at
-// m0 + IMM + 16 * lane (4 * lane): the immediate offset moves both addresses.  base is a wave-uniform
-// 64-bit address, lane_off a 32-bit per-lane offset.  Issued as inline assembly so that the waits for
-// these loads are exactly the explicit vmcnt waits of the ring (a wait the compiler inserted itself
-// before LDS reads would not know that they read another stage); the s_nop is the one wait state an
-// LDS DMA needs after an SALU write of M0.
-template <int IMM>
-__device__ __forceinline__ void dma16(const void *base, uint32_t lane_off, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3"
-               : : "s"(m0), "v"(lane_off), "s"(base), "i"(IMM) : "memory");
-}
-__device__ __forceinline__ void dma4(const void *base, uint32_t lane_off, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" : : "s"(m0), "v"(lane_off), "s"(base)
-               : "memory");
-}
 // Column groups G..NG-1 of one row group of K and V: LDS group g sits at m + 4096*g; the immediate 64*g
 // selects the source column group and is taken back out of M0.
 template <int G, int NG>
@@ -145,13 +130,6 @@ __device__ __forceinline__ void dma_groups(const char *kb, const char *vb, uint3
     dma_groups<G + 1, NG>(kb, vb, koff, voff, mk, mv);
   }
 }
-// s_waitcnt with only the vector-memory counter constrained (expcnt and lgkmcnt left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 __device__ __forceinline__ int readlane_i(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));

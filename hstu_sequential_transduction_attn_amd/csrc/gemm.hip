@@ -11,8 +11,13 @@
 //    is (o - mean) * rstd * u.  G is never stored.
 //
 // Both operands are K-contiguous (row-major activations, torch-Linear [out][in] weights), which is the
-// native operand form of the 32x32 MFMAs.  Workgroup tile 128x128, k-tile 32, 4 waves in a 2x2 grid,
-// each wave 64x64 (2x2 MFMA tiles); LDS double-buffered with one barrier per k-tile.
+// native operand form of the 32x32 MFMAs.  Two kernels:
+//  * gemm_big_kernel (bf16 weights, K a whole number of k-tiles, at least 256 tiles): large tiles,
+//    direct-to-LDS staging, fp32 activations converted while fragments are read, XCD-aware tile order;
+//    described where it is defined.
+//  * gemm_kernel (everything else: fp32 weights, small or odd shapes): workgroup tile 128x128, k-tile 32,
+//    4 waves in a 2x2 grid, each wave 64x64 (2x2 MFMA tiles); register staging, LDS double-buffered
+//    with one barrier per k-tile.
 //
 // Activation operand precision.  With bf16 weights the activation A may be stored in fp32; it is then
 // rounded to bf16 on the way into LDS, or (SPLIT = 2) split into hi = bf16(a) and lo = bf16(a - hi),
@@ -261,21 +266,312 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(const GemmParams p) {
         }
     } else {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i) {
+        // the 16 residuals of the fragment are loaded (rows clamped into the matrix) before any is used
+        float r[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = imin(m0 + wm + 32 * i + 8 * (e / 4) + 4 * half + (e % 4), p.M - 1);
+          const int64_t idx = (int64_t)m * p.N + n;
+          r[e] = p.resid_f32 ? ((const float *)p.resid)[idx] : to_f32(((const TM *)p.resid)[idx]);
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int m = m0 + wm + 32 * i + 8 * (e / 4) + 4 * half + (e % 4);
           if (m < p.M) {
             const int64_t idx = (int64_t)m * p.N + n;
-            const float r = p.resid_f32 ? ((const float *)p.resid)[idx] : to_f32(((const TM *)p.resid)[idx]);
-            const float y = acc[i][j][e] + bias + r;
+            const float y = acc[i][j][e] + bias + r[e];
             if (p.out32) p.out32[idx] = y;
             else if (p.y_f32) ((float *)p.out0)[idx] = y;
             else ((TM *)p.out0)[idx] = from_f32<TM>(y);
           }
         }
+      }
     }
   }
+}
+
+// ---------------------------------------------------------------------------------------------------
+// Large-tile kernel for bf16 weights and K a multiple of BK.
+//
+// Workgroup tile BM x BN in 4 waves of (BM/WM) x (BN/WN), two workgroups per CU; every operand goes
+// global -> LDS with direct-to-LDS loads into an S-stage ring, one barrier per k-tile.  LDS holds each
+// operand tile column-group-major: the BK-wide slice of a row is cut into 64-byte groups, and group g of
+// row r sits at (g * R + r) * 64 with its four 16-byte pieces XOR-permuted by bits 2..3 of r, so that one
+// 1 KB direct-to-LDS load fills 16 rows of one group and the 16 rows one fragment read touches land in
+// 16 distinct bank groups.  An fp32 activation (AK = kAkF32) or the gate's O and U (AK = kAkGate) are
+// staged as fp32 and turned into the bf16 operand (rounded, or split into hi + lo) while the fragment
+// is read, so no VALU work or registers are spent on staging.  Workgroups are dealt to the 8 XCDs
+// round-robin; the tile order gives each XCD a contiguous range of tiles, walked in groups of GM row
+// blocks, so that the workgroups resident on one XCD share A and B slices in its L2.
+//
+// The configurations below use 128 x 256 tiles (64 x 256 for the gate, whose A operand is 8 bytes per
+// element) with 2 x 2 waves and two workgroups per CU: one workgroup's barrier waits, prologue and
+// epilogue overlap the other's MFMA work, which single-workgroup 256 x 256 tiles cannot hide.
+enum AKind : int { kAkBf16 = 0, kAkF32 = 1, kAkGate = 2 };
+
+template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, int AK_, int SPLIT_, int GM_, int OCC_ = 1>
+struct BigCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_, AK = AK_, GM = GM_;
+  static constexpr int kOcc = OCC_;                                 // workgroups per CU
+  static constexpr int kTerms = (AK != kAkBf16 && SPLIT_ == 2) ? 2 : 1;
+  static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
+  static constexpr int kEA = AK == kAkBf16 ? 2 : 4;                 // A element bytes (global and LDS)
+  static constexpr int kABytes = BM * BK * kEA;
+  static constexpr int kUBytes = AK == kAkGate ? BM * BK * 4 : 0;
+  static constexpr int kBBytes = BN * BK * 2;
+  static constexpr int kStage = kABytes + kUBytes + kBBytes;
+  static constexpr int kDA = kABytes / 1024 / kWaves, kDU = kUBytes / 1024 / kWaves, kDB = kBBytes / 1024 / kWaves;
+  static constexpr int kD = kDA + kDU + kDB;                        // direct-to-LDS loads per wave per stage
+  static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  static constexpr int kSteps = BK / 16;
+  static constexpr int kLds = S * kStage;
+  static_assert((BK * kEA) % 64 == 0 && (BK * 2) % 64 == 0, "whole 64-byte column groups");
+  static_assert(kABytes % (1024 * kWaves) == 0 && kUBytes % (1024 * kWaves) == 0 &&
+                kBBytes % (1024 * kWaves) == 0, "loads split evenly over the waves");
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "32x32 fragments");
+  static_assert(S >= 2 && S <= 4 && (S - 2) * kD < 64, "ring depth");
+  static_assert(kLds * kOcc <= 160 * 1024, "LDS");
+};
+
+// LDS byte offset of 16-byte piece p (0..3) of column group g of row r, in a tile of R rows
+template <int R>
+__device__ __forceinline__ int cg_at(int r, int g, int p) {
+  return ((g * R + r) << 6) + ((p ^ ((r >> 2) & 3)) << 4);
+}
+
+// Eight fp32 values to bf16 (round to nearest even, two values per v_cvt_pk_bf16_f32), and the bf16
+// residuals x - hi, read back from the packed words without a second conversion.
+__device__ __forceinline__ u32x4 to_bf16x8(floatx4 x0, floatx4 x1) {
+  u32x4 h;
+  h.x = __builtin_bit_cast(uint32_t, bf16x2{f32_to_bf16(x0[0]), f32_to_bf16(x0[1])});
+  h.y = __builtin_bit_cast(uint32_t, bf16x2{f32_to_bf16(x0[2]), f32_to_bf16(x0[3])});
+  h.z = __builtin_bit_cast(uint32_t, bf16x2{f32_to_bf16(x1[0]), f32_to_bf16(x1[1])});
+  h.w = __builtin_bit_cast(uint32_t, bf16x2{f32_to_bf16(x1[2]), f32_to_bf16(x1[3])});
+  return h;
+}
+__device__ __forceinline__ float lo_half_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float hi_half_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+__device__ __forceinline__ u32x4 residual_bf16x8(floatx4 x0, floatx4 x1, u32x4 h) {
+  floatx4 r0, r1;
+  r0[0] = x0[0] - lo_half_f32(h.x); r0[1] = x0[1] - hi_half_f32(h.x);
+  r0[2] = x0[2] - lo_half_f32(h.y); r0[3] = x0[3] - hi_half_f32(h.y);
+  r1[0] = x1[0] - lo_half_f32(h.z); r1[1] = x1[1] - hi_half_f32(h.z);
+  r1[2] = x1[2] - lo_half_f32(h.w); r1[3] = x1[3] - hi_half_f32(h.w);
+  return to_bf16x8(r0, r1);
+}
+
+template <class C, int EPI>
+__global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const GemmParams p) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  HSTU_LDS char *smem = (HSTU_LDS char *)smem_raw;
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, FM = C::FM, FN = C::FN;
+
+  // ---- tile: XCD-contiguous ranges, groups of GM row blocks, row block fastest inside a group
+  const int nN = (p.N + BN - 1) / BN, nM = (p.M + BM - 1) / BM, total = nN * nM;
+  const int per = (total + 7) / 8;
+  const int w = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (w >= total) return;
+  const int grp = w / (C::GM * nN), gi = w % (C::GM * nN);
+  const int gm = imin(C::GM, nM - grp * C::GM);
+  const int m0 = (grp * C::GM + gi % gm) * BM, n0 = (gi / gm) * BN;
+
+  const int tid = threadIdx.x, lane = tid % 64, l32 = lane & 31, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // wave-uniform: LDS addresses go to M0
+  const int wm = (wave / C::WN) * C::TM, wn = (wave % C::WN) * C::TN;
+
+  // ---- per-lane source offsets of this wave's direct-to-LDS blocks (rows clamped into the matrix)
+  const int lrow = lane >> 2;
+  const uint32_t lpiece = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+  const int a_rows = imin(BM, p.M - m0), b_rows = imin(BN, p.N - n0);
+  const uint32_t a_rb = (uint32_t)p.K * C::kEA, b_rb = (uint32_t)p.K * 2u;
+  uint32_t aoff[C::kDA], boff[C::kDB];
+#pragma unroll
+  for (int t = 0; t < C::kDA; ++t) {
+    const int q = wave + t * C::kWaves, g = q / (BM / 16), r = (q % (BM / 16)) * 16 + lrow;
+    aoff[t] = (uint32_t)imin(r, a_rows - 1) * a_rb + (uint32_t)g * 64u + lpiece;
+  }
+#pragma unroll
+  for (int t = 0; t < C::kDB; ++t) {
+    const int q = wave + t * C::kWaves, g = q / (BN / 16), r = (q % (BN / 16)) * 16 + lrow;
+    boff[t] = (uint32_t)imin(r, b_rows - 1) * b_rb + (uint32_t)g * 64u + lpiece;
+  }
+  const char *abase = (const char *)p.a + (int64_t)m0 * a_rb;
+  const char *ubase = (const char *)p.gate_u + (int64_t)m0 * a_rb;
+  const char *bbase = (const char *)p.b + (int64_t)n0 * b_rb;
+
+  auto issue = [&](int kt, int slot) {
+    const uint32_t st = smem_addr + (uint32_t)(slot * C::kStage);
+    const char *ab = abase + (int64_t)kt * BK * C::kEA;
+#pragma unroll
+    for (int t = 0; t < C::kDA; ++t) dma16<0>(ab, aoff[t], st + (uint32_t)((wave + t * C::kWaves) * 1024));
+    if constexpr (C::AK == kAkGate) {
+      const char *ub = ubase + (int64_t)kt * BK * 4;
+#pragma unroll
+      for (int t = 0; t < C::kDU; ++t)
+        dma16<0>(ub, aoff[t], st + (uint32_t)(C::kABytes + (wave + t * C::kWaves) * 1024));
+    }
+    const char *bb = bbase + (int64_t)kt * BK * 2;
+#pragma unroll
+    for (int t = 0; t < C::kDB; ++t)
+      dma16<0>(bb, boff[t], st + (uint32_t)(C::kABytes + C::kUBytes + (wave + t * C::kWaves) * 1024));
+  };
+
+  // ---- gate: LayerNorm statistics of this lane's A rows, from the per-head (mean, M2) pairs
+  float rstd[C::AK == kAkGate ? FM : 1], nmr[C::AK == kAkGate ? FM : 1];
+  if constexpr (C::AK == kAkGate) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = imin(m0 + wm + 32 * i + l32, p.M - 1);
+      const float *st = p.row_stats + (int64_t)m * p.heads * 2;
+      float s = 0.0f;
+      for (int hh = 0; hh < p.heads; ++hh) s += st[2 * hh];
+      const float mean = s / (float)p.heads;
+      float m2 = 0.0f;
+      for (int hh = 0; hh < p.heads; ++hh) {
+        const float d = st[2 * hh] - mean;
+        m2 += st[2 * hh + 1] + (float)p.head_dim * d * d;
+      }
+      rstd[i] = 1.0f / sqrtf(m2 / (float)(p.heads * p.head_dim) + p.eps);
+      nmr[i] = -mean * rstd[i];
+    }
+  }
+
+  floatx16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx16{};
+
+  auto compute = [&](int slot) {
+    const HSTU_LDS char *As = smem + slot * C::kStage;
+    const HSTU_LDS char *Us = As + C::kABytes;
+    const HSTU_LDS char *Bs = As + C::kABytes + C::kUBytes;
+#pragma unroll
+    for (int st = 0; st < C::kSteps; ++st) {
+      bf16x8 bfr[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *(const HSTU_LDS bf16x8 *)(Bs + cg_at<BN>(wn + 32 * j + l32, st >> 1, 2 * (st & 1) + half));
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm + 32 * i + l32;
+        bf16x8 ahi, alo;
+        if constexpr (C::AK == kAkBf16) {
+          ahi = *(const HSTU_LDS bf16x8 *)(As + cg_at<BM>(r, st >> 1, 2 * (st & 1) + half));
+        } else {
+          u32x4 h, l;
+          floatx4 x0 = *(const HSTU_LDS floatx4 *)(As + cg_at<BM>(r, st, 2 * half));
+          floatx4 x1 = *(const HSTU_LDS floatx4 *)(As + cg_at<BM>(r, st, 2 * half + 1));
+          if constexpr (C::AK == kAkGate) {
+            const floatx4 u0 = *(const HSTU_LDS floatx4 *)(Us + cg_at<BM>(r, st, 2 * half));
+            const floatx4 u1 = *(const HSTU_LDS floatx4 *)(Us + cg_at<BM>(r, st, 2 * half + 1));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x0[e] = fmaf(x0[e], rstd[i], nmr[i]) * u0[e];
+              x1[e] = fmaf(x1[e], rstd[i], nmr[i]) * u1[e];
+            }
+          }
+          h = to_bf16x8(x0, x1);
+          ahi = __builtin_bit_cast(bf16x8, h);
+          if constexpr (C::kTerms == 2) {
+            l = residual_bf16x8(x0, x1, h);
+            alo = __builtin_bit_cast(bf16x8, l);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          acc[i][j] = mfma32(ahi, bfr[j], acc[i][j]);
+          if constexpr (C::kTerms == 2) acc[i][j] = mfma32(alo, bfr[j], acc[i][j]);
+        }
+      }
+    }
+  };
+
+  // ---- k loop over an S-stage ring
+  const int nk = p.K / BK;
+  constexpr int kAhead = C::S - 1;
+  for (int t = 0; t < kAhead; ++t)
+    if (t < nk) issue(t, t);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int after = imin(kAhead - 1, nk - 1 - kt);   // stages issued after this one
+    if constexpr (C::S >= 4) {
+      if (after >= 2) wait_vmcnt<2 * C::kD>();
+      else if (after == 1) wait_vmcnt<C::kD>();
+      else wait_vmcnt<0>();
+    } else if constexpr (C::S == 3) {
+      if (after >= 1) wait_vmcnt<C::kD>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();   // stage kt visible to every wave; every wave is done with stage kt - 1
+    if (kt + kAhead < nk) issue(kt + kAhead, (kt + kAhead) % C::S);
+    compute(kt % C::S);
+  }
+
+  // ---- epilogue: acc[i][j] element e -> row m0 + wm + 32i + 8(e/4) + 4 half + e%4, column n0 + wn + 32j + l32
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int n = n0 + wn + 32 * j + l32;
+    if (n >= p.N) continue;
+    const float bias = p.bias ? to_f32(((const __bf16 *)p.bias)[n]) : 0.0f;
+    if constexpr (EPI == kEpiUvqk) {
+      const int part = n / p.HD, col = n % p.HD;
+      void *dst = part == 0 ? p.out0 : part == 1 ? p.out1 : part == 2 ? p.out2 : p.out3;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + wm + 32 * i + 8 * (e / 4) + 4 * half + (e % 4);
+          if (m < p.M) {
+            const float s = silu_f32(acc[i][j][e] + bias);
+            const int64_t idx = (int64_t)m * p.HD + col;
+            if (part == 0) ((float *)dst)[idx] = s;
+            else ((__bf16 *)dst)[idx] = f32_to_bf16(s);
+          }
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        // the 16 residuals of the fragment are loaded (rows clamped into the matrix) before any is used
+        float r[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = imin(m0 + wm + 32 * i + 8 * (e / 4) + 4 * half + (e % 4), p.M - 1);
+          const int64_t idx = (int64_t)m * p.N + n;
+          r[e] = p.resid_f32 ? ((const float *)p.resid)[idx] : to_f32(((const __bf16 *)p.resid)[idx]);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + wm + 32 * i + 8 * (e / 4) + 4 * half + (e % 4);
+          if (m < p.M) {
+            const int64_t idx = (int64_t)m * p.N + n;
+            const float y = acc[i][j][e] + bias + r[e];
+            if (p.out32) p.out32[idx] = y;
+            else if (p.y_f32) ((float *)p.out0)[idx] = y;
+            else ((__bf16 *)p.out0)[idx] = f32_to_bf16(y);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <class C, int EPI>
+hipError_t launch_big(const GemmParams &p, hipStream_t s) {
+  if (p.M == 0 || p.N == 0) return hipSuccess;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_big_kernel<C, EPI>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const long long nt = (long long)((p.N + C::BN - 1) / C::BN) * ((p.M + C::BM - 1) / C::BM);
+  hipLaunchKernelGGL((gemm_big_kernel<C, EPI>), dim3((unsigned)((nt + 7) / 8 * 8)), dim3(C::kThreads), C::kLds, s, p);
+  return hipGetLastError();
 }
 
 template <typename TM, typename TA, int SPLIT, int EPI, bool GATE>
@@ -286,9 +582,32 @@ hipError_t launch(const GemmParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Large-tile configurations: <BM, BN, BK, stages, waves along M, waves along N, A kind, A terms, GM,
+// workgroups per CU>
+using CfgBf16 = BigCfg<128, 256, 32, 2, 2, 2, kAkBf16, 1, 4, 2>;
+using CfgF32 = BigCfg<128, 256, 32, 2, 2, 2, kAkF32, 1, 8, 2>;
+using CfgF32Split = BigCfg<128, 256, 32, 2, 2, 2, kAkF32, 2, 8, 2>;
+using CfgGate = BigCfg<64, 256, 32, 2, 2, 2, kAkGate, 1, 4, 2>;
+using CfgGateSplit = BigCfg<64, 256, 32, 2, 2, 2, kAkGate, 2, 4, 2>;
+
+// The large-tile kernel needs K to be a whole number of k-tiles and enough tiles to fill the chip.
+template <class C>
+bool big_fits(const GemmParams &p) {
+  const long long tiles = (long long)((p.N + C::BN - 1) / C::BN) * ((p.M + C::BM - 1) / C::BM);
+  return p.K % C::BK == 0 && tiles >= 256;
+}
+
 template <int EPI, bool GATE>
 hipError_t dispatch(const GemmParams &p, int dtype, int a_f32, int split, hipStream_t s) {
   if (dtype == kF32) return launch<float, float, 1, EPI, GATE>(p, s);
+  if constexpr (GATE) {
+    if (split && big_fits<CfgGateSplit>(p)) return launch_big<CfgGateSplit, EPI>(p, s);
+    if (!split && big_fits<CfgGate>(p)) return launch_big<CfgGate, EPI>(p, s);
+  } else {
+    if (a_f32 && split && big_fits<CfgF32Split>(p)) return launch_big<CfgF32Split, EPI>(p, s);
+    if (a_f32 && !split && big_fits<CfgF32>(p)) return launch_big<CfgF32, EPI>(p, s);
+    if (!a_f32 && big_fits<CfgBf16>(p)) return launch_big<CfgBf16, EPI>(p, s);
+  }
   if constexpr (!GATE) {
     if (!a_f32) return launch<__bf16, __bf16, 1, EPI, false>(p, s);
   }

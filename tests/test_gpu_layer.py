@@ -56,6 +56,21 @@ def test_layer_f32_residual_stream(act_split):
     assert_close(got, _oracle_stack(case), "bf16", "fp32 residual stream", magnitude_aware=True)
 
 
+@pytest.mark.parametrize("residual_f32,act_split", [(False, False), (True, False), (True, True)])
+def test_layer_large_tiles_ragged_tails(residual_f32, act_split):
+    """Enough rows for the large-tile GEMMs, with ragged row and column tails: T not a multiple of any
+    row tile, D = 352 (output-projection columns 256 + 96), H*Dh = 320 (U|V|Q|K boundaries inside
+    column tiles)."""
+    print(f"\n[case] large-tile GEMM tails residual_f32={residual_f32} act_split={act_split}", flush=True)
+    rng = np.random.default_rng(971)
+    lengths = [int(v) for v in rng.integers(1, 251, size=72)]
+    case = I.jagged_layer_case("tails", 971, lengths, D=352, H=5, Dh=64, P=64, Tb=64, dtype="bf16",
+                               num_layers=2, bias_std=0.2)
+    print(f"  T={sum(lengths)}", flush=True)
+    got = host(gpu_layer_stack(case, residual_f32=residual_f32, act_split=act_split))
+    assert_close(got, _oracle_stack(case), "bf16", "large-tile GEMM tails", magnitude_aware=True)
+
+
 def test_layer_candidates_small():
     print("\n[case] layer candidates small", flush=True)
     case = I.jagged_layer_case("candl", 970, [150, 40, 300], D=128, H=2, Dh=128, P=64, Tb=64, dtype="bf16",
