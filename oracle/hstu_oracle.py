@@ -182,6 +182,51 @@ def attn_fwd(jag: dict, q, k, v, pos_bias, time_bias, row_sample=None):
     return out
 
 
+# --------------------------------------------------------------------------- cached-history scoring
+def attn_cached(hist: dict, cand: dict, k_hist, v_hist, q, k, v, pos_bias, time_bias, attn_scale=None):
+    """Candidates scored against a cached user history: O [T_c, H, Dh] in float64.
+
+    Mini-batched candidate scoring ([HSTU] key contributions / technical approach: M-FALCON scores
+    candidates in mini-batches), read as: each user's history keys, values and timestamps are
+    computed once; a call scores some of that user's candidates, each against the whole history and
+    itself only ([DLRMv4] one training sample: candidates appended to the history see all of it).
+    hist: seq_offsets [B+1] into the history rows, timestamps [T_h]; cand: seq_offsets [B+1] into the
+    candidate rows, timestamps [T_c].  k_hist, v_hist: [T_h, H, Dh]; q, k, v: [T_c, H, Dh].
+    Candidate c of user b (n_h history tokens, m_b candidates in this call) has position n_h:
+        s_cj = q_c . k_j + w_p[min(n_h - j, P - 1)] + w_t[bt(tau_c, tau_j)]   for history j < n_h
+        s_cc = q_c . k_c + w_p[0] + w_t[0]                                     (itself: both distances 0)
+        O_c  = c_b * (sum_j SiLU(s_cj) v_j + SiLU(s_cc) v_c),  c_b = attn_scale[b] or 1 / (n_h + m_b)
+    """
+    k_hist = np.asarray(k_hist, np.float64)
+    v_hist = np.asarray(v_hist, np.float64)
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    wp = np.asarray(pos_bias, np.float64)
+    wt = np.asarray(time_bias, np.float64)
+    th = np.asarray(hist["timestamps"], np.int64)
+    tc = np.asarray(cand["timestamps"], np.int64)
+    ho = np.asarray(hist["seq_offsets"], np.int64)
+    co = np.asarray(cand["seq_offsets"], np.int64)
+    T_c, H, Dh = q.shape
+    R, P, Tb = wp.shape[0], wp.shape[1], wt.shape[1]
+    out = np.zeros((T_c, H, Dh), dtype=np.float64)
+    for b in range(len(co) - 1):
+        h0, h1, c0, c1 = int(ho[b]), int(ho[b + 1]), int(co[b]), int(co[b + 1])
+        n_h, m = h1 - h0, c1 - c0
+        if m == 0:
+            continue
+        scale = 1.0 / (n_h + m) if attn_scale is None else float(attn_scale[b])
+        j = np.arange(n_h, dtype=np.int64)
+        bp = np.minimum(n_h - j, P - 1)                                        # [n_h]
+        bt = time_bucket(tc[c0:c1][:, None], th[h0:h1][None, :], Tb)          # [m, n_h]
+        for h in range(H):
+            r = 0 if R == 1 else h
+            qh = q[c0:c1, h]
+            s_hist = qh @ k_hist[h0:h1, h].T + wp[r][bp][None, :] + wt[r][bt]
+            s_self = np.sum(qh * k[c0:c1, h], axis=1) + wp[r][0] + wt[r][0]
+            out[c0:c1, h] = scale * (silu(s_hist) @ v_hist[h0:h1, h] + silu(s_self)[:, None] * v[c0:c1, h])
+    return out
+
+
 # --------------------------------------------------------------------------- layer, stack, gather
 def projection(x, w_uvqk, b_uvqk, num_heads, head_dim):
     """Step 1 ([DLRMv4] Model architecture: a single projection makes all internal representations):
