@@ -78,6 +78,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_attn_fwd.restype = ctypes.c_int
     lib.hstu_attn_fwd.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT), ctypes.c_int, c_vp, c_vp, c_vp,
                                   c_vp, ctypes.c_int, c_vp, c_sz, c_vp]
+    lib.hstu_attn_cached_workspace_bytes.restype = c_sz
+    lib.hstu_attn_cached_workspace_bytes.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(JaggedT)]
+    lib.hstu_attn_fwd_cached.restype = ctypes.c_int
+    lib.hstu_attn_fwd_cached.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT),
+                                         ctypes.c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_int, c_vp, c_sz,
+                                         c_vp]
     lib.hstu_layer_workspace_bytes.restype = c_sz
     lib.hstu_layer_workspace_bytes.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT),
                                                ctypes.POINTER(LayerWeightsT), ctypes.c_int]
@@ -142,6 +148,27 @@ def attn_fwd(seq_offsets, timestamps, q, k, v, pos_bias, time_bias, *, max_seq_l
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device) if nws else None
     _check(lib.hstu_attn_fwd(ctypes.byref(jag), ctypes.byref(desc), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                              _dtype_code(out), _ptr(ws), nws, _stream(stream)))
+    return out
+
+
+def attn_fwd_cached(hist_offsets, hist_timestamps, k_hist, v_hist, cand_offsets, cand_timestamps, q, k, v,
+                    pos_bias, time_bias, *, max_candidates: int, attn_scale=None,
+                    out_dtype: Optional[torch.dtype] = None, out=None, workspace=None, stream=None):
+    """O = hstu_attn_fwd_cached(...): candidates q, k, v [T_c, H, Dh] against the cached history
+    k_hist, v_hist [T_h, H, Dh]; returns out [T_c, H, Dh]."""
+    lib = load_library()
+    T, H, Dh = q.shape
+    if out is None:
+        out = torch.empty((T, H, Dh), dtype=out_dtype or q.dtype, device=q.device)
+    hist = make_jagged(hist_offsets, hist_timestamps, 0)
+    cand = make_jagged(cand_offsets, cand_timestamps, max_candidates, None, attn_scale)
+    desc = make_desc(H, Dh, pos_bias, time_bias)
+    nws = int(lib.hstu_attn_cached_workspace_bytes(ctypes.byref(hist), ctypes.byref(cand)))
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.hstu_attn_fwd_cached(ctypes.byref(hist), ctypes.byref(cand), ctypes.byref(desc), _dtype_code(q),
+                                    _ptr(k_hist), _ptr(v_hist), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                    _dtype_code(out), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
 
 

@@ -192,6 +192,81 @@ hstu_status_t hstu_attn_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *de
   }
 }
 
+size_t hstu_attn_cached_workspace_bytes(const hstu_jagged_t *hist, const hstu_jagged_t *cand) {
+  if (!hist || !cand || hist->num_seqs < 0 || cand->num_seqs != hist->num_seqs) return 0;
+  if (cand->total_tokens <= 0) return 0;
+  const int64_t Th = hist->total_tokens > 0 ? hist->total_tokens : 0;
+  return round_up(hstu::attn_tau_stats_bytes(cand->total_tokens, cand->num_seqs), 256) +
+         round_up(hstu::attn_tau_stats_bytes(Th, hist->num_seqs), 256);
+}
+
+hstu_status_t hstu_attn_fwd_cached(const hstu_jagged_t *hist, const hstu_jagged_t *cand, const hstu_attn_desc_t *desc,
+                                   hstu_dtype_t in_dtype, const void *k_hist, const void *v_hist, const void *q,
+                                   const void *k, const void *v, void *out, hstu_dtype_t out_dtype, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  try {
+    if (!hist) return fail(HSTU_ERR_INVALID_ARGUMENT, "hist is NULL");
+    if (!desc) return fail(HSTU_ERR_INVALID_ARGUMENT, "desc is NULL");
+    hstu_attn_desc_t d = *desc;   // the mask field is not read: the candidate mask is implied
+    d.mask = HSTU_MASK_CAUSAL;
+    hstu_status_t st = check_jagged_desc(cand, &d);
+    if (st != HSTU_OK) return st;
+    if (hist->num_seqs != cand->num_seqs)
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "hist->num_seqs = %d != cand->num_seqs = %d", hist->num_seqs,
+                  cand->num_seqs);
+    if (hist->total_tokens < 0) return fail(HSTU_ERR_INVALID_ARGUMENT, "hist->total_tokens = %d < 0", hist->total_tokens);
+    if (!valid_dtype(in_dtype)) return fail(HSTU_ERR_INVALID_ARGUMENT, "in_dtype = %d invalid", (int)in_dtype);
+    if (!valid_dtype(out_dtype)) return fail(HSTU_ERR_INVALID_ARGUMENT, "out_dtype = %d invalid", (int)out_dtype);
+    if (in_dtype == HSTU_F32 && out_dtype != HSTU_F32)
+      return fail(HSTU_ERR_UNSUPPORTED, "f32 inputs need an f32 output");
+    const size_t need = hstu_attn_cached_workspace_bytes(hist, cand);
+    if (workspace_bytes < need)
+      return fail(HSTU_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+    const int64_t Tc = cand->total_tokens, Th = hist->total_tokens;
+    if (Tc == 0) return ok();
+    if (cand->num_seqs > 0 && !hist->seq_offsets) return fail(HSTU_ERR_INVALID_ARGUMENT, "hist->seq_offsets is NULL");
+    if (Th > 0 && !hist->timestamps) return fail(HSTU_ERR_INVALID_ARGUMENT, "hist->timestamps is NULL");
+    if (Th > 0 && (!k_hist || !v_hist)) return fail(HSTU_ERR_INVALID_ARGUMENT, "k_hist/v_hist is NULL");
+    if (!workspace) return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if (!aligned16(workspace)) return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    if (!q || !k || !v || !out) return fail(HSTU_ERR_INVALID_ARGUMENT, "q/k/v/out is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(k_hist) ||
+        !aligned16(v_hist))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "q/k/v/out/k_hist/v_hist must be 16-byte aligned");
+    const size_t hd = (size_t)desc->num_heads * desc->head_dim;
+    const size_t nin = (size_t)Tc * hd * esize(in_dtype), nhist = (size_t)Th * hd * esize(in_dtype);
+    const size_t nout = (size_t)Tc * hd * esize(out_dtype);
+    if (overlaps(out, nout, q, nin) || overlaps(out, nout, k, nin) || overlaps(out, nout, v, nin) ||
+        overlaps(out, nout, k_hist, nhist) || overlaps(out, nout, v_hist, nhist))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "out overlaps an input");
+    if (overlaps(workspace, need, out, nout) || overlaps(workspace, need, q, nin) || overlaps(workspace, need, k, nin) ||
+        overlaps(workspace, need, v, nin) || overlaps(workspace, need, k_hist, nhist) ||
+        overlaps(workspace, need, v_hist, nhist))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace overlaps an input or out");
+    hstu::AttnArgs a = attn_args(cand, &d);
+    a.num_candidates = nullptr;
+    a.mask = hstu::kCausalCandidates;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.row_stride = (int64_t)hd;
+    a.out_row_stride = a.row_stride;
+    a.in_dtype = in_dtype == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
+    a.out_dtype = out_dtype == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
+    a.tau_stats = (int64_t *)workspace;
+    a.k_hist = k_hist;
+    a.v_hist = v_hist;
+    a.hist_offsets = hist->seq_offsets;
+    a.hist_timestamps = hist->timestamps;
+    a.hist_tau_stats =
+        (int64_t *)((char *)workspace + round_up(hstu::attn_tau_stats_bytes(Tc, cand->num_seqs), 256));
+    return from_hip(hstu::launch_attn_cached(a, (hipStream_t)stream), "attn_fwd_cached launch");
+  } catch (...) {
+    return fail(HSTU_ERR_DEVICE, "unexpected C++ exception in hstu_attn_fwd_cached");
+  }
+}
+
 size_t hstu_layer_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc,
                                   const hstu_layer_weights_t *w, hstu_dtype_t dtype) {
   if (!jag || !desc || !w || jag->total_tokens < 0 || desc->num_heads < 1 || desc->head_dim < 1 || w->d_model < 1)

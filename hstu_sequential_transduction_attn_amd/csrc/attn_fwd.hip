@@ -330,7 +330,14 @@ __global__ void __launch_bounds__(256) tau_chunk_stats_kernel(const int32_t *__r
 }
 
 // Two waves per SIMD (<= 256 registers per lane) so that one wave's MFMAs overlap the other's VALU work.
-template <typename T, int DH, typename TO>
+//
+// CACHED: candidates scored against a cached history.  The queries are the candidate rows (q,
+// seq_offsets, timestamps); user b's keys are its n_h cached history rows (k_hist, v_hist,
+// hist_offsets, hist_timestamps), every one of them allowed, and each candidate also sees itself,
+// which the epilogue adds as one extra score per row.  A candidate has position n_h and local index
+// n_h + c in the virtual sequence [history | candidates], so the tile classes, buckets and masks are
+// those of the candidate rows of the one-pass candidate mask.
+template <typename T, int DH, typename TO, bool CACHED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   using L = Layout<T, DH>;
@@ -345,17 +352,26 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   const int qblk = n_qblocks - 1 - item / HB;
   const int b = (item % HB) / p.num_heads;
   const int h = (item % HB) % p.num_heads;
+  // o0/nq: first row and count of this sequence's query rows; ho/nh: first key row and history length;
+  // vq0: local (virtual-sequence) index of query row 0; n: virtual sequence length
   const int o0 = p.seq_offsets[b];
-  const int n = p.seq_offsets[b + 1] - o0;
+  const int nq = p.seq_offsets[b + 1] - o0;
   const int q0 = qblk * kBM;
-  if (q0 >= n) return;  // uniform over the workgroup
-  const bool cand = p.mask == kCausalCandidates;
-  const int nh = cand ? n - p.num_candidates[b] : n;
+  if (q0 >= nq) return;  // uniform over the workgroup
+  const bool cand = CACHED || p.mask == kCausalCandidates;
+  const int ho = CACHED ? p.hist_offsets[b] : o0;
+  const int nh = CACHED ? p.hist_offsets[b + 1] - ho : (cand ? nq - p.num_candidates[b] : nq);
+  const int vq0 = CACHED ? nh : 0;
+  const int n = vq0 + nq;
+  const int nkeys = CACHED ? nh : nq;             // rows of the key buffers of this sequence
   const float cb = p.attn_scale ? p.attn_scale[b] : 1.0f / (float)n;
   const int P = p.num_pos_buckets;
   const int Tb = p.num_time_buckets;
   const int rr = p.rab_rows == 1 ? 0 : h;
-  const int64_t *cstats = p.tau_stats + 2 * (int64_t)((o0 >> 5) + b);   // chunk c at cstats[2c], [2c+1]
+  // 32-token timestamp ranges: chunk c at [2c], [2c+1]; of the query rows and of the key rows
+  const int64_t *qstats = p.tau_stats + 2 * (int64_t)((o0 >> 5) + b);
+  const int64_t *kstats = CACHED ? p.hist_tau_stats + 2 * (int64_t)((ho >> 5) + b) : qstats;
+  const int64_t *ktau = CACHED ? p.hist_timestamps : p.timestamps;
 
   const int tid = threadIdx.x;
   // wave index in a scalar register: the query range and the tile classes derived from it are
@@ -373,19 +389,21 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   for (int i = tid; i < nt_tab; i += kThreads) wt_lds[i] = p.time_bias[(int64_t)rr * Tb + i];
 
   // ---- this wave's queries
-  const int qa = q0 + wave * kQW;                 // first query of the wave (a multiple of 32)
-  const int ql = imin(qa + kQW - 1, n - 1);       // last valid query of the wave
-  const bool wave_active = qa < n;
-  const int my_q = qa + l32;
-  const bool my_valid = my_q < n;
-  const int64_t my_tau = my_valid ? p.timestamps[o0 + my_q] : 0;
-  const int64_t wmin = wave_active ? cstats[2 * (qa >> 5)] : 0;
-  const int64_t wmax = wave_active ? cstats[2 * (qa >> 5) + 1] : 0;
+  const int qr = q0 + wave * kQW;                 // first query row of the wave (a multiple of 32)
+  const int qa = vq0 + qr;                        // its local index
+  const int ql = vq0 + imin(qr + kQW - 1, nq - 1);   // local index of the wave's last valid query
+  const bool wave_active = qr < nq;
+  const int my_row = qr + l32;                    // this lane's query row (sequence-relative)
+  const int my_q = vq0 + my_row;                  // its local index
+  const bool my_valid = my_row < nq;
+  const int64_t my_tau = my_valid ? p.timestamps[o0 + my_row] : 0;
+  const int64_t wmin = wave_active ? qstats[2 * (qr >> 5)] : 0;
+  const int64_t wmax = wave_active ? qstats[2 * (qr >> 5) + 1] : 0;
 
   // Q fragments (B operand of S^T = K Q^T): lane holds query l32, dh = kKStep*s + kKPL*half + [0, kKPL)
   Frag qf[L::kQSteps];
   {
-    const T *qrow = (const T *)p.q + (int64_t)(o0 + (my_valid ? my_q : 0)) * p.row_stride + h * DH;
+    const T *qrow = (const T *)p.q + (int64_t)(o0 + (my_valid ? my_row : 0)) * p.row_stride + h * DH;
 #pragma unroll
     for (int s = 0; s < L::kQSteps; ++s) {
       if constexpr (L::kBf16) {
@@ -399,10 +417,10 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   }
 
   // ---- key tiles needed by the workgroup: [0, r1_end) and, for candidate rows, their own tiles
-  const int blast = imin(q0 + kBM - 1, n - 1);
+  const int blast = vq0 + imin(q0 + kBM - 1, nq - 1);
   const int r1_end = (imin(blast + 1, nh) + kBN - 1) / kBN;
   int r2_begin = 0, r2_end = 0;
-  if (blast >= nh) {
+  if (!CACHED && blast >= nh) {
     r2_begin = imax(imax(q0, nh) / kBN, r1_end);
     r2_end = blast / kBN + 1;
   }
@@ -420,19 +438,19 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   const uint32_t v_add = (uint32_t)(h * L::kRB) + 16u * (uint32_t)(lane & 3);
   const int tr16 = 16 * wave + ((lane & 31) >> 1);               // tile-local key of this lane's tau word
   const uint32_t t_add = 4u * (uint32_t)(lane & 1);
-  const char *kbase = (const char *)p.k, *vbase = (const char *)p.v;
+  const char *kbase = (const char *)(CACHED ? p.k_hist : p.k), *vbase = (const char *)(CACHED ? p.v_hist : p.v);
   auto issue_tile = [&](int i, int stage) {
     const int k0 = tile_of(i) * kBN;
-    const int lim = n - 1 - k0;                                  // >= 0: every tile starts inside the sequence
+    const int lim = nkeys - 1 - k0;                              // >= 0: every tile starts inside the keys
     const uint32_t r = (uint32_t)imin(lr16, lim);
     const uint32_t koff = __umul24(r, rsb) + k_add;
     const uint32_t voff = __umul24(r, rsb) + v_add;
     const uint32_t toff = 8u * (uint32_t)imin(tr16, lim) + t_add;
-    const int64_t row0 = (int64_t)(o0 + k0) * rsb;
+    const int64_t row0 = (int64_t)(ho + k0) * rsb;
     const uint32_t sb = smem_addr + stage * L::kStageBytes;
     dma_groups<0, L::kG>(kbase + row0, vbase + row0, koff, voff, sb + L::kOffK + wave * 1024,
                          sb + L::kOffV + wave * 1024);
-    dma4((const char *)(p.timestamps + o0 + k0), toff, sb + L::kOffTau + 256 * wave);
+    dma4((const char *)(ktau + ho + k0), toff, sb + L::kOffTau + 256 * wave);
   };
 
   // ---- tile classes, one tile per lane, 64 tiles at a time (vector code, once per 64 tiles)
@@ -449,9 +467,9 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
       const bool none = k0 > ql || (k0 >= nh && k0 + kBN - 1 < imax(qa, nh));
       if (!none) {
         const int c0 = k0 >> 5;
-        int64_t kmin = cstats[2 * c0], kmax = cstats[2 * c0 + 1];
-        if (k0 + kChunk < n) {
-          const int64_t a = cstats[2 * c0 + 2], bb = cstats[2 * c0 + 3];
+        int64_t kmin = kstats[2 * c0], kmax = kstats[2 * c0 + 1];
+        if (k0 + kChunk < nkeys) {
+          const int64_t a = kstats[2 * c0 + 2], bb = kstats[2 * c0 + 3];
           kmin = a < kmin ? a : kmin;
           kmax = bb > kmax ? bb : kmax;
         }
@@ -495,7 +513,9 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   for (int d = 0; d < L::kDB; ++d) oacc.d[d] = floatx16{};
 
   TileCtx c;
-  c.my_q = my_q;
+  // cached mode: the tiles hold history keys only (rows past the history repeat its last row), and the
+  // candidate's score against itself is added in the epilogue, so no tile key may match it
+  c.my_q = CACHED ? -1 : my_q;
   c.my_pos = cand ? imin(my_q, nh) : my_q;
   c.pos_lim = cand ? nh : n;
   // a history query sees keys 0..my_q, a candidate the whole history and itself (every allowed key is
@@ -543,6 +563,34 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
 
   // ---- epilogue: O^T element e of dh block db is dh = 32*db + 8*(e/4) + 4*half + e%4; the sums carry
   // the factor -log2(e) of the folded SiLU, removed here together with c_b
+  if constexpr (CACHED) {
+    // the candidate's score against itself: both distances are 0, so the bias is w_p[0] + w_t[0]
+    const int64_t crow = (int64_t)(o0 + (my_valid ? my_row : 0));
+    const T *krow = (const T *)p.k + crow * p.row_stride + h * DH;
+    const T *vrow = (const T *)p.v + crow * p.row_stride + h * DH;
+    float dot = 0.0f;
+#pragma unroll
+    for (int st = 0; st < L::kQSteps; ++st) {
+      if constexpr (L::kBf16) {
+        const bf16x8 kv = *(const bf16x8 *)(krow + st * 16 + half * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot = fmaf(bf16_to_f32(qf[st][e]), bf16_to_f32(kv[e]), dot);
+      } else {
+        dot = fmaf(qf[st], krow[st * 2 + half], dot);
+      }
+    }
+    dot += __shfl_xor(dot, 32, kWave);
+    const float u = (dot + wp_lds[0] + wt_lds[0]) * kNegLog2e;
+    const float a = my_valid ? u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u)) : 0.0f;
+#pragma unroll
+    for (int db = 0; db < L::kDB; ++db)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int dh = 32 * db + 8 * e4 + 4 * half;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) oacc.d[db][4 * e4 + x] = fmaf(a, to_f32(vrow[dh + x]), oacc.d[db][4 * e4 + x]);
+      }
+  }
   const float scale = cb * kNegLn2;
   if (p.row_stats) {
     // mean and sum of squared deviations of the stored head row: each lane holds 16*kDB of its query's
@@ -565,13 +613,13 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
     const float mean_o = __shfl_xor(mean_l, 32, kWave), m2_o = __shfl_xor(m2_l, 32, kWave);
     const float dm = mean_l - mean_o;
     if (my_valid && half == 0) {
-      float *st = p.row_stats + 2 * ((int64_t)(o0 + my_q) * p.num_heads + h);
+      float *st = p.row_stats + 2 * ((int64_t)(o0 + my_row) * p.num_heads + h);
       st[0] = 0.5f * (mean_l + mean_o);
       st[1] = m2_l + m2_o + dm * dm * (0.5f * kN);
     }
   }
   if (my_valid) {
-    TO *orow = (TO *)p.out + (int64_t)(o0 + my_q) * p.out_row_stride + h * DH;
+    TO *orow = (TO *)p.out + (int64_t)(o0 + my_row) * p.out_row_stride + h * DH;
 #pragma unroll
     for (int db = 0; db < L::kDB; ++db) {
 #pragma unroll
@@ -593,7 +641,7 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   }
 }
 
-template <typename T, int DH, typename TO>
+template <typename T, int DH, typename TO, bool CACHED>
 hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
   using L = Layout<T, DH>;
   const int n_qblocks = (a.max_seq_len + kBM - 1) / kBM;
@@ -603,23 +651,27 @@ hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
   const size_t lds = (size_t)L::kStages * L::kStageBytes + (size_t)(a.num_pos_buckets + kTimeTab) * sizeof(float);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_kernel<T, DH, TO>,
+    hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_kernel<T, DH, TO, CACHED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   hipLaunchKernelGGL(tau_chunk_stats_kernel, dim3(a.num_seqs), dim3(256), 0, stream, a.seq_offsets, a.timestamps,
                      a.tau_stats);
-  hipLaunchKernelGGL((attn_fwd_kernel<T, DH, TO>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a, n_qblocks);
+  if constexpr (CACHED)
+    hipLaunchKernelGGL(tau_chunk_stats_kernel, dim3(a.num_seqs), dim3(256), 0, stream, a.hist_offsets,
+                       a.hist_timestamps, a.hist_tau_stats);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, DH, TO, CACHED>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a,
+                     n_qblocks);
   return hipGetLastError();
 }
 
-template <typename T, typename TO>
+template <typename T, typename TO, bool CACHED>
 hipError_t launch_dh(const AttnArgs &a, hipStream_t stream) {
   switch (a.head_dim) {
-    case 32: return launch_typed<T, 32, TO>(a, stream);
-    case 64: return launch_typed<T, 64, TO>(a, stream);
-    case 128: return launch_typed<T, 128, TO>(a, stream);
+    case 32: return launch_typed<T, 32, TO, CACHED>(a, stream);
+    case 64: return launch_typed<T, 64, TO, CACHED>(a, stream);
+    case 128: return launch_typed<T, 128, TO, CACHED>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -632,9 +684,16 @@ size_t attn_tau_stats_bytes(int64_t total_tokens, int64_t num_seqs) {
 
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream) {
   if (a.in_dtype == kBF16) {
-    return a.out_dtype == kBF16 ? launch_dh<__bf16, __bf16>(a, stream) : launch_dh<__bf16, float>(a, stream);
+    return a.out_dtype == kBF16 ? launch_dh<__bf16, __bf16, false>(a, stream) : launch_dh<__bf16, float, false>(a, stream);
   }
-  return launch_dh<float, float>(a, stream);
+  return launch_dh<float, float, false>(a, stream);
+}
+
+hipError_t launch_attn_cached(const AttnArgs &a, hipStream_t stream) {
+  if (a.in_dtype == kBF16) {
+    return a.out_dtype == kBF16 ? launch_dh<__bf16, __bf16, true>(a, stream) : launch_dh<__bf16, float, true>(a, stream);
+  }
+  return launch_dh<float, float, true>(a, stream);
 }
 
 }  // namespace hstu

@@ -30,11 +30,20 @@ struct AttnArgs {
   int64_t *tau_stats;             // workspace: attn_tau_stats_bytes() of per-32-token timestamp ranges
   float *row_stats;               // [T][H][2] mean and sum of squared deviations of each stored head row
                                   // (fp32 output only; the gate of the output projection uses them), or null
+  // Cached-history scoring only (launch_attn_cached): the fields above describe the candidate rows
+  // (q, k, v, out, seq_offsets, timestamps, tau_stats; max_seq_len = most candidates of one user);
+  // the keys are each user's cached history rows.
+  const void *k_hist, *v_hist;     // [T_h][row_stride] elements
+  const int32_t *hist_offsets;     // [B+1]
+  const int64_t *hist_timestamps;  // [T_h]
+  int64_t *hist_tau_stats;         // workspace: attn_tau_stats_bytes(T_h, B)
 };
 
 // Workspace bytes of the per-32-token timestamp ranges the attention kernel classifies tiles with.
 size_t attn_tau_stats_bytes(int64_t total_tokens, int64_t num_seqs);
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream);
+// Candidates against a cached history: each candidate sees every history key of its user and itself.
+hipError_t launch_attn_cached(const AttnArgs &a, hipStream_t stream);
 
 // C[M][N] = epilogue(A[M][K] * B[N][K]^T): bf16 or f32 weights (MFMA operand type `dtype`), fp32
 // accumulation.  With bf16 weights the activation A may be fp32 (x_f32 / g_f32): rounded to bf16, or with

@@ -239,3 +239,53 @@ def attn_case(name: str, config_id: int, lengths: List[int], H: int, Dh: int, P:
     return AttnCase(name=name, jagged=jag, rab=rab, q=Tensor.make(q, dtype), k=Tensor.make(k, dtype),
                     v=Tensor.make(v, dtype), u=None if u is None else Tensor.make(u, dtype),
                     num_heads=H, head_dim=Dh, dtype=dtype)
+
+
+# --------------------------------------------------------------------------- cached-history scoring
+@dataclasses.dataclass
+class CachedCase:
+    """A candidate batch split from a one-pass candidate case: each user's history rows (the cache) and
+    the candidate rows, plus where the candidates sit in the one-pass layout."""
+    name: str
+    hist_offsets: np.ndarray        # int32 [B+1]
+    hist_timestamps: np.ndarray     # int64 [T_h]
+    cand_offsets: np.ndarray        # int32 [B+1]
+    cand_timestamps: np.ndarray     # int64 [T_c]
+    k_hist: Tensor                  # [T_h, H, Dh]
+    v_hist: Tensor
+    q: Tensor                       # [T_c, H, Dh]
+    k: Tensor
+    v: Tensor
+    rab: Rab
+    num_heads: int
+    head_dim: int
+    dtype: str
+    cand_rows: np.ndarray           # int64 [T_c]: row of each candidate in the one-pass batch
+    one_pass_lengths: np.ndarray    # int64 [B]: n_h + m_b
+
+    @property
+    def max_candidates(self) -> int:
+        d = np.diff(self.cand_offsets.astype(np.int64))
+        return int(d.max()) if len(d) else 0
+
+
+def _take(t: Tensor, idx: np.ndarray) -> Tensor:
+    return Tensor(values=t.values[idx], dtype=t.dtype, bits=None if t.bits is None else t.bits[idx])
+
+
+def split_candidates(case: AttnCase) -> CachedCase:
+    """Slices a candidate-mask case (num_candidates set) into history and candidate parts per user."""
+    offs = case.jagged.seq_offsets.astype(np.int64)
+    m = case.jagged.num_candidates.astype(np.int64)
+    B = len(offs) - 1
+    hist_idx = [np.arange(offs[b], offs[b + 1] - m[b]) for b in range(B)]
+    cand_idx = [np.arange(offs[b + 1] - m[b], offs[b + 1]) for b in range(B)]
+    hi = np.concatenate(hist_idx) if B else np.zeros(0, np.int64)
+    ci = np.concatenate(cand_idx) if B else np.zeros(0, np.int64)
+    tau = case.jagged.timestamps
+    return CachedCase(name=case.name + "_cached", hist_offsets=offsets_of([len(x) for x in hist_idx]),
+                      hist_timestamps=tau[hi], cand_offsets=offsets_of([len(x) for x in cand_idx]),
+                      cand_timestamps=tau[ci], k_hist=_take(case.k, hi), v_hist=_take(case.v, hi),
+                      q=_take(case.q, ci), k=_take(case.k, ci), v=_take(case.v, ci), rab=case.rab,
+                      num_heads=case.num_heads, head_dim=case.head_dim, dtype=case.dtype, cand_rows=ci,
+                      one_pass_lengths=np.diff(offs))

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 1
+#define HSTU_ABI_VERSION 2
 
 typedef enum {
   HSTU_OK = 0,
@@ -129,6 +129,41 @@ size_t hstu_attn_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_
 hstu_status_t hstu_attn_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, hstu_dtype_t in_dtype,
                             const void *q, const void *k, const void *v, void *out, hstu_dtype_t out_dtype,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace needed by hstu_attn_fwd_cached (bytes; 0 is possible): the per-32-token timestamp ranges
+ * of the candidate rows and of the history rows.  Depends only on the host fields of hist and cand.
+ */
+size_t hstu_attn_cached_workspace_bytes(const hstu_jagged_t *hist, const hstu_jagged_t *cand);
+
+/*
+ * Candidates scored against a cached history: mini-batched candidate scoring ("Actions Speak Louder
+ * than Words ..." summary page, key contributions and technical approach: M-FALCON), with each
+ * candidate seeing the whole history of its user and itself ("DLRMv4" page, section on how one training
+ * sample is processed).  For every candidate row c of user b (n_h history tokens, m_b candidates in
+ * this call, every candidate at position n_h):
+ *   out[c][h][:] = c_b * ( sum_{j < n_h} SiLU(q_c . k_hist_j + w_p[min(n_h - j, P-1)] + w_t[bt(tau_c, tau_j)]) v_hist_j
+ *                          + SiLU(q_c . k_c + w_p[0] + w_t[0]) v_c ),
+ *   c_b = cand->attn_scale[b], or 1 / (n_h + m_b) when attn_scale is NULL.
+ * With all of a user's candidates in one call (or with attn_scale carrying that c_b) this equals the
+ * candidate rows of hstu_attn_fwd with HSTU_MASK_CAUSAL_CANDIDATES over [history | candidates], so the
+ * history's keys and values, computed once, serve any number of candidate micro-batches.
+ * hist: num_seqs = B, total_tokens = T_h, seq_offsets [B+1], timestamps [T_h] (device); max_seq_len,
+ *       num_candidates and attn_scale are not read.
+ * cand: num_seqs = B (the same users, in the same order), total_tokens = T_c, max_seq_len = the most
+ *       candidates of one user, seq_offsets [B+1], timestamps [T_c], attn_scale [B] or NULL (device);
+ *       num_candidates is not read.
+ * desc: as for hstu_attn_fwd; desc->mask is not read.
+ * k_hist, v_hist: [T_h][H][Dh]; q, k, v (the candidates' own rows): [T_c][H][Dh]; all in_dtype,
+ * row-major, 16-byte aligned (device).  out: [T_c][H][Dh], out_dtype = HSTU_F32 or in_dtype; may not
+ * overlap an input or the workspace.  Caller-owned; nothing is allocated or retained.
+ * Errors: as for hstu_attn_fwd; hist->num_seqs != cand->num_seqs, or a NULL pointer that the sizes
+ * require, is HSTU_ERR_INVALID_ARGUMENT.
+ */
+hstu_status_t hstu_attn_fwd_cached(const hstu_jagged_t *hist, const hstu_jagged_t *cand, const hstu_attn_desc_t *desc,
+                                   hstu_dtype_t in_dtype, const void *k_hist, const void *v_hist, const void *q,
+                                   const void *k, const void *v, void *out, hstu_dtype_t out_dtype, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 /* Workspace needed by hstu_layer_fwd (bytes). */
 size_t hstu_layer_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc,

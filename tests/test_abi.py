@@ -39,7 +39,7 @@ def _attn(jag, desc, in_dt=L.HSTU_BF16, out_dt=L.HSTU_BF16, q=P16 + 0x10000, k=P
 
 def test_exports_every_declared_symbol():
     names = L.exported_functions_in_header()
-    assert len(names) == 8
+    assert len(names) == 10
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib()
-    assert lib.hstu_abi_version() == 1
+    assert lib.hstu_abi_version() == 2
     assert lib.hstu_status_string(OK) == b"HSTU_OK"
     assert lib.hstu_status_string(WS_SMALL) == b"HSTU_ERR_WORKSPACE_TOO_SMALL"
     assert lib.hstu_status_string(99) == b"HSTU_STATUS_UNKNOWN"
@@ -148,3 +148,49 @@ def test_python_binding_raises_with_message():
     with pytest.raises(L.HstuError) as ei:
         L._check(UNSUPPORTED)
     assert ei.value.name == "HSTU_ERR_UNSUPPORTED"
+
+
+def _cached(hist, cand, desc, in_dt=L.HSTU_BF16, out_dt=L.HSTU_BF16, kh=P16 + 0x100000, vh=P16 + 0x8000000,
+            q=P16 + 0x10000000, k=P16 + 0x20000000, v=P16 + 0x30000000, out=P16 + 0x40000000,
+            ws=P16 + 0x80000000, nws=1 << 20):
+    lib = _lib()
+    st = lib.hstu_attn_fwd_cached(ctypes.byref(hist) if hist else None, ctypes.byref(cand) if cand else None,
+                                  ctypes.byref(desc) if desc else None, in_dt, kh, vh, q, k, v, out, out_dt, ws, nws,
+                                  None)
+    return st, lib.hstu_last_error().decode()
+
+
+def test_cached_argument_errors():
+    hist, cand = _jag(B=2, T=500, max_len=300), _jag(B=2, T=64, max_len=40)
+    assert _cached(None, cand, _desc())[0] == INVALID
+    assert _cached(hist, None, _desc())[0] == INVALID
+    assert _cached(hist, cand, None)[0] == INVALID
+    st, msg = _cached(_jag(B=3, T=500, max_len=300), cand, _desc())
+    assert st == INVALID and "num_seqs" in msg
+    st, msg = _cached(hist, cand, _desc(Dh=96))
+    assert st == UNSUPPORTED and "head_dim" in msg
+    st, msg = _cached(hist, cand, _desc(), in_dt=L.HSTU_F32, out_dt=L.HSTU_BF16)
+    assert st == UNSUPPORTED
+    st, msg = _cached(hist, cand, _desc(), nws=16)
+    assert st == WS_SMALL
+    st, msg = _cached(hist, cand, _desc(), q=P16 + 8)
+    assert st == INVALID and "aligned" in msg
+    st, msg = _cached(hist, cand, _desc(), out=P16 + 0x10000000)
+    assert st == INVALID and "overlaps" in msg
+    # the mask field is not read: a candidate mask without num_candidates is fine up to the launch
+    st, msg = _cached(hist, cand, _desc(mask=1), nws=16)
+    assert st == WS_SMALL
+
+
+def test_cached_zero_candidates_is_a_no_op():
+    hist, cand = _jag(B=2, T=500, max_len=300), _jag(B=2, T=0, max_len=0)
+    assert _cached(hist, cand, _desc(), ws=None, nws=0)[0] == OK
+
+
+def test_cached_workspace_covers_both_timestamp_ranges():
+    lib = _lib()
+    hist, cand = _jag(B=4, T=1000, max_len=300), _jag(B=4, T=64, max_len=40)
+    n = lib.hstu_attn_cached_workspace_bytes(ctypes.byref(hist), ctypes.byref(cand))
+    one = lib.hstu_attn_workspace_bytes(ctypes.byref(cand), ctypes.byref(_desc()), L.HSTU_BF16)
+    assert n > one and n % 256 == 0
+    assert lib.hstu_attn_cached_workspace_bytes(ctypes.byref(_jag(B=3)), ctypes.byref(cand)) == 0
