@@ -219,6 +219,85 @@ def extended(args, dev):
         print(f"[extended] {name}: {ms:.3f} ms per forward ({len(layers)} layers, T={T}, D={D}, H={H}x{Dh}); "
               f"{flop:.3e} algorithmic FLOP -> {flop / ms / 1e9:.1f} TFLOP/s", file=sys.stderr, flush=True)
         del table, ws
+    cached_scoring(dev)
+
+
+def cached_scoring(dev):
+    """Candidates against a cached history (stderr, informational).  16 users with the mfalcon_bf16
+    history lengths U{1024..8192}, 1024 candidates each, H = 4 x 128, P = Tb = 128, bf16.  The same
+    request is scored (a) in one pass: hstu_attn_fwd with the candidate mask over history + candidates,
+    and (b) as 4 micro-batches of 256 candidates per user against the history's K, V and timestamps
+    (hstu_attn_fwd_cached, c_b of the one pass), and as one micro-batch of 1024.  Inputs resident; HIP
+    events on the kernels' stream."""
+    import torch
+    from hstu_sequential_transduction_attn_amd import inputs as I
+    from hstu_sequential_transduction_attn_amd import _lib as ops
+
+    def t(x):
+        if isinstance(x, I.Tensor):
+            return torch.from_numpy(np.ascontiguousarray(x.bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    users, m, mb = 16, 1024, 256
+    hist = [int(v) for v in I.rng_for(5, 0).integers(1024, 8193, size=users)]
+    full = I.attn_case("mfalcon_cached", 5, [h + m for h in hist], H=4, Dh=128, P=128, Tb=128, dtype="bf16",
+                       num_candidates=[m] * users, with_u=False)
+    cc = I.split_candidates(full)
+    j = full.jagged
+    offs, tau, ncand = t(j.seq_offsets.astype(np.int32)), t(j.timestamps.astype(np.int64)), t(j.num_candidates)
+    q, k, v = t(full.q), t(full.k), t(full.v)
+    wp, wt = t(full.rab.pos_bias), t(full.rab.time_bias)
+    h_offs, h_tau = t(cc.hist_offsets.astype(np.int32)), t(cc.hist_timestamps.astype(np.int64))
+    kh, vh = t(cc.k_hist), t(cc.v_hist)
+    scale = t((1.0 / cc.one_pass_lengths).astype(np.float32))
+    co = cc.cand_offsets.astype(np.int64)
+
+    def one_pass():
+        ops.attn_fwd(offs, tau, q, k, v, wp, wt, max_seq_len=j.max_seq_len, mask=ops.MASK_CAUSAL_CANDIDATES,
+                     num_candidates=ncand)
+
+    def micro_batches(mb):
+        batches = []
+        for s in range(m // mb):
+            idx = np.concatenate([np.arange(co[b] + s * mb, co[b] + (s + 1) * mb) for b in range(users)])
+            ti = torch.from_numpy(idx).to(dev)
+            batches.append(dict(offs=t(I.offsets_of([mb] * users)), tau=t(cc.cand_timestamps[idx]),
+                                q=t(cc.q)[ti].contiguous(), k=t(cc.k)[ti].contiguous(), v=t(cc.v)[ti].contiguous()))
+        b0 = batches[0]
+        nws = ops.attn_cached_workspace_bytes(h_offs, h_tau, b0["offs"], b0["tau"], 4, 128, wp, wt,
+                                              max_candidates=mb, max_history=max(hist))
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+
+        def run():
+            for bt in batches:
+                ops.attn_fwd_cached(h_offs, h_tau, kh, vh, bt["offs"], bt["tau"], bt["q"], bt["k"], bt["v"], wp, wt,
+                                    max_candidates=mb, max_history=max(hist), attn_scale=scale, workspace=ws)
+        return run
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 5
+
+    per_pair = 4 * 4 * 128
+    pairs_cached = sum(m * (h + 1) for h in hist)
+    t_one = timed(one_pass)
+    line = (f"[extended] mfalcon_cached: one pass (history + {m} candidates) {t_one:.3f} ms, "
+            f"{I.allowed_pairs(j) * per_pair / t_one / 1e9:.1f} TFLOP/s")
+    for mb in (256, 1024):
+        tc = timed(micro_batches(mb))
+        line += (f"; cached history, {m // mb} micro-batch(es) of {mb}: {tc:.3f} ms, "
+                 f"{pairs_cached * per_pair / tc / 1e9:.1f} TFLOP/s, {t_one / tc:.2f}x faster")
+    print(line, file=sys.stderr, flush=True)
 
 
 def main():

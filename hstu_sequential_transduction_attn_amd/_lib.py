@@ -79,7 +79,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_attn_fwd.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT), ctypes.c_int, c_vp, c_vp, c_vp,
                                   c_vp, ctypes.c_int, c_vp, c_sz, c_vp]
     lib.hstu_attn_cached_workspace_bytes.restype = c_sz
-    lib.hstu_attn_cached_workspace_bytes.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(JaggedT)]
+    lib.hstu_attn_cached_workspace_bytes.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(JaggedT),
+                                                     ctypes.POINTER(AttnDescT)]
     lib.hstu_attn_fwd_cached.restype = ctypes.c_int
     lib.hstu_attn_fwd_cached.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT),
                                          ctypes.c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_int, c_vp, c_sz,
@@ -151,8 +152,17 @@ def attn_fwd(seq_offsets, timestamps, q, k, v, pos_bias, time_bias, *, max_seq_l
     return out
 
 
+def attn_cached_workspace_bytes(hist_offsets, hist_timestamps, cand_offsets, cand_timestamps, num_heads: int,
+                                head_dim: int, pos_bias, time_bias, *, max_candidates: int, max_history: int) -> int:
+    lib = load_library()
+    hist = make_jagged(hist_offsets, hist_timestamps, max_history)
+    cand = make_jagged(cand_offsets, cand_timestamps, max_candidates)
+    desc = make_desc(num_heads, head_dim, pos_bias, time_bias)
+    return int(lib.hstu_attn_cached_workspace_bytes(ctypes.byref(hist), ctypes.byref(cand), ctypes.byref(desc)))
+
+
 def attn_fwd_cached(hist_offsets, hist_timestamps, k_hist, v_hist, cand_offsets, cand_timestamps, q, k, v,
-                    pos_bias, time_bias, *, max_candidates: int, attn_scale=None,
+                    pos_bias, time_bias, *, max_candidates: int, max_history: int, attn_scale=None,
                     out_dtype: Optional[torch.dtype] = None, out=None, workspace=None, stream=None):
     """O = hstu_attn_fwd_cached(...): candidates q, k, v [T_c, H, Dh] against the cached history
     k_hist, v_hist [T_h, H, Dh]; returns out [T_c, H, Dh]."""
@@ -160,10 +170,10 @@ def attn_fwd_cached(hist_offsets, hist_timestamps, k_hist, v_hist, cand_offsets,
     T, H, Dh = q.shape
     if out is None:
         out = torch.empty((T, H, Dh), dtype=out_dtype or q.dtype, device=q.device)
-    hist = make_jagged(hist_offsets, hist_timestamps, 0)
+    hist = make_jagged(hist_offsets, hist_timestamps, max_history)
     cand = make_jagged(cand_offsets, cand_timestamps, max_candidates, None, attn_scale)
     desc = make_desc(H, Dh, pos_bias, time_bias)
-    nws = int(lib.hstu_attn_cached_workspace_bytes(ctypes.byref(hist), ctypes.byref(cand)))
+    nws = int(lib.hstu_attn_cached_workspace_bytes(ctypes.byref(hist), ctypes.byref(cand), ctypes.byref(desc)))
     if workspace is None or workspace.numel() < nws:
         workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
     _check(lib.hstu_attn_fwd_cached(ctypes.byref(hist), ctypes.byref(cand), ctypes.byref(desc), _dtype_code(q),

@@ -92,6 +92,7 @@ hstu::AttnArgs attn_args(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc)
   a.num_heads = desc->num_heads;
   a.head_dim = desc->head_dim;
   a.max_seq_len = jag->max_seq_len;
+  a.num_rows_total = jag->total_tokens;
   a.num_pos_buckets = desc->num_pos_buckets;
   a.num_time_buckets = desc->num_time_buckets;
   a.rab_rows = desc->rab_rows;
@@ -192,12 +193,35 @@ hstu_status_t hstu_attn_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *de
   }
 }
 
-size_t hstu_attn_cached_workspace_bytes(const hstu_jagged_t *hist, const hstu_jagged_t *cand) {
-  if (!hist || !cand || hist->num_seqs < 0 || cand->num_seqs != hist->num_seqs) return 0;
-  if (cand->total_tokens <= 0) return 0;
+namespace {
+// Cached-scoring workspace: timestamp ranges of the candidates and of the history, then (with key
+// splits) the partial sums [kv_splits][T_c][H][Dh] fp32; each region 256-byte aligned.
+struct CachedWs {
+  size_t cand_stats, hist_stats, partial, total;
+  int splits;
+  int32_t tiles_per_split;
+};
+
+CachedWs cached_ws(const hstu_jagged_t *hist, const hstu_jagged_t *cand, const hstu_attn_desc_t *desc) {
+  CachedWs w{};
   const int64_t Th = hist->total_tokens > 0 ? hist->total_tokens : 0;
-  return round_up(hstu::attn_tau_stats_bytes(cand->total_tokens, cand->num_seqs), 256) +
-         round_up(hstu::attn_tau_stats_bytes(Th, hist->num_seqs), 256);
+  w.splits = hstu::attn_cached_splits(cand->num_seqs, desc->num_heads, cand->max_seq_len,
+                                      hist->max_seq_len > 0 ? hist->max_seq_len : 0, &w.tiles_per_split);
+  size_t off = 0;
+  w.cand_stats = off; off += round_up(hstu::attn_tau_stats_bytes(cand->total_tokens, cand->num_seqs), 256);
+  w.hist_stats = off; off += round_up(hstu::attn_tau_stats_bytes(Th, hist->num_seqs), 256);
+  w.partial = off;
+  if (w.splits > 1) off += round_up((size_t)w.splits * cand->total_tokens * desc->num_heads * desc->head_dim * 4, 256);
+  w.total = off;
+  return w;
+}
+}  // namespace
+
+size_t hstu_attn_cached_workspace_bytes(const hstu_jagged_t *hist, const hstu_jagged_t *cand,
+                                        const hstu_attn_desc_t *desc) {
+  if (!hist || !cand || !desc || hist->num_seqs < 0 || cand->num_seqs != hist->num_seqs) return 0;
+  if (cand->total_tokens <= 0 || desc->num_heads < 1 || desc->head_dim < 1) return 0;
+  return cached_ws(hist, cand, desc).total;
 }
 
 hstu_status_t hstu_attn_fwd_cached(const hstu_jagged_t *hist, const hstu_jagged_t *cand, const hstu_attn_desc_t *desc,
@@ -215,11 +239,17 @@ hstu_status_t hstu_attn_fwd_cached(const hstu_jagged_t *hist, const hstu_jagged_
       return fail(HSTU_ERR_INVALID_ARGUMENT, "hist->num_seqs = %d != cand->num_seqs = %d", hist->num_seqs,
                   cand->num_seqs);
     if (hist->total_tokens < 0) return fail(HSTU_ERR_INVALID_ARGUMENT, "hist->total_tokens = %d < 0", hist->total_tokens);
+    if (hist->max_seq_len < 0 || hist->max_seq_len > hist->total_tokens)
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "hist->max_seq_len = %d outside [0, hist->total_tokens = %d]",
+                  hist->max_seq_len, hist->total_tokens);
     if (!valid_dtype(in_dtype)) return fail(HSTU_ERR_INVALID_ARGUMENT, "in_dtype = %d invalid", (int)in_dtype);
     if (!valid_dtype(out_dtype)) return fail(HSTU_ERR_INVALID_ARGUMENT, "out_dtype = %d invalid", (int)out_dtype);
     if (in_dtype == HSTU_F32 && out_dtype != HSTU_F32)
       return fail(HSTU_ERR_UNSUPPORTED, "f32 inputs need an f32 output");
-    const size_t need = hstu_attn_cached_workspace_bytes(hist, cand);
+    const CachedWs cw = cached_ws(hist, cand, &d);
+    const size_t need = cand->total_tokens > 0 ? cw.total : 0;
+    const long long blocks = ((long long)cand->max_seq_len + 127) / 128 * d.num_heads * cand->num_seqs * cw.splits;
+    if (blocks > 0x7fffffffLL) return fail(HSTU_ERR_UNSUPPORTED, "launch too large (%lld workgroups)", blocks);
     if (workspace_bytes < need)
       return fail(HSTU_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
     const int64_t Tc = cand->total_tokens, Th = hist->total_tokens;
@@ -254,13 +284,17 @@ hstu_status_t hstu_attn_fwd_cached(const hstu_jagged_t *hist, const hstu_jagged_
     a.out_row_stride = a.row_stride;
     a.in_dtype = in_dtype == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
     a.out_dtype = out_dtype == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
-    a.tau_stats = (int64_t *)workspace;
+    a.tau_stats = (int64_t *)((char *)workspace + cw.cand_stats);
     a.k_hist = k_hist;
     a.v_hist = v_hist;
     a.hist_offsets = hist->seq_offsets;
     a.hist_timestamps = hist->timestamps;
-    a.hist_tau_stats =
-        (int64_t *)((char *)workspace + round_up(hstu::attn_tau_stats_bytes(Tc, cand->num_seqs), 256));
+    a.hist_tau_stats = (int64_t *)((char *)workspace + cw.hist_stats);
+    a.num_rows = (int32_t)Tc;
+    a.num_hist_rows = Th;
+    a.kv_splits = cw.splits;
+    a.tiles_per_split = cw.tiles_per_split;
+    a.partial = cw.splits > 1 ? (float *)((char *)workspace + cw.partial) : nullptr;
     return from_hip(hstu::launch_attn_cached(a, (hipStream_t)stream), "attn_fwd_cached launch");
   } catch (...) {
     return fail(HSTU_ERR_DEVICE, "unexpected C++ exception in hstu_attn_fwd_cached");

@@ -307,26 +307,70 @@ __device__ __forceinline__ void tile_body(OAcc<Layout<T, DH>::kDB> &oacc,
 }
 
 // Timestamp minimum and maximum of every 32-token chunk of every sequence.  Chunk c of sequence b is
-// stored at index (o_b >> 5) + b + c, which never collides across sequences (at most T/32 + B + 1
-// entries).  One workgroup per sequence.
+// stored at index first(b) + c with first(b) = (o_b >> 5) + b, which never collides across sequences
+// (first(b + 1) >= first(b) + ceil(n_b / 32)) and stays below T/32 + B + 1.  Flat over that index
+// space, one lane per token: lanes 32i..32i+31 of the grid own storage index i, find its sequence by a
+// binary search of first(b), load one timestamp each and reduce over the 32 lanes.
 __global__ void __launch_bounds__(256) tau_chunk_stats_kernel(const int32_t *__restrict__ offs,
                                                               const int64_t *__restrict__ tau,
-                                                              int64_t *__restrict__ stats) {
-  const int b = blockIdx.x;
-  const int o0 = offs[b], n = offs[b + 1] - o0;
-  const int nc = (n + kChunk - 1) / kChunk;
-  const int base = (o0 >> 5) + b;
-  for (int c = threadIdx.x; c < nc; c += blockDim.x) {
-    int64_t mn = INT64_MAX, mx = INT64_MIN;
-    const int e = imin(kChunk, n - kChunk * c);
-    for (int i = 0; i < e; ++i) {
-      const int64_t t = tau[o0 + kChunk * c + i];
-      mn = t < mn ? t : mn;
-      mx = t > mx ? t : mx;
+                                                              int64_t *__restrict__ stats, int num_seqs,
+                                                              int num_slots) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int slot = (int)(g >> 5), t = (int)(g & 31);
+  int64_t mn = INT64_MAX, mx = INT64_MIN;
+  bool owned = false;
+  if (slot < num_slots) {
+    int lo = 0, hi = num_seqs - 1;                 // last b with first(b) <= slot
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((offs[mid] >> 5) + mid <= slot) lo = mid; else hi = mid - 1;
     }
-    stats[2 * (int64_t)(base + c)] = mn;
-    stats[2 * (int64_t)(base + c) + 1] = mx;
+    const int o0 = offs[lo], n = offs[lo + 1] - o0;
+    const int c = slot - ((o0 >> 5) + lo);
+    owned = c < (n + kChunk - 1) / kChunk;         // false in the gaps between sequences
+    if (owned && kChunk * c + t < n) mn = mx = tau[o0 + kChunk * c + t];
   }
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) {
+    const int64_t a = __shfl_xor(mn, m, 32), b2 = __shfl_xor(mx, m, 32);
+    mn = a < mn ? a : mn;
+    mx = b2 > mx ? b2 : mx;
+  }
+  if (owned && t == 0) {
+    stats[2 * (int64_t)slot] = mn;
+    stats[2 * (int64_t)slot + 1] = mx;
+  }
+}
+
+// Sum of the key splits of cached scoring, in split order (deterministic), times c_b * (-ln 2) (the
+// folded SiLU's factor).  One thread per 4 consecutive output values of one candidate row; the user of
+// the row comes from a binary search of the candidate offsets.
+template <typename TO>
+__global__ void __launch_bounds__(256) attn_split_reduce_kernel(const AttnArgs p, int row_vals) {
+  const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = i4 * 4 / row_vals;
+  if (row >= p.num_rows) return;
+  const int col = (int)(i4 * 4 - row * row_vals);
+  int lo = 0, hi = p.num_seqs - 1;                 // last b with seq_offsets[b] <= row
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.seq_offsets[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  const int nh = p.hist_offsets[b + 1] - p.hist_offsets[b];
+  const int nq = p.seq_offsets[b + 1] - p.seq_offsets[b];
+  const int tiles = (nh + kBN - 1) / kBN;
+  const int used = imin(p.kv_splits, imax(1, (tiles + p.tiles_per_split - 1) / p.tiles_per_split));
+  const float cb = p.attn_scale ? p.attn_scale[b] : 1.0f / (float)(nh + nq);
+  const float scale = cb * kNegLn2;
+  floatx4 acc = floatx4{};
+  for (int sp = 0; sp < used; ++sp) {
+    const floatx4 v = *(const floatx4 *)(p.partial + ((int64_t)sp * p.num_rows + row) * row_vals + col);
+    acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
+  }
+  TO *o = (TO *)p.out + row * p.out_row_stride + col;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = from_f32<TO>(acc[e] * scale);
 }
 
 // Two waves per SIMD (<= 256 registers per lane) so that one wave's MFMAs overlap the other's VALU work.
@@ -336,7 +380,10 @@ __global__ void __launch_bounds__(256) tau_chunk_stats_kernel(const int32_t *__r
 // hist_offsets, hist_timestamps), every one of them allowed, and each candidate also sees itself,
 // which the epilogue adds as one extra score per row.  A candidate has position n_h and local index
 // n_h + c in the virtual sequence [history | candidates], so the tile classes, buckets and masks are
-// those of the candidate rows of the one-pass candidate mask.
+// those of the candidate rows of the one-pass candidate mask.  A user's history tiles may be split over
+// kv_splits workgroups (tiles_per_split each, the last one taking the rest): with no softmax the partial
+// sums over key ranges simply add, so each split stores its raw sums in `partial` and a reduction kernel
+// adds them in split order.
 template <typename T, int DH, typename TO, bool CACHED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
@@ -346,9 +393,10 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   HSTU_LDS char *smem = (HSTU_LDS char *)smem_raw;
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
-  // ---- work item: query block major (longest first), then (sequence, head)
+  // ---- work item: query block major (longest first), then (sequence, head); cached: key split fastest
   const int HB = p.num_heads * p.num_seqs;
-  const int item = blockIdx.x;
+  const int split = CACHED ? (int)(blockIdx.x % (unsigned)p.kv_splits) : 0;
+  const int item = CACHED ? (int)(blockIdx.x / (unsigned)p.kv_splits) : (int)blockIdx.x;
   const int qblk = n_qblocks - 1 - item / HB;
   const int b = (item % HB) / p.num_heads;
   const int h = (item % HB) % p.num_heads;
@@ -424,8 +472,15 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
     r2_begin = imax(imax(q0, nh) / kBN, r1_end);
     r2_end = blast / kBN + 1;
   }
-  const int ntiles = r1_end + imax(r2_end - r2_begin, 0);
-  auto tile_of = [&](int i) -> int { return i < r1_end ? i : r2_begin + (i - r1_end); };
+  int ntiles = r1_end + imax(r2_end - r2_begin, 0);
+  int t_first = 0;                                // cached: first history tile of this key split
+  if constexpr (CACHED) {
+    t_first = split * p.tiles_per_split;
+    const int t_end = split == p.kv_splits - 1 ? r1_end : imin(r1_end, t_first + p.tiles_per_split);
+    if (split > 0 && t_first >= t_end) return;    // an empty split (split 0 always runs: the self term)
+    ntiles = imax(t_end - t_first, 0);
+  }
+  auto tile_of = [&](int i) -> int { return i < r1_end ? t_first + i : r2_begin + (i - r1_end); };
 
   // ---- direct-to-LDS staging.  Per tile, wave w loads rows 16w..16w+15 of each 64-byte column group g
   // of K and of V (1 KB each: lane l takes row 16w + l/4 and 16-byte piece l%4 of the group; in K, the
@@ -563,7 +618,7 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
 
   // ---- epilogue: O^T element e of dh block db is dh = 32*db + 8*(e/4) + 4*half + e%4; the sums carry
   // the factor -log2(e) of the folded SiLU, removed here together with c_b
-  if constexpr (CACHED) {
+  if (CACHED && split == 0) {
     // the candidate's score against itself: both distances are 0, so the bias is w_p[0] + w_t[0]
     const int64_t crow = (int64_t)(o0 + (my_valid ? my_row : 0));
     const T *krow = (const T *)p.k + crow * p.row_stride + h * DH;
@@ -590,6 +645,22 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
 #pragma unroll
         for (int x = 0; x < 4; ++x) oacc.d[db][4 * e4 + x] = fmaf(a, to_f32(vrow[dh + x]), oacc.d[db][4 * e4 + x]);
       }
+  }
+  if (CACHED && p.kv_splits > 1) {
+    // raw sums of this key split; attn_split_reduce_kernel adds the splits and applies the scale
+    if (my_valid) {
+      float *prow = p.partial + (((int64_t)split * p.num_rows + o0 + my_row) * p.num_heads + h) * DH;
+#pragma unroll
+      for (int db = 0; db < L::kDB; ++db)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          floatx4 w;
+          w[0] = oacc.d[db][4 * e4 + 0]; w[1] = oacc.d[db][4 * e4 + 1];
+          w[2] = oacc.d[db][4 * e4 + 2]; w[3] = oacc.d[db][4 * e4 + 3];
+          *(floatx4 *)(prow + 32 * db + 8 * e4 + 4 * half) = w;
+        }
+    }
+    return;
   }
   const float scale = cb * kNegLn2;
   if (p.row_stats) {
@@ -641,11 +712,19 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   }
 }
 
+void launch_tau_stats(const int32_t *offs, const int64_t *tau, int64_t *stats, int num_seqs, int64_t total_tokens,
+                      hipStream_t stream) {
+  if (num_seqs <= 0) return;
+  const int64_t slots = (total_tokens >> 5) + num_seqs + 1;
+  hipLaunchKernelGGL(tau_chunk_stats_kernel, dim3((unsigned)((slots * 32 + 255) / 256)), dim3(256), 0, stream, offs,
+                     tau, stats, num_seqs, (int)slots);
+}
+
 template <typename T, int DH, typename TO, bool CACHED>
 hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
   using L = Layout<T, DH>;
   const int n_qblocks = (a.max_seq_len + kBM - 1) / kBM;
-  const long long grid = (long long)n_qblocks * a.num_heads * a.num_seqs;
+  const long long grid = (long long)n_qblocks * a.num_heads * a.num_seqs * (CACHED ? a.kv_splits : 1);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const size_t lds = (size_t)L::kStages * L::kStageBytes + (size_t)(a.num_pos_buckets + kTimeTab) * sizeof(float);
@@ -656,13 +735,16 @@ hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(tau_chunk_stats_kernel, dim3(a.num_seqs), dim3(256), 0, stream, a.seq_offsets, a.timestamps,
-                     a.tau_stats);
+  launch_tau_stats(a.seq_offsets, a.timestamps, a.tau_stats, a.num_seqs, a.num_rows_total, stream);
   if constexpr (CACHED)
-    hipLaunchKernelGGL(tau_chunk_stats_kernel, dim3(a.num_seqs), dim3(256), 0, stream, a.hist_offsets,
-                       a.hist_timestamps, a.hist_tau_stats);
+    launch_tau_stats(a.hist_offsets, a.hist_timestamps, a.hist_tau_stats, a.num_seqs, a.num_hist_rows, stream);
   hipLaunchKernelGGL((attn_fwd_kernel<T, DH, TO, CACHED>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a,
                      n_qblocks);
+  if (CACHED && a.kv_splits > 1) {
+    const long long n4 = (long long)a.num_rows * a.num_heads * DH / 4;
+    hipLaunchKernelGGL(attn_split_reduce_kernel<TO>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, a,
+                       a.num_heads * DH);
+  }
   return hipGetLastError();
 }
 
@@ -677,6 +759,26 @@ hipError_t launch_dh(const AttnArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int attn_cached_splits(int64_t num_seqs, int64_t num_heads, int64_t max_candidates, int64_t max_history,
+                       int32_t *tiles_per_split) {
+  // about 1024 workgroups (two resident per CU, two rounds), at least 8 tiles per split so that the
+  // partial sums (written once, read once) stay small against the tile work
+  constexpr int64_t kTarget = 1024, kMinTiles = 8;
+  const int64_t base = (max_candidates + kBM - 1) / kBM * num_heads * num_seqs;
+  const int64_t tiles = (max_history + kBN - 1) / kBN;
+  int64_t splits = 1;
+  if (base > 0 && tiles >= 2 * kMinTiles) {
+    splits = (kTarget + base - 1) / base;
+    const int64_t cap = tiles / kMinTiles;
+    splits = splits < cap ? splits : cap;
+    splits = splits < 1 ? 1 : splits;
+  }
+  int64_t tps = splits > 1 ? (tiles + splits - 1) / splits : (tiles > 1 ? tiles : 1);
+  if (splits > 1) splits = (tiles + tps - 1) / tps;   // no trailing empty split
+  *tiles_per_split = (int32_t)tps;
+  return (int)splits;
+}
 
 size_t attn_tau_stats_bytes(int64_t total_tokens, int64_t num_seqs) {
   return (size_t)((total_tokens >> 5) + num_seqs + 1) * 2 * sizeof(int64_t);

@@ -24,6 +24,7 @@ struct AttnArgs {
   const float *pos_bias;          // [R][P]
   const float *time_bias;         // [R][Tb]
   int32_t num_seqs, num_heads, head_dim, max_seq_len;
+  int64_t num_rows_total;         // T (rows of q, k, v, timestamps)
   int32_t num_pos_buckets, num_time_buckets, rab_rows;
   int32_t mask;
   int32_t in_dtype, out_dtype;
@@ -37,7 +38,17 @@ struct AttnArgs {
   const int32_t *hist_offsets;     // [B+1]
   const int64_t *hist_timestamps;  // [T_h]
   int64_t *hist_tau_stats;         // workspace: attn_tau_stats_bytes(T_h, B)
+  int32_t num_rows;                // T_c (candidate rows)
+  int64_t num_hist_rows;           // T_h
+  int32_t kv_splits;               // workgroups per (candidate block, user, head) along the history, >= 1
+  int32_t tiles_per_split;         // 64-key history tiles per split (the last split takes the rest)
+  float *partial;                  // kv_splits > 1: workspace [kv_splits][T_c][H][Dh] fp32 raw sums
 };
+
+// Key splits of cached scoring for a batch: enough workgroups to fill the chip, each split a whole
+// number of 64-key tiles.  Returns kv_splits (>= 1) and sets tiles_per_split.
+int attn_cached_splits(int64_t num_seqs, int64_t num_heads, int64_t max_candidates, int64_t max_history,
+                       int32_t *tiles_per_split);
 
 // Workspace bytes of the per-32-token timestamp ranges the attention kernel classifies tiles with.
 size_t attn_tau_stats_bytes(int64_t total_tokens, int64_t num_seqs);

@@ -132,9 +132,11 @@ hstu_status_t hstu_attn_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *de
 
 /*
  * Workspace needed by hstu_attn_fwd_cached (bytes; 0 is possible): the per-32-token timestamp ranges
- * of the candidate rows and of the history rows.  Depends only on the host fields of hist and cand.
+ * of the candidate rows and of the history rows and, when a user's history is split over several
+ * workgroups, their fp32 partial sums.  Depends only on the host fields of hist, cand and desc.
  */
-size_t hstu_attn_cached_workspace_bytes(const hstu_jagged_t *hist, const hstu_jagged_t *cand);
+size_t hstu_attn_cached_workspace_bytes(const hstu_jagged_t *hist, const hstu_jagged_t *cand,
+                                        const hstu_attn_desc_t *desc);
 
 /*
  * Candidates scored against a cached history: mini-batched candidate scoring ("Actions Speak Louder
@@ -148,8 +150,9 @@ size_t hstu_attn_cached_workspace_bytes(const hstu_jagged_t *hist, const hstu_ja
  * With all of a user's candidates in one call (or with attn_scale carrying that c_b) this equals the
  * candidate rows of hstu_attn_fwd with HSTU_MASK_CAUSAL_CANDIDATES over [history | candidates], so the
  * history's keys and values, computed once, serve any number of candidate micro-batches.
- * hist: num_seqs = B, total_tokens = T_h, seq_offsets [B+1], timestamps [T_h] (device); max_seq_len,
- *       num_candidates and attn_scale are not read.
+ * hist: num_seqs = B, total_tokens = T_h, max_seq_len = the longest history (host; it only sets how
+ *       finely histories are split over workgroups, any value in [0, T_h] gives the same result),
+ *       seq_offsets [B+1], timestamps [T_h] (device); num_candidates and attn_scale are not read.
  * cand: num_seqs = B (the same users, in the same order), total_tokens = T_c, max_seq_len = the most
  *       candidates of one user, seq_offsets [B+1], timestamps [T_c], attn_scale [B] or NULL (device);
  *       num_candidates is not read.
@@ -157,8 +160,9 @@ size_t hstu_attn_cached_workspace_bytes(const hstu_jagged_t *hist, const hstu_ja
  * k_hist, v_hist: [T_h][H][Dh]; q, k, v (the candidates' own rows): [T_c][H][Dh]; all in_dtype,
  * row-major, 16-byte aligned (device).  out: [T_c][H][Dh], out_dtype = HSTU_F32 or in_dtype; may not
  * overlap an input or the workspace.  Caller-owned; nothing is allocated or retained.
- * Errors: as for hstu_attn_fwd; hist->num_seqs != cand->num_seqs, or a NULL pointer that the sizes
- * require, is HSTU_ERR_INVALID_ARGUMENT.
+ * The partial sums of a split history are added in a fixed order: the result is bitwise deterministic.
+ * Errors: as for hstu_attn_fwd; hist->num_seqs != cand->num_seqs, hist->max_seq_len outside [0, T_h],
+ * or a NULL pointer that the sizes require, is HSTU_ERR_INVALID_ARGUMENT.
  */
 hstu_status_t hstu_attn_fwd_cached(const hstu_jagged_t *hist, const hstu_jagged_t *cand, const hstu_attn_desc_t *desc,
                                    hstu_dtype_t in_dtype, const void *k_hist, const void *v_hist, const void *q,

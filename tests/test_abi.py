@@ -187,10 +187,18 @@ def test_cached_zero_candidates_is_a_no_op():
     assert _cached(hist, cand, _desc(), ws=None, nws=0)[0] == OK
 
 
-def test_cached_workspace_covers_both_timestamp_ranges():
+def test_cached_workspace_covers_timestamp_ranges_and_partial_sums():
     lib = _lib()
+    desc = _desc(H=4, Dh=128)
+    cws = lambda h, c: lib.hstu_attn_cached_workspace_bytes(ctypes.byref(h), ctypes.byref(c), ctypes.byref(desc))
     hist, cand = _jag(B=4, T=1000, max_len=300), _jag(B=4, T=64, max_len=40)
-    n = lib.hstu_attn_cached_workspace_bytes(ctypes.byref(hist), ctypes.byref(cand))
-    one = lib.hstu_attn_workspace_bytes(ctypes.byref(cand), ctypes.byref(_desc()), L.HSTU_BF16)
+    n = cws(hist, cand)
+    one = lib.hstu_attn_workspace_bytes(ctypes.byref(cand), ctypes.byref(desc), L.HSTU_BF16)
     assert n > one and n % 256 == 0
-    assert lib.hstu_attn_cached_workspace_bytes(ctypes.byref(_jag(B=3)), ctypes.byref(cand)) == 0
+    assert n < 64 * 4 * 128 * 4          # short histories: no key split, no partial sums
+    # long histories, few candidates: split histories, room for at least two fp32 partial outputs
+    long_hist = _jag(B=4, T=40000, max_len=10000)
+    assert cws(long_hist, cand) >= n + 2 * 64 * 4 * 128 * 4
+    assert cws(_jag(B=3), cand) == 0
+    st, msg = _cached(_jag(B=2, T=500, max_len=501), _jag(B=2, T=64, max_len=40), _desc())
+    assert st == INVALID and "max_seq_len" in msg

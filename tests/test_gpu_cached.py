@@ -43,12 +43,16 @@ def _oracle(cc, attn_scale=None):
                          cc.rab.pos_bias, cc.rab.time_bias, attn_scale)
 
 
-def _gpu(cc, attn_scale=None, out_dtype=None):
+def _gpu(cc, attn_scale=None, out_dtype=None, max_history=None):
     from hstu_sequential_transduction_attn_amd import _lib as ops
+    if max_history is None:
+        d = np.diff(cc.hist_offsets.astype(np.int64))
+        max_history = int(d.max()) if len(d) else 0
     return ops.attn_fwd_cached(dev(cc.hist_offsets.astype(np.int32)), dev(cc.hist_timestamps.astype(np.int64)),
                                dev(cc.k_hist), dev(cc.v_hist), dev(cc.cand_offsets.astype(np.int32)),
                                dev(cc.cand_timestamps.astype(np.int64)), dev(cc.q), dev(cc.k), dev(cc.v),
                                dev(cc.rab.pos_bias), dev(cc.rab.time_bias), max_candidates=cc.max_candidates,
+                               max_history=max_history,
                                attn_scale=None if attn_scale is None else dev(np.asarray(attn_scale, np.float32)),
                                out_dtype=out_dtype)
 
@@ -132,3 +136,18 @@ def test_mfalcon_size_micro_batch_sampled_users():
         rows = np.arange(so[b], so[b + 1])
         want = _oracle(one, attn_scale=scale)
         assert_close(got[rows], want, "bf16", f"user {b}")
+
+
+@pytest.mark.parametrize("max_history", [None, 0, 1500, 100000])
+def test_history_split_over_workgroups(max_history):
+    """Few candidates and long histories: the history is split over several workgroups whose partial
+    sums are reduced in order.  max_history only sets the split; any value gives the same result
+    (an underestimate leaves the rest to the last split; 100000 > T_h is clamped to T_h by the caller)."""
+    print(f"\n[case] cached key splits max_history={max_history}", flush=True)
+    _, cc = _case(1060, [4000, 2500, 37, 0, 3100], [3, 70, 5, 2, 129], H=2, Dh=128, P=200, Tb=40)
+    T_h = int(cc.hist_offsets[-1])
+    mh = None if max_history is None else min(max_history, T_h)
+    got = host(_gpu(cc, out_dtype=torch.float32, max_history=mh))
+    assert_close(got, _oracle(cc), "bf16", f"key splits {max_history}", magnitude_aware=True)
+    again = host(_gpu(cc, out_dtype=torch.float32, max_history=mh))
+    assert np.array_equal(got, again), "not deterministic"
