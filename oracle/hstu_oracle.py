@@ -182,6 +182,57 @@ def attn_fwd(jag: dict, q, k, v, pos_bias, time_bias, row_sample=None):
     return out
 
 
+# --------------------------------------------------------------------------- attention backward
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d SiLU / dz = sigma(z) (1 + z (1 - sigma(z))), float64 (the derivative of z * sigma(z))."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-z))
+    return sig * (1.0 + z * (1.0 - sig))
+
+
+def attn_bwd(jag: dict, q, k, v, pos_bias, time_bias, d_out):
+    """Gradients of the pointwise attention (the forward of attn_fwd) for an upstream gradient d_out.
+
+    Returns (dq, dk, dv, d_pos_bias, d_time_bias) in float64: [T, H, Dh] x 3, [R, P], [R, Tb].
+    With a_ij = SiLU(s_ij) on allowed pairs and O_i = c_b sum_j a_ij v_j:
+        dv_j = c_b sum_i a_ij dO_i,   dA_ij = c_b dO_i . v_j,   dS_ij = dA_ij SiLU'(s_ij) (allowed pairs),
+        dq_i = sum_j dS_ij k_j,   dk_j = sum_i dS_ij q_i,
+        d w_p[r][p] = sum of dS_ij over the pairs with bp(i, j) = p (heads of table row r, all sequences),
+        d w_t[r][t] likewise with bt(i, j) = t.
+    c_b is a constant (no gradient).  No softmax, hence no normaliser term.
+    """
+    q, k, v, g = (np.asarray(a, np.float64) for a in (q, k, v, d_out))
+    wp = np.asarray(pos_bias, np.float64)
+    wt = np.asarray(time_bias, np.float64)
+    tau = np.asarray(jag["timestamps"], np.int64)
+    T, H, Dh = q.shape
+    R, P, Tb = wp.shape[0], wp.shape[1], wt.shape[1]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dwp, dwt = np.zeros_like(wp), np.zeros_like(wt)
+    B = len(jag["seq_offsets"]) - 1
+    for b in range(B):
+        o0, o1, n, n_hist, mask, scale = _seq_params(jag, b)
+        if n == 0:
+            continue
+        pos = positions(n, n_hist, mask)
+        bp = position_bucket(pos[:, None], pos[None, :], P)
+        bt = time_bucket(tau[o0:o1][:, None], tau[o0:o1][None, :], Tb)
+        ok = allowed(np.arange(n), n, n_hist, mask)
+        for h in range(H):
+            r = 0 if R == 1 else h
+            qh, kh, vh, gh = q[o0:o1, h], k[o0:o1, h], v[o0:o1, h], g[o0:o1, h]
+            s = qh @ kh.T + wp[r][bp] + wt[r][bt]
+            a = np.where(ok, silu(s), 0.0)
+            dv[o0:o1, h] = scale * (a.T @ gh)
+            ds = np.where(ok, scale * (gh @ vh.T) * silu_grad(s), 0.0)
+            dq[o0:o1, h] = ds @ kh
+            dk[o0:o1, h] = ds.T @ qh
+            dwp[r] += np.bincount(bp[ok], weights=ds[ok], minlength=P)
+            dwt[r] += np.bincount(bt[ok], weights=ds[ok], minlength=Tb)
+    return dq, dk, dv, dwp, dwt
+
+
 # --------------------------------------------------------------------------- cached-history scoring
 def attn_cached(hist: dict, cand: dict, k_hist, v_hist, q, k, v, pos_bias, time_bias, attn_scale=None):
     """Candidates scored against a cached user history: O [T_c, H, Dh] in float64.
