@@ -85,6 +85,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_attn_fwd_cached.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT),
                                          ctypes.c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_int, c_vp, c_sz,
                                          c_vp]
+    lib.hstu_attn_bwd_workspace_bytes.restype = c_sz
+    lib.hstu_attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT), ctypes.c_int]
+    lib.hstu_attn_bwd.restype = ctypes.c_int
+    lib.hstu_attn_bwd.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT), ctypes.c_int, c_vp, c_vp, c_vp,
+                                  c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
     lib.hstu_layer_workspace_bytes.restype = c_sz
     lib.hstu_layer_workspace_bytes.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT),
                                                ctypes.POINTER(LayerWeightsT), ctypes.c_int]
@@ -150,6 +155,27 @@ def attn_fwd(seq_offsets, timestamps, q, k, v, pos_bias, time_bias, *, max_seq_l
     _check(lib.hstu_attn_fwd(ctypes.byref(jag), ctypes.byref(desc), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                              _dtype_code(out), _ptr(ws), nws, _stream(stream)))
     return out
+
+
+def attn_bwd(seq_offsets, timestamps, q, k, v, d_out, pos_bias, time_bias, *, max_seq_len: int,
+             mask: int = MASK_CAUSAL, num_candidates=None, attn_scale=None, workspace=None, stream=None):
+    """(dq, dk, dv, d_pos_bias, d_time_bias) = hstu_attn_bwd(...): gradients of attn_fwd's output for
+    the upstream gradient d_out [T, H, Dh] (q's dtype); all returned in fp32."""
+    lib = load_library()
+    T, H, Dh = q.shape
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq, dk, dv = (torch.empty((T, H, Dh), **f32) for _ in range(3))
+    d_pos, d_time = torch.empty(pos_bias.shape, **f32), torch.empty(time_bias.shape, **f32)
+    jag = make_jagged(seq_offsets, timestamps, max_seq_len, num_candidates, attn_scale)
+    desc = make_desc(H, Dh, pos_bias, time_bias, mask)
+    dt = _dtype_code(q)
+    nws = int(lib.hstu_attn_bwd_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), dt))
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.hstu_attn_bwd(ctypes.byref(jag), ctypes.byref(desc), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(d_out),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(d_pos), _ptr(d_time), _ptr(workspace),
+                             workspace.numel(), _stream(stream)))
+    return dq, dk, dv, d_pos, d_time
 
 
 def attn_cached_workspace_bytes(hist_offsets, hist_timestamps, cand_offsets, cand_timestamps, num_heads: int,

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -298,6 +299,87 @@ hstu_status_t hstu_attn_fwd_cached(const hstu_jagged_t *hist, const hstu_jagged_
     return from_hip(hstu::launch_attn_cached(a, (hipStream_t)stream), "attn_fwd_cached launch");
   } catch (...) {
     return fail(HSTU_ERR_DEVICE, "unexpected C++ exception in hstu_attn_fwd_cached");
+  }
+}
+
+size_t hstu_attn_bwd_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, hstu_dtype_t in_dtype) {
+  (void)in_dtype;
+  if (!jag || !desc || jag->total_tokens <= 0 || jag->num_seqs < 0 || desc->num_heads < 1 ||
+      desc->num_pos_buckets < 1)
+    return 0;
+  return round_up(hstu::attn_tau_stats_bytes(jag->total_tokens, jag->num_seqs), 256) +
+         round_up((size_t)hstu::attn_bwd_partial_floats(jag->num_seqs, desc->num_heads, jag->max_seq_len,
+                                                        desc->num_pos_buckets) * 4, 256);
+}
+
+hstu_status_t hstu_attn_bwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, hstu_dtype_t in_dtype,
+                            const void *q, const void *k, const void *v, const void *d_out, float *dq, float *dk,
+                            float *dv, float *d_pos_bias, float *d_time_bias, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  try {
+    hstu_status_t st = check_jagged_desc(jag, desc);
+    if (st != HSTU_OK) return st;
+    if (!valid_dtype(in_dtype)) return fail(HSTU_ERR_INVALID_ARGUMENT, "in_dtype = %d invalid", (int)in_dtype);
+    if (!d_pos_bias || !d_time_bias) return fail(HSTU_ERR_INVALID_ARGUMENT, "d_pos_bias/d_time_bias is NULL");
+    const int ityp = in_dtype == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
+    const size_t lds = std::max(hstu::attn_bwd_dq_lds_bytes(ityp, desc->head_dim, desc->num_pos_buckets),
+                                hstu::attn_bwd_dkdv_lds_bytes(ityp, desc->head_dim, desc->num_pos_buckets));
+    if (lds > 160 * 1024)
+      return fail(HSTU_ERR_UNSUPPORTED, "num_pos_buckets = %d needs %zu bytes of LDS in the backward (160 KB max)",
+                  desc->num_pos_buckets, lds);
+    const size_t need = hstu_attn_bwd_workspace_bytes(jag, desc, in_dtype);
+    if (workspace_bytes < need)
+      return fail(HSTU_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+    const int64_t T = jag->total_tokens;
+    const size_t R = desc->rab_rows, P = desc->num_pos_buckets, Tb = desc->num_time_buckets;
+    if (overlaps(d_pos_bias, R * P * 4, d_time_bias, R * Tb * 4))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "d_pos_bias overlaps d_time_bias");
+    if (T > 0) {
+      if (!workspace) return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace is NULL");
+      if (!aligned16(workspace)) return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+      if (!q || !k || !v || !d_out || !dq || !dk || !dv)
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "q/k/v/d_out/dq/dk/dv is NULL");
+      if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_out) || !aligned16(dq) || !aligned16(dk) ||
+          !aligned16(dv))
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "q/k/v/d_out/dq/dk/dv must be 16-byte aligned");
+      const size_t nin = (size_t)T * desc->num_heads * desc->head_dim * esize(in_dtype);
+      const size_t ng = (size_t)T * desc->num_heads * desc->head_dim * 4;
+      const void *ins[4] = {q, k, v, d_out};
+      const void *outs[6] = {dq, dk, dv, d_pos_bias, d_time_bias, workspace};
+      const size_t out_n[6] = {ng, ng, ng, R * P * 4, R * Tb * 4, need};
+      for (int o = 0; o < 6; ++o) {
+        for (int i = 0; i < 4; ++i)
+          if (overlaps(outs[o], out_n[o], ins[i], nin))
+            return fail(HSTU_ERR_INVALID_ARGUMENT, "an output or the workspace overlaps an input");
+        for (int o2 = o + 1; o2 < 6; ++o2)
+          if (overlaps(outs[o], out_n[o], outs[o2], out_n[o2]))
+            return fail(HSTU_ERR_INVALID_ARGUMENT, "two outputs (or an output and the workspace) overlap");
+      }
+    }
+    hstu::AttnArgs a = attn_args(jag, desc);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.d_out = d_out;
+    a.out = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.d_pos_bias = d_pos_bias;
+    a.d_time_bias = d_time_bias;
+    a.row_stride = (int64_t)desc->num_heads * desc->head_dim;
+    a.out_row_stride = a.row_stride;
+    a.in_dtype = ityp;
+    a.out_dtype = hstu::kF32;
+    a.tau_stats = (int64_t *)workspace;
+    a.partial = T > 0 ? (float *)((char *)workspace +
+                                  round_up(hstu::attn_tau_stats_bytes(T, jag->num_seqs), 256))
+                      : nullptr;
+    hipError_t e = hstu::launch_attn_bwd_dq(a, (hipStream_t)stream);
+    if (e != hipSuccess) return from_hip(e, "attn_bwd dq launch");
+    if (T == 0) return ok();
+    return from_hip(hstu::launch_attn_bwd_dkdv(a, (hipStream_t)stream), "attn_bwd dk/dv launch");
+  } catch (...) {
+    return fail(HSTU_ERR_DEVICE, "unexpected C++ exception in hstu_attn_bwd");
   }
 }
 

@@ -51,226 +51,12 @@
 // All classes share one tile body: the MFMA code and the SiLU are common, and the classes other than
 // uniform add their per-score bias (and the mask) to the score accumulators in place, in a branch of
 // their own, so that the output accumulators never change registers between classes.
-#include "device_common.hpp"
-#include "kernels.h"
+#include "attn_common.hpp"
 
 namespace hstu {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kQW = 32;                  // queries per wave
-constexpr int kBM = kWaves * kQW;        // queries per workgroup
-constexpr int kBN = 64;                  // keys per LDS tile
-constexpr int kThreads = kWaves * kWave;
-constexpr int kTimeTab = 65;             // a 64-bit gap has bit length 0..64
-constexpr int kChunk = 32;               // tokens per timestamp-range chunk
-constexpr int kRingBudget = 68 * 1024;   // LDS for the stage ring: two workgroups per CU
-constexpr float kNegLog2e = -1.4426950408889634f;
-constexpr float kNegLn2 = -0.6931471805599453f;
-static_assert(kWaves * 16 == kBN, "each wave stages 16 rows of a tile");
-
-// Tile classes.  A class code is body | (low time bucket << 8).
-enum Body : int { kNone = 0, kUniform = 1, kTwo = 2, kGen32 = 3, kGen64 = 4, kGen32M = 5, kGen64M = 6 };
-
-// Row order of K inside each 32-row block of LDS: row r holds key kperm(r) (an involution swapping
-// rows 4..7 with 8..11 and 20..23 with 24..27, i.e. bits 2 and 3 of r).  With it, accumulator element e of lane half hf holds
-// key 16*(e/8) + 8*hf + e%8.
-__device__ __forceinline__ int kperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
-
-template <typename T, int DH>
-struct Layout {
-  static constexpr bool kBf16 = sizeof(T) == 2;
-  static constexpr int kES = sizeof(T);
-  static constexpr int kRB = DH * kES;                 // bytes of one K or V row
-  static constexpr int kG = kRB / 64;                  // 64-byte column groups per row
-  static constexpr int kTileBytes = kBN * kRB;
-  static constexpr int kOffK = 0;
-  static constexpr int kOffV = kTileBytes;
-  static constexpr int kOffTau = 2 * kTileBytes;       // wave w's 16 timestamps at 256*w (+128 B unused)
-  static constexpr int kStageBytes = 2 * kTileBytes + kWaves * 256;
-  static constexpr int kFit = kRingBudget / kStageBytes;
-  static constexpr int kStages = kFit >= 4 ? 4 : (kFit >= 2 ? kFit : 2);   // at least double-buffered
-  static constexpr int kLoadsPerTile = 2 * kG + 1;     // per wave: K and V column groups, timestamps
-  static constexpr int kKPL = kBf16 ? 8 : 1;           // operand values per lane per MFMA
-  static constexpr int kKStep = kBf16 ? 16 : 2;        // k per MFMA
-  static constexpr int kQSteps = DH / kKStep;          // MFMAs per 32x32 score block
-  static constexpr int kDB = DH / 32;                  // 32-row dh blocks of O^T
-  static_assert(kStages >= 2, "ring");
-  static_assert(kRB % 64 == 0, "rows of whole 64-byte groups");
-  static_assert(kStageBytes % 16 == 0, "stage alignment");
-  // LDS byte offset of byte b of row r in a V tile, and in a K tile (16-byte pieces XOR-permuted)
-  __device__ static int v_at(int r, int b) { return (((b >> 6) * 64 + r) << 6) + (b & 63); }
-  __device__ static int k_at(int r, int b) {
-    return (((b >> 6) * 64 + r) << 6) + ((((b >> 4) & 3) ^ ((r >> 2) & 3)) << 4) + (b & 15);
-  }
-  // LDS byte offset (from the stage) of the timestamp of tile-local key j
-  __device__ static int tau_at(int j) { return kOffTau + 256 * (j >> 4) + 8 * (j & 15); }
-};
-
-// The O^T accumulators of one wave: N blocks of 32 dh rows x 32 queries.
-template <int N>
-struct OAcc {
-  floatx16 d[N];
-};
-
-template <typename T> struct QFrag;
-template <> struct QFrag<__bf16> { using type = bf16x8; };
-template <> struct QFrag<float> { using type = float; };
-
-__device__ __forceinline__ int bitlen_u32(uint32_t d) { return 32 - __clz((int)d); }  // __clz(0) = 32
-
-// Column groups G..NG-1 of one row group of K and V: LDS group g sits at m + 4096*g; the immediate 64*g
-// selects the source column group and is taken back out of M0.
-template <int G, int NG>
-__device__ __forceinline__ void dma_groups(const char *kb, const char *vb, uint32_t koff, uint32_t voff, uint32_t mk,
-                                           uint32_t mv) {
-  if constexpr (G < NG) {
-    dma16<64 * G>(kb, koff, mk + (uint32_t)G * (4096u - 64u));
-    dma16<64 * G>(vb, voff, mv + (uint32_t)G * (4096u - 64u));
-    dma_groups<G + 1, NG>(kb, vb, koff, voff, mk, mv);
-  }
-}
-__device__ __forceinline__ int readlane_i(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
-__device__ __forceinline__ float readlane_f(float v, int lane) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
-}
-
-// Per-wave constants of the score pointwise work for one tile.
-struct TileCtx {
-  int k0;              // first key of the tile (sequence-local)
-  int my_q, my_pos;    // this lane's query and its position
-  int pos_lim;         // position of key j is min(j, pos_lim): n_h with candidates, else n
-  int key_lim;         // allowed keys of this lane's query: j <= key_lim, or j == my_q
-  int nh;              // history length
-  int P, Tb;
-  int64_t my_tau;
-  uint32_t qoff;       // (uint32)(my_tau - base) for the 32-bit modes
-  uint32_t base_lo;    // low word of the tile's timestamp base
-  uint32_t thr;        // two-bucket mode: |dt| >= thr selects bias_hi
-  float c1;            // -log2(e) * bias of a uniform tile, 0 otherwise
-  float bias_lo, bias_hi;          // two-bucket mode: the two biases
-  const HSTU_LDS float *wp, *wt;   // bias tables
-  const HSTU_LDS char *stage;      // the tile's LDS stage
-};
-
-// Score of a pair outside the mask: SiLU of it is exactly 0 in silu_block (u = 1.4e30 is finite, 2^u
-// overflows to +inf, the reciprocal of 1 + inf is 0 and u * 0 = 0), and adding a finite q.k keeps it there.
-constexpr float kMaskedScore = -1.0e30f;
-
-// Per-score bias and mask of a non-uniform tile, added to the 16 scores of 32-key block kb in place;
-// element e holds key k0 + 32*kb + 16*(e/8) + 8*half + e%8.
-template <typename T, int DH, int MODE>
-__device__ __forceinline__ void adjust_block(floatx16 &s, const TileCtx &c, int kb, int half) {
-  using L = Layout<T, DH>;
-  constexpr bool kMasked = MODE == kGen32M || MODE == kGen64M;
-  constexpr bool k64 = MODE == kGen64 || MODE == kGen64M;
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int jl0 = 32 * kb + 16 * g + 8 * half;   // tile-local key of element 8*g
-    uint32_t lo[8], hi[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4 w = *(const HSTU_LDS u32x4 *)(c.stage + L::tau_at(jl0 + 2 * q));
-      lo[2 * q] = w.x; hi[2 * q] = w.y; lo[2 * q + 1] = w.z; hi[2 * q + 1] = w.w;
-    }
-#pragma unroll
-    for (int e8 = 0; e8 < 8; ++e8) {
-      const int e = 8 * g + e8;
-      float bias;
-      if constexpr (MODE == kTwo) {
-        const uint32_t d = __usad(c.qoff, lo[e8] - c.base_lo, 0u);
-        bias = d >= c.thr ? c.bias_hi : c.bias_lo;
-      } else {
-        const int j = c.k0 + jl0 + e8;
-        const int pj = imin(j, c.pos_lim);
-        const uint32_t dp = __usad((uint32_t)c.my_pos, (uint32_t)pj, 0u);
-        const int bp = (int)(dp < (uint32_t)(c.P - 1) ? dp : (uint32_t)(c.P - 1));
-        int bt;
-        if constexpr (!k64) {
-          bt = bitlen_u32(__usad(c.qoff, lo[e8] - c.base_lo, 0u));
-        } else {
-          const int64_t tj = (int64_t)(((uint64_t)hi[e8] << 32) | lo[e8]);
-          bt = bitlen_absdiff(c.my_tau, tj);
-        }
-        bt = imin(bt, c.Tb - 1);
-        bias = c.wp[bp] + c.wt[bt];
-      }
-      if constexpr (kMasked) {
-        const int j = c.k0 + jl0 + e8;
-        const bool ok = (j <= c.key_lim) | (j == c.my_q);
-        s[e] = ok ? s[e] + bias : kMaskedScore;
-      } else {
-        s[e] = s[e] + bias;
-      }
-    }
-  }
-}
-
-// u / (1 + 2^u) for u = -log2(e) * (score + bias) of the 16 scores of one block (the bias is c1 for a
-// uniform tile, already inside the scores otherwise).
-__device__ __forceinline__ void silu_block(const floatx16 &s, float (&a)[16], float c1) {
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const float u = __builtin_fmaf(s[e], kNegLog2e, c1);
-    a[e] = u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u));
-  }
-}
-
-template <typename T, int DH>
-__device__ __forceinline__ void score_block(floatx16 &s, const HSTU_LDS char *lK, int kb, int l32, int half,
-                                            const typename QFrag<T>::type (&qf)[Layout<T, DH>::kQSteps]) {
-  using L = Layout<T, DH>;
-  const int r = 32 * kb + kperm(l32);   // MFMA row l32 takes key kperm(l32) of this 32-key block
-  s = floatx16{};
-#pragma unroll
-  for (int st = 0; st < L::kQSteps; ++st) {
-    if constexpr (L::kBf16) {
-      const bf16x8 kf = *(const HSTU_LDS bf16x8 *)(lK + L::k_at(r, (16 * st + 8 * half) * 2));
-      s = mfma32(kf, qf[st], s);
-    } else {
-      const float kf = *(const HSTU_LDS float *)(lK + L::k_at(r, (2 * st + half) * 4));
-      s = mfma32(kf, qf[st], s);
-    }
-  }
-}
-
-template <typename T, int DH>
-__device__ __forceinline__ void av_block(OAcc<Layout<T, DH>::kDB> &oacc, const float (&a)[16],
-                                         const HSTU_LDS char *lV, int kb, int lane) {
-  using L = Layout<T, DH>;
-  const int l32 = lane & 31, half = lane >> 5;
-  if constexpr (L::kBf16) {
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      bf16x8 pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = f32_to_bf16(a[8 * s2 + e]);
-      const int g16 = lane >> 4, i16 = lane & 15;
-      const int r0 = 32 * kb + 16 * s2 + 8 * half + (i16 >> 2);
-#pragma unroll
-      for (int db = 0; db < L::kDB; ++db) {
-        const int b = (32 * db + 16 * (g16 & 1) + 4 * (i16 & 3)) * 2;
-        const shortx4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HSTU_LDS shortx4 *)(lV + L::v_at(r0, b)));
-        const shortx4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HSTU_LDS shortx4 *)(lV + L::v_at(r0 + 4, b)));
-        const bf16x4 w0 = __builtin_bit_cast(bf16x4, v0), w1 = __builtin_bit_cast(bf16x4, v1);
-        bf16x8 vf;
-        vf[0] = w0[0]; vf[1] = w0[1]; vf[2] = w0[2]; vf[3] = w0[3];
-        vf[4] = w1[0]; vf[5] = w1[1]; vf[6] = w1[2]; vf[7] = w1[3];
-        oacc.d[db] = mfma32(vf, pf, oacc.d[db]);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int r = 32 * kb + 16 * (e / 8) + 8 * half + (e % 8);
-#pragma unroll
-      for (int db = 0; db < L::kDB; ++db) {
-        const float vf = *(const HSTU_LDS float *)(lV + L::v_at(r, (32 * db + l32) * 4));
-        oacc.d[db] = mfma32(vf, a[e], oacc.d[db]);
-      }
-    }
-  }
-}
+using namespace attn;
 
 // One key tile for one wave: both score blocks; for a non-uniform tile the per-score bias and mask
 // patched into them in place (so that every class shares the MFMA code and the accumulators stay in
@@ -304,6 +90,104 @@ __device__ __forceinline__ void tile_body(OAcc<Layout<T, DH>::kDB> &oacc,
   av_block<T, DH>(oacc, a0, lV, 0, lane);
   silu_block(s1, a1, c.c1);
   av_block<T, DH>(oacc, a1, lV, 1, lane);
+}
+
+// ---- backward (dQ and the bias-table gradients), the same tiles as the forward
+//   S^T = K Q^T (+ bias, mask);  dP^T = V dO^T;  dS = dP * SiLU'(s);  dQ^T += K^T dS^T
+// (c_b is applied at the end).  V is staged in the K layout, so that its rows feed the A operand of
+// dP^T like K's feed S^T, and K is read transposed for dQ^T.
+
+// Bias-table gradient bins of one wave: all uniform and two-bucket tiles have position bucket P-1
+// (run_p); consecutive uniform tiles with the same time bucket share run_t; every other score goes
+// straight into the wave's own LDS bins.  Per-wave bins and single-lane flushes keep the sums in a
+// fixed order.
+struct GradBins {
+  HSTU_LDS float *hp, *ht;   // this wave's position bins [P] and time bins [kTimeTab]
+  float run_p, run_t;        // per-lane running sums
+  int cur_bt;                // wave-uniform time bucket of run_t; -1 before the first uniform tile
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Lane 0 adds the wave's total of v (its own butterfly order, the same on every run) to an LDS bin.
+__device__ __forceinline__ void flush_bin(HSTU_LDS float *bin, float v, int lane) {
+  const float t = wave_sum(v);
+  if (lane == 0) *bin += t;
+}
+
+// SiLU'(x) with x = s + bias recovered from the folded exponent u = -log2(e) x:
+// sigma = 1 / (1 + 2^u), SiLU'(x) = sigma (1 + x (1 - sigma)).  A masked score (u = 1.4e30) gives
+// sigma = 0 and a derivative of exactly 0.
+__device__ __forceinline__ float silu_grad_folded(float u) {
+  const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u));
+  return sig * fmaf(u * kNegLn2, 1.0f - sig, 1.0f);
+}
+
+// One tile for one wave.  As in the forward, every class shares one copy of the MFMA code (so the dQ^T
+// accumulators never change registers between classes); only the bias/mask adjustment and the
+// bias-gradient binning branch on the class.
+template <typename T, int DH>
+__device__ __forceinline__ void bwd_tile_body(OAcc<Layout<T, DH>::kDB> &dq,
+                                              const typename QFrag<T>::type (&qf)[Layout<T, DH>::kQSteps],
+                                              const typename QFrag<T>::type (&gf)[Layout<T, DH>::kQSteps],
+                                              const TileCtx &c, int body, int code, int lane, GradBins &gb) {
+  using L = Layout<T, DH>;
+  const int l32 = lane & 31, half = lane >> 5;
+  const HSTU_LDS char *lK = c.stage + L::kOffK;
+  const HSTU_LDS char *lV = c.stage + L::kOffV;
+  float sa = 0.0f, sb = 0.0f;   // uniform: the tile's sum; two-bucket: the sums of the two buckets
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    floatx16 s, dp;
+    score_block<T, DH>(s, lK, kb, l32, half, qf);
+    score_block<T, DH>(dp, lV, kb, l32, half, gf);
+    int bp[16], bt[16];
+    if (body != kUniform) {
+      if (body == kTwo) adjust_block<T, DH, kTwo, true>(s, c, kb, half, bp, bt);
+      else if (body == kGen32) adjust_block<T, DH, kGen32, true>(s, c, kb, half, bp, bt);
+      else if (body == kGen32M) adjust_block<T, DH, kGen32M, true>(s, c, kb, half, bp, bt);
+      else if (body == kGen64) adjust_block<T, DH, kGen64, true>(s, c, kb, half, bp, bt);
+      else adjust_block<T, DH, kGen64M, true>(s, c, kb, half, bp, bt);
+    }
+    float ds[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ds[e] = dp[e] * silu_grad_folded(fmaf(s[e], kNegLog2e, c.c1));
+    if (body == kUniform) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sa += ds[e];
+    } else if (body == kTwo) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if (bt[e] == c.blo) sa += ds[e];
+        else sb += ds[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        __builtin_amdgcn_ds_faddf(gb.hp + bp[e], ds[e], 0, 0, false);
+        __builtin_amdgcn_ds_faddf(gb.ht + bt[e], ds[e], 0, 0, false);
+      }
+    }
+    av_block_in<T, DH, true>(dq, ds, lK, kb, lane);
+  }
+  if (body == kUniform) {
+    const int bt = (code >> 8) & 255;
+    if (bt != gb.cur_bt) {                     // wave-uniform
+      if (gb.cur_bt >= 0) flush_bin(gb.ht + gb.cur_bt, gb.run_t, lane);
+      gb.run_t = 0.0f;
+      gb.cur_bt = bt;
+    }
+    gb.run_t += sa;
+    gb.run_p += sa;
+  } else if (body == kTwo) {
+    flush_bin(gb.ht + c.blo, sa, lane);
+    flush_bin(gb.ht + c.blo + 1, sb, lane);
+    gb.run_p += sa + sb;
+  }
 }
 
 // Timestamp minimum and maximum of every 32-token chunk of every sequence.  Chunk c of sequence b is
@@ -384,7 +268,10 @@ __global__ void __launch_bounds__(256) attn_split_reduce_kernel(const AttnArgs p
 // kv_splits workgroups (tiles_per_split each, the last one taking the rest): with no softmax the partial
 // sums over key ranges simply add, so each split stores its raw sums in `partial` and a reduction kernel
 // adds them in split order.
-template <typename T, int DH, typename TO, bool CACHED>
+//
+// BWD: the dQ pass of the backward (bwd_tile_body); out is dQ (fp32) and each workgroup writes its
+// bias-gradient bins (times c_b) to row blockIdx.x of `partial`.
+template <typename T, int DH, typename TO, bool CACHED, bool BWD>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   using L = Layout<T, DH>;
@@ -405,7 +292,12 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   const int o0 = p.seq_offsets[b];
   const int nq = p.seq_offsets[b + 1] - o0;
   const int q0 = qblk * kBM;
-  if (q0 >= nq) return;  // uniform over the workgroup
+  const int nbins = p.num_pos_buckets + kTimeTab;  // backward: bias-gradient bins per wave
+  if (q0 >= nq) {        // uniform over the workgroup
+    if constexpr (BWD)
+      for (int i = threadIdx.x; i < nbins; i += kThreads) p.partial[(int64_t)blockIdx.x * nbins + i] = 0.0f;
+    return;
+  }
   const bool cand = CACHED || p.mask == kCausalCandidates;
   const int ho = CACHED ? p.hist_offsets[b] : o0;
   const int nh = CACHED ? p.hist_offsets[b + 1] - ho : (cand ? nq - p.num_candidates[b] : nq);
@@ -464,6 +356,22 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
     }
   }
 
+  // dO fragments (backward: B operand of dP^T = V dO^T), laid out like the Q fragments
+  Frag gf[BWD ? L::kQSteps : 1];
+  if constexpr (BWD) {
+    const T *grow = (const T *)p.d_out + (int64_t)(o0 + (my_valid ? my_row : 0)) * p.row_stride + h * DH;
+#pragma unroll
+    for (int s = 0; s < L::kQSteps; ++s) {
+      if constexpr (L::kBf16) {
+        bf16x8 v = *(const bf16x8 *)(grow + s * 16 + half * 8);
+        if (!my_valid) v = bf16x8{};
+        gf[s] = v;
+      } else {
+        gf[s] = my_valid ? grow[s * 2 + half] : 0.0f;
+      }
+    }
+  }
+
   // ---- key tiles needed by the workgroup: [0, r1_end) and, for candidate rows, their own tiles
   const int blast = vq0 + imin(q0 + kBM - 1, nq - 1);
   const int r1_end = (imin(blast + 1, nh) + kBN - 1) / kBN;
@@ -490,7 +398,7 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   const uint32_t rsb = (uint32_t)(p.row_stride * L::kES);        // bytes between tokens (<= 16 KB)
   const int lr16 = 16 * wave + (lane >> 2);                      // tile-local row this lane loads
   const uint32_t k_add = (uint32_t)(h * L::kRB) + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-  const uint32_t v_add = (uint32_t)(h * L::kRB) + 16u * (uint32_t)(lane & 3);
+  const uint32_t v_add = BWD ? k_add : (uint32_t)(h * L::kRB) + 16u * (uint32_t)(lane & 3);
   const int tr16 = 16 * wave + ((lane & 31) >> 1);               // tile-local key of this lane's tau word
   const uint32_t t_add = 4u * (uint32_t)(lane & 1);
   const char *kbase = (const char *)(CACHED ? p.k_hist : p.k), *vbase = (const char *)(CACHED ? p.v_hist : p.v);
@@ -550,7 +458,7 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
           const int bhi = imin(hi == 0 ? 0 : 64 - __clzll((long long)hi), Tb - 1);
           const float wpc = wp_lds[P - 1];
           if (blo == bhi) {
-            code = kUniform;
+            code = kUniform | (blo << 8);   // the bucket is read only by the backward
             clo = kNegLog2e * (wpc + wt_lds[blo]);
           } else if (bhi == blo + 1 && span < (1ull << 32)) {
             code = kTwo | (blo << 8);      // threshold 2^blo: |dt| >= 2^blo has bit length > blo
@@ -583,6 +491,15 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   c.wp = wp_lds;
   c.wt = wt_lds;
 
+  // backward: this wave's bias-gradient bins (after the bias tables), cleared by the wave itself
+  GradBins gb{};
+  if constexpr (BWD) {
+    gb.hp = wt_lds + kTimeTab + wave * nbins;
+    gb.ht = gb.hp + P;
+    gb.cur_bt = -1;
+    for (int i = lane; i < nbins; i += kWave) gb.hp[i] = 0.0f;
+  }
+
   constexpr int kAhead = L::kStages - 1;      // tiles in flight beyond the one being computed
 #pragma unroll
   for (int i = 0; i < kAhead; ++i)
@@ -610,9 +527,11 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
       c.bias_lo = lo_v;
       c.bias_hi = readlane_f(cls_hi, li);
       c.thr = 1u << ((code >> 8) & 31);
+      c.blo = (code >> 8) & 255;
       c.base_lo = (uint32_t)readlane_i((int)cls_base, li);
       c.qoff = (uint32_t)(uint64_t)my_tau - c.base_lo;
-      tile_body<T, DH>(oacc, qf, c, body, lane);
+      if constexpr (BWD) bwd_tile_body<T, DH>(oacc, qf, gf, c, body, code, lane, gb);
+      else tile_body<T, DH>(oacc, qf, c, body, lane);
     }
   }
 
@@ -645,6 +564,30 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
 #pragma unroll
         for (int x = 0; x < 4; ++x) oacc.d[db][4 * e4 + x] = fmaf(a, to_f32(vrow[dh + x]), oacc.d[db][4 * e4 + x]);
       }
+  }
+  if constexpr (BWD) {
+    // dQ = c_b * sum dS k (the accumulators hold true dS values); then the bias-gradient bins
+    if (gb.cur_bt >= 0) flush_bin(gb.ht + gb.cur_bt, gb.run_t, lane);
+    flush_bin(gb.hp + (P - 1), gb.run_p, lane);
+    if (my_valid) {
+      float *drow = (float *)p.out + (int64_t)(o0 + my_row) * p.out_row_stride + h * DH;
+#pragma unroll
+      for (int db = 0; db < L::kDB; ++db)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          floatx4 w;
+          w[0] = oacc.d[db][4 * e4 + 0] * cb; w[1] = oacc.d[db][4 * e4 + 1] * cb;
+          w[2] = oacc.d[db][4 * e4 + 2] * cb; w[3] = oacc.d[db][4 * e4 + 3] * cb;
+          *(floatx4 *)(drow + 32 * db + 8 * e4 + 4 * half) = w;
+        }
+    }
+    __syncthreads();   // every wave's bins complete
+    const HSTU_LDS float *h0 = wt_lds + kTimeTab;
+    for (int i = tid; i < nbins; i += kThreads) {
+      const float v = ((h0[i] + h0[nbins + i]) + h0[2 * nbins + i]) + h0[3 * nbins + i];
+      p.partial[(int64_t)blockIdx.x * nbins + i] = v * cb;
+    }
+    return;
   }
   if (CACHED && p.kv_splits > 1) {
     // raw sums of this key split; attn_split_reduce_kernel adds the splits and applies the scale
@@ -720,17 +663,51 @@ void launch_tau_stats(const int32_t *offs, const int64_t *tau, int64_t *stats, i
                      tau, stats, num_seqs, (int)slots);
 }
 
-template <typename T, int DH, typename TO, bool CACHED>
-hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
+// Dynamic LDS of the query-major kernel: the stage ring, the bias tables and (backward) four waves'
+// bias-gradient bins.
+template <typename T, int DH, bool BWD>
+size_t attn_lds_bytes(int num_pos_buckets) {
   using L = Layout<T, DH>;
+  const size_t tables = (size_t)(num_pos_buckets + kTimeTab) * sizeof(float);
+  return (size_t)L::kStages * L::kStageBytes + tables * (BWD ? 1 + kWaves : 1);
+}
+
+// Bias-table gradients: the workgroups' bins (already times c_b) added in workgroup order, one thread
+// per table entry; time buckets past the largest possible bit length (64) get 0.
+__global__ void __launch_bounds__(256) attn_bias_grad_reduce_kernel(const AttnArgs p, int nwg) {
+  const int P = p.num_pos_buckets, Tb = p.num_time_buckets, nbins = P + kTimeTab;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= p.rab_rows * (P + Tb)) return;
+  const int r = idx / (P + Tb), i = idx % (P + Tb);
+  const int bin = i < P ? i : (i - P < kTimeTab ? i : -1);
+  const int HB = p.num_heads * p.num_seqs;
+  float sum = 0.0f;
+  if (bin >= 0)
+    for (int w = 0; w < nwg; ++w)
+      if (p.rab_rows == 1 || (w % HB) % p.num_heads == r) sum += p.partial[(int64_t)w * nbins + bin];
+  if (i < P) p.d_pos_bias[(int64_t)r * P + i] = sum;
+  else p.d_time_bias[(int64_t)r * Tb + (i - P)] = sum;
+}
+
+template <typename T, int DH, typename TO, bool CACHED, bool BWD>
+hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
   const int n_qblocks = (a.max_seq_len + kBM - 1) / kBM;
   const long long grid = (long long)n_qblocks * a.num_heads * a.num_seqs * (CACHED ? a.kv_splits : 1);
-  if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const size_t lds = (size_t)L::kStages * L::kStageBytes + (size_t)(a.num_pos_buckets + kTimeTab) * sizeof(float);
+  const size_t lds = attn_lds_bytes<T, DH, BWD>(a.num_pos_buckets);
+  if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
+  if (grid == 0) {
+    if constexpr (BWD) {   // no tokens: the bias-table gradients are 0
+      hipLaunchKernelGGL(attn_bias_grad_reduce_kernel,
+                         dim3((unsigned)((a.rab_rows * (a.num_pos_buckets + a.num_time_buckets) + 255) / 256)),
+                         dim3(256), 0, stream, a, 0);
+      return hipGetLastError();
+    }
+    return hipSuccess;
+  }
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_kernel<T, DH, TO, CACHED>,
+    hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_kernel<T, DH, TO, CACHED, BWD>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -738,22 +715,26 @@ hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
   launch_tau_stats(a.seq_offsets, a.timestamps, a.tau_stats, a.num_seqs, a.num_rows_total, stream);
   if constexpr (CACHED)
     launch_tau_stats(a.hist_offsets, a.hist_timestamps, a.hist_tau_stats, a.num_seqs, a.num_hist_rows, stream);
-  hipLaunchKernelGGL((attn_fwd_kernel<T, DH, TO, CACHED>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a,
+  hipLaunchKernelGGL((attn_fwd_kernel<T, DH, TO, CACHED, BWD>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a,
                      n_qblocks);
   if (CACHED && a.kv_splits > 1) {
     const long long n4 = (long long)a.num_rows * a.num_heads * DH / 4;
     hipLaunchKernelGGL(attn_split_reduce_kernel<TO>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, a,
                        a.num_heads * DH);
   }
+  if constexpr (BWD)
+    hipLaunchKernelGGL(attn_bias_grad_reduce_kernel,
+                       dim3((unsigned)((a.rab_rows * (a.num_pos_buckets + a.num_time_buckets) + 255) / 256)),
+                       dim3(256), 0, stream, a, (int)grid);
   return hipGetLastError();
 }
 
-template <typename T, typename TO, bool CACHED>
+template <typename T, typename TO, bool CACHED, bool BWD = false>
 hipError_t launch_dh(const AttnArgs &a, hipStream_t stream) {
   switch (a.head_dim) {
-    case 32: return launch_typed<T, 32, TO, CACHED>(a, stream);
-    case 64: return launch_typed<T, 64, TO, CACHED>(a, stream);
-    case 128: return launch_typed<T, 128, TO, CACHED>(a, stream);
+    case 32: return launch_typed<T, 32, TO, CACHED, BWD>(a, stream);
+    case 64: return launch_typed<T, 64, TO, CACHED, BWD>(a, stream);
+    case 128: return launch_typed<T, 128, TO, CACHED, BWD>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -789,6 +770,20 @@ hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream) {
     return a.out_dtype == kBF16 ? launch_dh<__bf16, __bf16, false>(a, stream) : launch_dh<__bf16, float, false>(a, stream);
   }
   return launch_dh<float, float, false>(a, stream);
+}
+
+hipError_t launch_attn_bwd_dq(const AttnArgs &a, hipStream_t stream) {
+  if (a.in_dtype == kBF16) return launch_dh<__bf16, float, false, true>(a, stream);
+  return launch_dh<float, float, false, true>(a, stream);
+}
+
+size_t attn_bwd_dq_lds_bytes(int in_dtype, int head_dim, int num_pos_buckets) {
+  const bool bf = in_dtype == kBF16;
+  switch (head_dim) {
+    case 32: return bf ? attn_lds_bytes<__bf16, 32, true>(num_pos_buckets) : attn_lds_bytes<float, 32, true>(num_pos_buckets);
+    case 64: return bf ? attn_lds_bytes<__bf16, 64, true>(num_pos_buckets) : attn_lds_bytes<float, 64, true>(num_pos_buckets);
+    default: return bf ? attn_lds_bytes<__bf16, 128, true>(num_pos_buckets) : attn_lds_bytes<float, 128, true>(num_pos_buckets);
+  }
 }
 
 hipError_t launch_attn_cached(const AttnArgs &a, hipStream_t stream) {

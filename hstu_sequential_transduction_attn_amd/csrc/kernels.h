@@ -42,7 +42,12 @@ struct AttnArgs {
   int64_t num_hist_rows;           // T_h
   int32_t kv_splits;               // workgroups per (candidate block, user, head) along the history, >= 1
   int32_t tiles_per_split;         // 64-key history tiles per split (the last split takes the rest)
-  float *partial;                  // kv_splits > 1: workspace [kv_splits][T_c][H][Dh] fp32 raw sums
+  float *partial;                  // kv_splits > 1: workspace [kv_splits][T_c][H][Dh] fp32 raw sums;
+                                   // backward dQ pass: [workgroups][P + 65] bias-gradient bins
+  // Backward only (launch_attn_bwd_dq / launch_attn_bwd_dkdv)
+  const void *d_out;               // [T][row_stride] upstream gradient of out, in_dtype
+  float *d_pos_bias, *d_time_bias; // [R][P], [R][Tb]
+  float *dk, *dv;                  // [T][row_stride] fp32 (dQ goes to out, fp32)
 };
 
 // Key splits of cached scoring for a batch: enough workgroups to fill the chip, each split a whole
@@ -55,6 +60,17 @@ size_t attn_tau_stats_bytes(int64_t total_tokens, int64_t num_seqs);
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream);
 // Candidates against a cached history: each candidate sees every history key of its user and itself.
 hipError_t launch_attn_cached(const AttnArgs &a, hipStream_t stream);
+
+// Backward of the pointwise attention.  The dQ pass (query-major, the forward's tiles) writes dQ to
+// `out` and the bias-table gradients; the dK/dV pass (key-major) writes dk and dv.  Both recompute the
+// scores.  Workspace of the dQ pass: tau_stats and `partial` (attn_bwd_partial_floats floats).
+hipError_t launch_attn_bwd_dq(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_attn_bwd_dkdv(const AttnArgs &a, hipStream_t stream);
+size_t attn_bwd_dq_lds_bytes(int in_dtype, int head_dim, int num_pos_buckets);
+size_t attn_bwd_dkdv_lds_bytes(int in_dtype, int head_dim, int num_pos_buckets);
+inline int64_t attn_bwd_partial_floats(int64_t num_seqs, int64_t num_heads, int64_t max_seq_len, int64_t P) {
+  return (max_seq_len + 127) / 128 * num_heads * num_seqs * (P + 65);
+}
 
 // C[M][N] = epilogue(A[M][K] * B[N][K]^T): bf16 or f32 weights (MFMA operand type `dtype`), fp32
 // accumulation.  With bf16 weights the activation A may be fp32 (x_f32 / g_f32): rounded to bf16, or with

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 2
+#define HSTU_ABI_VERSION 3
 
 typedef enum {
   HSTU_OK = 0,
@@ -168,6 +168,35 @@ hstu_status_t hstu_attn_fwd_cached(const hstu_jagged_t *hist, const hstu_jagged_
                                    hstu_dtype_t in_dtype, const void *k_hist, const void *v_hist, const void *q,
                                    const void *k, const void *v, void *out, hstu_dtype_t out_dtype, void *workspace,
                                    size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace needed by hstu_attn_bwd (bytes; 0 is possible): the timestamp ranges and the per-workgroup
+ * bias-gradient bins.  Depends only on the host fields of `jag` and `desc`.
+ */
+size_t hstu_attn_bwd_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc,
+                                     hstu_dtype_t in_dtype);
+
+/*
+ * Backward of hstu_attn_fwd (the attention of "DLRMv4" page, section on the model architecture, is
+ * trained: the page describes a training benchmark).  For an upstream gradient d_out of out:
+ *   dv_j = c_b sum_i SiLU(s_ij) dO_i,   dS_ij = c_b (dO_i . v_j) SiLU'(s_ij) on allowed pairs,
+ *   dq_i = sum_j dS_ij k_j,   dk_j = sum_i dS_ij q_i,
+ *   d_pos_bias[r][p] = sum of dS_ij over the pairs with position bucket p (heads of table row r),
+ *   d_time_bias[r][t] likewise over the time buckets,
+ * with s_ij, the buckets, the masks and c_b exactly as in hstu_attn_fwd (c_b is a constant here).
+ * q, k, v, d_out: [T][H][Dh], in_dtype, row-major, 16-byte aligned (device).
+ * dq, dk, dv: [T][H][Dh] fp32; d_pos_bias: [R][P] fp32; d_time_bias: [R][Tb] fp32 (device, written, not
+ * accumulated into; no output may overlap an input, another output or the workspace).
+ * bf16 inputs: the products run on bf16 MFMA with fp32 accumulation (SiLU(s) and dS rounded to bf16 as
+ * MFMA operands); f32 inputs: fp32 MFMA.  The result is bitwise deterministic (bias gradients are
+ * summed per wave, per workgroup and across workgroups in a fixed order).
+ * Errors: as hstu_attn_fwd; HSTU_ERR_UNSUPPORTED when the tables do not fit the kernels' LDS
+ * (P up to 4096 fits for bf16 inputs).
+ */
+hstu_status_t hstu_attn_bwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, hstu_dtype_t in_dtype,
+                            const void *q, const void *k, const void *v, const void *d_out, float *dq, float *dk,
+                            float *dv, float *d_pos_bias, float *d_time_bias, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 /* Workspace needed by hstu_layer_fwd (bytes). */
 size_t hstu_layer_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc,

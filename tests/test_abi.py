@@ -39,7 +39,7 @@ def _attn(jag, desc, in_dt=L.HSTU_BF16, out_dt=L.HSTU_BF16, q=P16 + 0x10000, k=P
 
 def test_exports_every_declared_symbol():
     names = L.exported_functions_in_header()
-    assert len(names) == 10
+    assert len(names) == 12
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib()
-    assert lib.hstu_abi_version() == 2
+    assert lib.hstu_abi_version() == 3
     assert lib.hstu_status_string(OK) == b"HSTU_OK"
     assert lib.hstu_status_string(WS_SMALL) == b"HSTU_ERR_WORKSPACE_TOO_SMALL"
     assert lib.hstu_status_string(99) == b"HSTU_STATUS_UNKNOWN"
