@@ -220,6 +220,50 @@ def extended(args, dev):
               f"{flop:.3e} algorithmic FLOP -> {flop / ms / 1e9:.1f} TFLOP/s", file=sys.stderr, flush=True)
         del table, ws
     cached_scoring(dev)
+    attn_backward(dev)
+
+
+def attn_backward(dev):
+    """Attention backward on the attn_L8192 shapes (stderr, informational): hstu_attn_bwd (dq, dk, dv and
+    both bias-table gradients) for a random upstream gradient.  Algorithmic FLOP: five pair products per
+    allowed pair (the score recompute, dP = dO v, dv, dq, dk), i.e. 2.5x the forward's."""
+    import torch
+    from hstu_sequential_transduction_attn_amd import configs as C
+    from hstu_sequential_transduction_attn_amd import inputs as I
+    from hstu_sequential_transduction_attn_amd import _lib as ops
+
+    case = C.attn_L8192()
+    j = case.jagged
+
+    def t(x):
+        if isinstance(x, I.Tensor):
+            return torch.from_numpy(np.ascontiguousarray(x.bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    offs, tau = t(j.seq_offsets.astype(np.int32)), t(j.timestamps.astype(np.int64))
+    q, k, v = t(case.q), t(case.k), t(case.v)
+    g = torch.randn(q.shape, device=dev).to(torch.bfloat16)
+    wp, wt = t(case.rab.pos_bias), t(case.rab.time_bias)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+
+    def run():
+        ops.attn_bwd(offs, tau, q, k, v, g, wp, wt, max_seq_len=j.max_seq_len, workspace=ws)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    flop = 2.5 * case.flops()
+    print(f"[extended] attn_bwd_L8192: {ms:.3f} ms per backward (dq, dk, dv, bias tables); {flop:.3e} algorithmic "
+          f"FLOP -> {flop / ms / 1e9:.1f} TFLOP/s ({flop / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS * 100:.1f}% of dense bf16 peak)",
+          file=sys.stderr, flush=True)
 
 
 def cached_scoring(dev):

@@ -257,7 +257,8 @@ __global__ void __launch_bounds__(256) attn_split_reduce_kernel(const AttnArgs p
   for (int e = 0; e < 4; ++e) o[e] = from_f32<TO>(acc[e] * scale);
 }
 
-// Two waves per SIMD (<= 256 registers per lane) so that one wave's MFMAs overlap the other's VALU work.
+// The query-major attention body, shared by the forward, cached scoring (CACHED) and the backward's dQ
+// pass (BWD); the kernels that run it are defined after it.
 //
 // CACHED: candidates scored against a cached history.  The queries are the candidate rows (q,
 // seq_offsets, timestamps); user b's keys are its n_h cached history rows (k_hist, v_hist,
@@ -272,8 +273,7 @@ __global__ void __launch_bounds__(256) attn_split_reduce_kernel(const AttnArgs p
 // BWD: the dQ pass of the backward (bwd_tile_body); out is dQ (fp32) and each workgroup writes its
 // bias-gradient bins (times c_b) to row blockIdx.x of `partial`.
 template <typename T, int DH, typename TO, bool CACHED, bool BWD>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
+__device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_qblocks) {
   using L = Layout<T, DH>;
   using Frag = typename QFrag<T>::type;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
@@ -663,6 +663,22 @@ void launch_tau_stats(const int32_t *offs, const int64_t *tau, int64_t *stats, i
                      tau, stats, num_seqs, (int)slots);
 }
 
+// The forward and cached scoring: two waves per SIMD (<= 256 registers per lane), so that one wave's
+// MFMAs overlap the other's VALU work.
+template <typename T, int DH, typename TO, bool CACHED>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
+  attn_query_major<T, DH, TO, CACHED, false>(p, n_qblocks);
+}
+
+// The backward's dQ pass carries dO fragments and bucket indices as well: one wave per SIMD, so that
+// nothing spills.
+template <typename T, int DH>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_bwd_dq_kernel(const AttnArgs p, const int n_qblocks) {
+  attn_query_major<T, DH, float, false, true>(p, n_qblocks);
+}
+
 // Dynamic LDS of the query-major kernel: the stage ring, the bias tables and (backward) four waves'
 // bias-gradient bins.
 template <typename T, int DH, bool BWD>
@@ -672,21 +688,32 @@ size_t attn_lds_bytes(int num_pos_buckets) {
   return (size_t)L::kStages * L::kStageBytes + tables * (BWD ? 1 + kWaves : 1);
 }
 
-// Bias-table gradients: the workgroups' bins (already times c_b) added in workgroup order, one thread
-// per table entry; time buckets past the largest possible bit length (64) get 0.
+// Bias-table gradients: the workgroups' bins (already times c_b) added over the workgroups, one
+// 256-thread block per table entry: thread t adds rows t, t + 256, ... in order, then the block adds
+// its 256 partial sums in a fixed tree (so the result is the same on every run).  Time buckets past
+// the largest possible bit length (64) get 0.
 __global__ void __launch_bounds__(256) attn_bias_grad_reduce_kernel(const AttnArgs p, int nwg) {
   const int P = p.num_pos_buckets, Tb = p.num_time_buckets, nbins = P + kTimeTab;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= p.rab_rows * (P + Tb)) return;
+  const int idx = blockIdx.x;                      // < rab_rows * (P + Tb)
   const int r = idx / (P + Tb), i = idx % (P + Tb);
   const int bin = i < P ? i : (i - P < kTimeTab ? i : -1);
   const int HB = p.num_heads * p.num_seqs;
   float sum = 0.0f;
   if (bin >= 0)
-    for (int w = 0; w < nwg; ++w)
+    for (int w = threadIdx.x; w < nwg; w += 256)
       if (p.rab_rows == 1 || (w % HB) % p.num_heads == r) sum += p.partial[(int64_t)w * nbins + bin];
-  if (i < P) p.d_pos_bias[(int64_t)r * P + i] = sum;
-  else p.d_time_bias[(int64_t)r * Tb + (i - P)] = sum;
+  __shared__ float part[256];
+  part[threadIdx.x] = sum;
+  __syncthreads();
+#pragma unroll
+  for (int h = 128; h >= 1; h >>= 1) {
+    if ((int)threadIdx.x < h) part[threadIdx.x] += part[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    if (i < P) p.d_pos_bias[(int64_t)r * P + i] = part[0];
+    else p.d_time_bias[(int64_t)r * Tb + (i - P)] = part[0];
+  }
 }
 
 template <typename T, int DH, typename TO, bool CACHED, bool BWD>
@@ -698,8 +725,7 @@ hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
   if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
   if (grid == 0) {
     if constexpr (BWD) {   // no tokens: the bias-table gradients are 0
-      hipLaunchKernelGGL(attn_bias_grad_reduce_kernel,
-                         dim3((unsigned)((a.rab_rows * (a.num_pos_buckets + a.num_time_buckets) + 255) / 256)),
+      hipLaunchKernelGGL(attn_bias_grad_reduce_kernel, dim3((unsigned)(a.rab_rows * (a.num_pos_buckets + a.num_time_buckets))),
                          dim3(256), 0, stream, a, 0);
       return hipGetLastError();
     }
@@ -707,24 +733,26 @@ hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
   }
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_kernel<T, DH, TO, CACHED, BWD>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    const void *fn = BWD ? (const void *)attn_bwd_dq_kernel<T, DH> : (const void *)attn_fwd_kernel<T, DH, TO, CACHED>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   launch_tau_stats(a.seq_offsets, a.timestamps, a.tau_stats, a.num_seqs, a.num_rows_total, stream);
   if constexpr (CACHED)
     launch_tau_stats(a.hist_offsets, a.hist_timestamps, a.hist_tau_stats, a.num_seqs, a.num_hist_rows, stream);
-  hipLaunchKernelGGL((attn_fwd_kernel<T, DH, TO, CACHED, BWD>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a,
-                     n_qblocks);
+  if constexpr (BWD)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DH>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a, n_qblocks);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<T, DH, TO, CACHED>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a,
+                       n_qblocks);
   if (CACHED && a.kv_splits > 1) {
     const long long n4 = (long long)a.num_rows * a.num_heads * DH / 4;
     hipLaunchKernelGGL(attn_split_reduce_kernel<TO>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, a,
                        a.num_heads * DH);
   }
   if constexpr (BWD)
-    hipLaunchKernelGGL(attn_bias_grad_reduce_kernel,
-                       dim3((unsigned)((a.rab_rows * (a.num_pos_buckets + a.num_time_buckets) + 255) / 256)),
+    hipLaunchKernelGGL(attn_bias_grad_reduce_kernel, dim3((unsigned)(a.rab_rows * (a.num_pos_buckets + a.num_time_buckets))),
                        dim3(256), 0, stream, a, (int)grid);
   return hipGetLastError();
 }
