@@ -112,10 +112,11 @@ constexpr float kMaskedScore = -1.0e30f;
 
 // Per-score bias and mask of a non-uniform tile, added to the 16 scores of 32-key block kb in place;
 // element e holds key k0 + 32*kb + 16*(e/8) + 8*half + e%8.
-// BINS: also return each score's position and time bucket (bp, bt) for the bias-table gradients.
+// BINS: also return each score's position and time bucket for the bias-table gradients, packed as
+// bp | (bt << 16) (bp < 4096, bt <= 64).
 template <typename T, int DH, int MODE, bool BINS = false>
-__device__ __forceinline__ void adjust_block(floatx16 &s, const TileCtx &c, int kb, int half, int *bp_out = nullptr,
-                                             int *bt_out = nullptr) {
+__device__ __forceinline__ void adjust_block(floatx16 &s, const TileCtx &c, int kb, int half,
+                                             int *bins_out = nullptr) {
   using L = Layout<T, DH>;
   constexpr bool kMasked = MODE == kGen32M || MODE == kGen64M;
   constexpr bool k64 = MODE == kGen64 || MODE == kGen64M;
@@ -135,10 +136,7 @@ __device__ __forceinline__ void adjust_block(floatx16 &s, const TileCtx &c, int 
       if constexpr (MODE == kTwo) {
         const uint32_t d = __usad(c.qoff, lo[e8] - c.base_lo, 0u);
         bias = d >= c.thr ? c.bias_hi : c.bias_lo;
-        if constexpr (BINS) {
-          bp_out[e] = c.P - 1;
-          bt_out[e] = d >= c.thr ? c.blo + 1 : c.blo;
-        }
+        if constexpr (BINS) bins_out[e] = (c.P - 1) | ((d >= c.thr ? c.blo + 1 : c.blo) << 16);
       } else {
         const int j = c.k0 + jl0 + e8;
         const int pj = imin(j, c.pos_lim);
@@ -153,10 +151,7 @@ __device__ __forceinline__ void adjust_block(floatx16 &s, const TileCtx &c, int 
         }
         bt = imin(bt, c.Tb - 1);
         bias = c.wp[bp] + c.wt[bt];
-        if constexpr (BINS) {
-          bp_out[e] = bp;
-          bt_out[e] = bt;
-        }
+        if constexpr (BINS) bins_out[e] = bp | (bt << 16);
       }
       if constexpr (kMasked) {
         const int j = c.k0 + jl0 + e8;

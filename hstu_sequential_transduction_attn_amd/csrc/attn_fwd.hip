@@ -145,13 +145,13 @@ __device__ __forceinline__ void bwd_tile_body(OAcc<Layout<T, DH>::kDB> &dq,
     floatx16 s, dp;
     score_block<T, DH>(s, lK, kb, l32, half, qf);
     score_block<T, DH>(dp, lV, kb, l32, half, gf);
-    int bp[16], bt[16];
+    int bins[16];
     if (body != kUniform) {
-      if (body == kTwo) adjust_block<T, DH, kTwo, true>(s, c, kb, half, bp, bt);
-      else if (body == kGen32) adjust_block<T, DH, kGen32, true>(s, c, kb, half, bp, bt);
-      else if (body == kGen32M) adjust_block<T, DH, kGen32M, true>(s, c, kb, half, bp, bt);
-      else if (body == kGen64) adjust_block<T, DH, kGen64, true>(s, c, kb, half, bp, bt);
-      else adjust_block<T, DH, kGen64M, true>(s, c, kb, half, bp, bt);
+      if (body == kTwo) adjust_block<T, DH, kTwo, true>(s, c, kb, half, bins);
+      else if (body == kGen32) adjust_block<T, DH, kGen32, true>(s, c, kb, half, bins);
+      else if (body == kGen32M) adjust_block<T, DH, kGen32M, true>(s, c, kb, half, bins);
+      else if (body == kGen64) adjust_block<T, DH, kGen64, true>(s, c, kb, half, bins);
+      else adjust_block<T, DH, kGen64M, true>(s, c, kb, half, bins);
     }
     float ds[16];
 #pragma unroll
@@ -162,14 +162,14 @@ __device__ __forceinline__ void bwd_tile_body(OAcc<Layout<T, DH>::kDB> &dq,
     } else if (body == kTwo) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        if (bt[e] == c.blo) sa += ds[e];
+        if ((bins[e] >> 16) == c.blo) sa += ds[e];
         else sb += ds[e];
       }
     } else {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        __builtin_amdgcn_ds_faddf(gb.hp + bp[e], ds[e], 0, 0, false);
-        __builtin_amdgcn_ds_faddf(gb.ht + bt[e], ds[e], 0, 0, false);
+        __builtin_amdgcn_ds_faddf(gb.hp + (bins[e] & 0xffff), ds[e], 0, 0, false);
+        __builtin_amdgcn_ds_faddf(gb.ht + (bins[e] >> 16), ds[e], 0, 0, false);
       }
     }
     av_block_in<T, DH, true>(dq, ds, lK, kb, lane);
@@ -671,10 +671,11 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
   attn_query_major<T, DH, TO, CACHED, false>(p, n_qblocks);
 }
 
-// The backward's dQ pass carries dO fragments and bucket indices as well: one wave per SIMD, so that
-// nothing spills.
+// The backward's dQ pass carries dO fragments and bucket indices as well.  It too runs two waves per
+// SIMD: at Dh = 128 a few registers spill, and that is still faster than one wave per SIMD without
+// spills (the waves' MFMA and VALU phases overlap).
 template <typename T, int DH>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq_kernel(const AttnArgs p, const int n_qblocks) {
   attn_query_major<T, DH, float, false, true>(p, n_qblocks);
 }
