@@ -202,3 +202,51 @@ def test_cached_workspace_covers_timestamp_ranges_and_partial_sums():
     assert cws(_jag(B=3), cand) == 0
     st, msg = _cached(_jag(B=2, T=500, max_len=501), _jag(B=2, T=64, max_len=40), _desc())
     assert st == INVALID and "max_seq_len" in msg
+
+
+def _bwd(jag, desc, in_dt=L.HSTU_BF16, q=P16 + 0x10000, k=P16 + 0x2000000, v=P16 + 0x4000000, g=P16 + 0x6000000,
+         dq=P16 + 0x8000000, dk=P16 + 0xA000000, dv=P16 + 0xC000000, dwp=P16 + 0xE000000, dwt=P16 + 0xE100000,
+         ws=P16 + 0x10000000, nws=1 << 24):
+    lib = _lib()
+    st = lib.hstu_attn_bwd(ctypes.byref(jag) if jag else None, ctypes.byref(desc) if desc else None, in_dt, q, k, v, g,
+                           dq, dk, dv, dwp, dwt, ws, nws, None)
+    return st, lib.hstu_last_error().decode()
+
+
+def test_bwd_argument_errors():
+    jag, desc = _jag(B=2, T=100, max_len=60), _desc(H=2, Dh=64, P=32, Tb=32)
+    assert _bwd(None, desc)[0] == INVALID
+    assert _bwd(jag, None)[0] == INVALID
+    st, msg = _bwd(jag, _desc(Dh=96))
+    assert st == UNSUPPORTED and "head_dim" in msg
+    st, msg = _bwd(jag, desc, dwp=None)
+    assert st == INVALID and "d_pos_bias" in msg
+    st, msg = _bwd(jag, desc, nws=16)
+    assert st == WS_SMALL
+    st, msg = _bwd(jag, desc, g=None)
+    assert st == INVALID and "NULL" in msg
+    st, msg = _bwd(jag, desc, dk=P16 + 0x8)
+    assert st == INVALID and "aligned" in msg
+    st, msg = _bwd(jag, desc, dq=P16 + 0x2000000)          # dq on top of k
+    assert st == INVALID and "overlaps" in msg
+    st, msg = _bwd(jag, desc, dv=P16 + 0x8000000)          # dv on top of dq
+    assert st == INVALID and "overlap" in msg
+    st, msg = _bwd(jag, desc, dwt=P16 + 0xE000000)         # the two bias gradients on top of each other
+    assert st == INVALID and "overlaps" in msg
+
+
+def test_bwd_tables_too_large_for_lds_are_unsupported():
+    jag = _jag(B=2, T=100, max_len=60)
+    st, msg = _bwd(jag, _desc(H=2, Dh=128, P=4096, Tb=64), in_dt=L.HSTU_F32)
+    assert st == UNSUPPORTED and "LDS" in msg
+
+
+def test_bwd_workspace_holds_bins_per_workgroup():
+    lib = _lib()
+    desc = _desc(H=4, Dh=128, P=256, Tb=256)
+    jag = _jag(B=8, T=65536, max_len=8192)
+    n = lib.hstu_attn_bwd_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), L.HSTU_BF16)
+    workgroups = (8192 // 128) * 4 * 8
+    assert n >= workgroups * (256 + 65) * 4 and n % 256 == 0
+    assert lib.hstu_attn_bwd_workspace_bytes(ctypes.byref(_jag(B=2, T=0, max_len=0)), ctypes.byref(desc),
+                                             L.HSTU_BF16) == 0
