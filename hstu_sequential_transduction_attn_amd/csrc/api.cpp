@@ -175,8 +175,8 @@ hstu_status_t hstu_attn_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *de
     const size_t nout = (size_t)T * desc->num_heads * desc->head_dim * esize(out_dtype);
     if (overlaps(out, nout, q, nin) || overlaps(out, nout, k, nin) || overlaps(out, nout, v, nin))
       return fail(HSTU_ERR_INVALID_ARGUMENT, "out overlaps q, k or v");
-    if (overlaps(workspace, need, out, nout) || overlaps(workspace, need, q, nin) || overlaps(workspace, need, k, nin) ||
-        overlaps(workspace, need, v, nin))
+    if (overlaps(workspace, need, out, nout) || overlaps(workspace, need, q, nin) ||
+        overlaps(workspace, need, k, nin) || overlaps(workspace, need, v, nin))
       return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace overlaps q, k, v or out");
     hstu::AttnArgs a = attn_args(jag, desc);
     a.q = q;
@@ -239,7 +239,8 @@ hstu_status_t hstu_attn_fwd_cached(const hstu_jagged_t *hist, const hstu_jagged_
     if (hist->num_seqs != cand->num_seqs)
       return fail(HSTU_ERR_INVALID_ARGUMENT, "hist->num_seqs = %d != cand->num_seqs = %d", hist->num_seqs,
                   cand->num_seqs);
-    if (hist->total_tokens < 0) return fail(HSTU_ERR_INVALID_ARGUMENT, "hist->total_tokens = %d < 0", hist->total_tokens);
+    if (hist->total_tokens < 0)
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "hist->total_tokens = %d < 0", hist->total_tokens);
     if (hist->max_seq_len < 0 || hist->max_seq_len > hist->total_tokens)
       return fail(HSTU_ERR_INVALID_ARGUMENT, "hist->max_seq_len = %d outside [0, hist->total_tokens = %d]",
                   hist->max_seq_len, hist->total_tokens);
@@ -270,9 +271,9 @@ hstu_status_t hstu_attn_fwd_cached(const hstu_jagged_t *hist, const hstu_jagged_
     if (overlaps(out, nout, q, nin) || overlaps(out, nout, k, nin) || overlaps(out, nout, v, nin) ||
         overlaps(out, nout, k_hist, nhist) || overlaps(out, nout, v_hist, nhist))
       return fail(HSTU_ERR_INVALID_ARGUMENT, "out overlaps an input");
-    if (overlaps(workspace, need, out, nout) || overlaps(workspace, need, q, nin) || overlaps(workspace, need, k, nin) ||
-        overlaps(workspace, need, v, nin) || overlaps(workspace, need, k_hist, nhist) ||
-        overlaps(workspace, need, v_hist, nhist))
+    if (overlaps(workspace, need, out, nout) || overlaps(workspace, need, q, nin) ||
+        overlaps(workspace, need, k, nin) || overlaps(workspace, need, v, nin) ||
+        overlaps(workspace, need, k_hist, nhist) || overlaps(workspace, need, v_hist, nhist))
       return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace overlaps an input or out");
     hstu::AttnArgs a = attn_args(cand, &d);
     a.num_candidates = nullptr;
@@ -485,7 +486,8 @@ hstu_status_t hstu_gather_rows(const void *table, int64_t table_rows, int32_t d,
     if (table_rows < 1) return fail(HSTU_ERR_INVALID_ARGUMENT, "table_rows = %lld < 1", (long long)table_rows);
     if (T == 0) return ok();
     if (!table || !ids || !out) return fail(HSTU_ERR_INVALID_ARGUMENT, "table/ids/out is NULL");
-    if (!aligned16(table) || !aligned16(out)) return fail(HSTU_ERR_INVALID_ARGUMENT, "table/out must be 16-byte aligned");
+    if (!aligned16(table) || !aligned16(out))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "table/out must be 16-byte aligned");
     if (overlaps(out, (size_t)T * row_bytes, table, (size_t)table_rows * row_bytes))
       return fail(HSTU_ERR_INVALID_ARGUMENT, "out overlaps table");
     return from_hip(hstu::launch_gather_rows(table, table_rows, (int32_t)row_bytes, ids, T, out, (hipStream_t)stream),

@@ -726,8 +726,8 @@ hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
   if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
   if (grid == 0) {
     if constexpr (BWD) {   // no tokens: the bias-table gradients are 0
-      hipLaunchKernelGGL(attn_bias_grad_reduce_kernel, dim3((unsigned)(a.rab_rows * (a.num_pos_buckets + a.num_time_buckets))),
-                         dim3(256), 0, stream, a, 0);
+      const unsigned entries = (unsigned)(a.rab_rows * (a.num_pos_buckets + a.num_time_buckets));
+      hipLaunchKernelGGL(attn_bias_grad_reduce_kernel, dim3(entries), dim3(256), 0, stream, a, 0);
       return hipGetLastError();
     }
     return hipSuccess;
@@ -752,9 +752,10 @@ hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(attn_split_reduce_kernel<TO>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, a,
                        a.num_heads * DH);
   }
-  if constexpr (BWD)
-    hipLaunchKernelGGL(attn_bias_grad_reduce_kernel, dim3((unsigned)(a.rab_rows * (a.num_pos_buckets + a.num_time_buckets))),
-                       dim3(256), 0, stream, a, (int)grid);
+  if constexpr (BWD) {
+    const unsigned entries = (unsigned)(a.rab_rows * (a.num_pos_buckets + a.num_time_buckets));
+    hipLaunchKernelGGL(attn_bias_grad_reduce_kernel, dim3(entries), dim3(256), 0, stream, a, (int)grid);
+  }
   return hipGetLastError();
 }
 
@@ -796,7 +797,8 @@ size_t attn_tau_stats_bytes(int64_t total_tokens, int64_t num_seqs) {
 
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream) {
   if (a.in_dtype == kBF16) {
-    return a.out_dtype == kBF16 ? launch_dh<__bf16, __bf16, false>(a, stream) : launch_dh<__bf16, float, false>(a, stream);
+    return a.out_dtype == kBF16 ? launch_dh<__bf16, __bf16, false>(a, stream)
+                                : launch_dh<__bf16, float, false>(a, stream);
   }
   return launch_dh<float, float, false>(a, stream);
 }
@@ -808,16 +810,18 @@ hipError_t launch_attn_bwd_dq(const AttnArgs &a, hipStream_t stream) {
 
 size_t attn_bwd_dq_lds_bytes(int in_dtype, int head_dim, int num_pos_buckets) {
   const bool bf = in_dtype == kBF16;
+  const int P = num_pos_buckets;
   switch (head_dim) {
-    case 32: return bf ? attn_lds_bytes<__bf16, 32, true>(num_pos_buckets) : attn_lds_bytes<float, 32, true>(num_pos_buckets);
-    case 64: return bf ? attn_lds_bytes<__bf16, 64, true>(num_pos_buckets) : attn_lds_bytes<float, 64, true>(num_pos_buckets);
-    default: return bf ? attn_lds_bytes<__bf16, 128, true>(num_pos_buckets) : attn_lds_bytes<float, 128, true>(num_pos_buckets);
+    case 32: return bf ? attn_lds_bytes<__bf16, 32, true>(P) : attn_lds_bytes<float, 32, true>(P);
+    case 64: return bf ? attn_lds_bytes<__bf16, 64, true>(P) : attn_lds_bytes<float, 64, true>(P);
+    default: return bf ? attn_lds_bytes<__bf16, 128, true>(P) : attn_lds_bytes<float, 128, true>(P);
   }
 }
 
 hipError_t launch_attn_cached(const AttnArgs &a, hipStream_t stream) {
   if (a.in_dtype == kBF16) {
-    return a.out_dtype == kBF16 ? launch_dh<__bf16, __bf16, true>(a, stream) : launch_dh<__bf16, float, true>(a, stream);
+    return a.out_dtype == kBF16 ? launch_dh<__bf16, __bf16, true>(a, stream)
+                                : launch_dh<__bf16, float, true>(a, stream);
   }
   return launch_dh<float, float, true>(a, stream);
 }
