@@ -1,4 +1,4 @@
-"""Float64 CPU oracle of the HSTU layer forward -- TEST INFRASTRUCTURE ONLY.
+"""Float64 CPU oracle of the HSTU layer (forward and its gradients) -- TEST INFRASTRUCTURE ONLY.
 
 Only the tests, the package's smoke check and the benchmark's CPU-baseline leg may import this
 module.  The HIP library never calls it, and it imports nothing from the library: it depends on
@@ -315,6 +315,67 @@ def layer_fwd(x, jag, w_uvqk, b_uvqk, w_out, b_out, pos_bias, time_bias, num_hea
     if return_parts:
         return y, dict(u=u, v=v, q=q, k=k, o=o, g=g)
     return y
+
+
+def layer_norm_bwd(x, eps, dy):
+    """Gradient of y = layer_norm(x, eps) over the last axis for an upstream gradient dy, float64.
+    With x_hat = (x - mean) * rstd and rstd = 1/sqrt(var + eps):
+        dx = rstd * (dy - mean(dy) - x_hat * mean(dy * x_hat)).
+    """
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    rstd = 1.0 / np.sqrt(((x - mu) ** 2).mean(axis=-1, keepdims=True) + eps)
+    xh = (x - mu) * rstd
+    return rstd * (dy - dy.mean(axis=-1, keepdims=True) - xh * (dy * xh).mean(axis=-1, keepdims=True))
+
+
+def layer_bwd(x, jag, w_uvqk, b_uvqk, w_out, b_out, pos_bias, time_bias, num_heads, head_dim,
+              ln_eps, ln_output, dy):
+    """Gradients of layer_fwd for an upstream gradient dy of its output y (the layer is trained:
+    [DLRMv4] describes a training benchmark).  Returns a dict of float64 arrays:
+        dx [T, D], d_w_uvqk [4*H*Dh, D], d_b_uvqk [4*H*Dh], d_w_out [D, H*Dh], d_b_out [D],
+        d_pos_bias [R, P], d_time_bias [R, Tb].
+    The chain, from the output back (r = x + g W2^T + b2 is the pre-LayerNorm sum, g = LN(o) * U):
+        dr = layer_norm_bwd(r, dy) if ln_output else dy
+        d_b_out = sum_t dr;  d_w_out = dr^T g;  dg = dr W2
+        dU = dg * LN(o);  do = layer_norm_bwd(o, dg * U)       (o = concat_h O, per token)
+        dQ, dK, dV, d_pos_bias, d_time_bias = attn_bwd(..., do)
+        dz = [dU | dV | dQ | dK] * SiLU'(z)                     (z = x W1^T + b1, before the SiLU)
+        d_b_uvqk = sum_t dz;  d_w_uvqk = dz^T x;  dx = dr + dz W1
+    """
+    x = np.asarray(x, np.float64)
+    w1 = np.asarray(w_uvqk, np.float64)
+    w2 = np.asarray(w_out, np.float64)
+    T = x.shape[0]
+    hd = num_heads * head_dim
+    z = x @ w1.T
+    if b_uvqk is not None:
+        z = z + np.asarray(b_uvqk, np.float64)
+    s = silu(z)
+    u, v, q, k = (s[:, c * hd:(c + 1) * hd].reshape(T, num_heads, head_dim) for c in range(4))
+    o = attn_fwd(jag, q, k, v, pos_bias, time_bias).reshape(T, hd)
+    on = layer_norm(o, ln_eps)
+    uf = u.reshape(T, hd)
+    g = on * uf
+    dy = np.asarray(dy, np.float64)
+    if ln_output:
+        r = x + g @ w2.T
+        if b_out is not None:
+            r = r + np.asarray(b_out, np.float64)
+        dr = layer_norm_bwd(r, ln_eps, dy)
+    else:
+        dr = dy
+    d_w_out = dr.T @ g
+    d_b_out = dr.sum(axis=0)
+    dg = dr @ w2
+    du = dg * on
+    do = layer_norm_bwd(o, ln_eps, dg * uf)
+    dq, dk, dv, dwp, dwt = attn_bwd(jag, q, k, v, pos_bias, time_bias, do.reshape(T, num_heads, head_dim))
+    ds = np.concatenate([du, dv.reshape(T, hd), dq.reshape(T, hd), dk.reshape(T, hd)], axis=1)
+    dz = ds * silu_grad(z)
+    return dict(dx=dr + dz @ w1, d_w_uvqk=dz.T @ x, d_b_uvqk=dz.sum(axis=0), d_w_out=d_w_out,
+                d_b_out=d_b_out, d_pos_bias=dwp, d_time_bias=dwt)
 
 
 def stack_fwd(x, jag, layers, num_heads, head_dim):

@@ -1,0 +1,118 @@
+"""Pins of the float64 layer backward (oracle.layer_bwd) and of the LayerNorm backward.
+
+Every gradient is compared with central finite differences of the forward oracle (layer_fwd,
+layer_norm), which are pinned elsewhere; the difference quotient shares none of the backward's
+formulas, so a dropped term of the LayerNorm Jacobian, a missing SiLU' factor, a transposed weight
+gradient, the wrong slice of the projection or a lost residual path fails here.  The LayerNorm
+backward is also held to two exact invariances of LayerNorm itself.
+"""
+import numpy as np
+import pytest
+
+from oracle import hstu_oracle as O
+
+
+def _fd(f, x, eps=1e-6):
+    """Central differences of the scalar f with respect to every entry of x (modified in place)."""
+    out = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        old = x[i]
+        x[i] = old + eps; fp = f()
+        x[i] = old - eps; fm = f()
+        x[i] = old
+        out[i] = (fp - fm) / (2 * eps)
+    return out
+
+
+def test_layer_norm_bwd_matches_finite_differences():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4, 7)) * 2 + 0.5
+    dy = rng.standard_normal((4, 7))
+    for eps in (1e-6, 0.3):
+        got = O.layer_norm_bwd(x, eps, dy)
+        want = _fd(lambda: float(np.sum(O.layer_norm(x, eps) * dy)), x)
+        np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-8)
+
+
+def test_layer_norm_bwd_invariances():
+    """LN(x + c) = LN(x) for any eps, so each row of dx sums to 0; with eps = 0, LN(a x) = LN(x)
+    for a > 0, so each row of dx is orthogonal to its x."""
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((5, 16)) * 3 - 1
+    dy = rng.standard_normal((5, 16))
+    dx = O.layer_norm_bwd(x, 1e-3, dy)
+    np.testing.assert_allclose(dx.sum(axis=1), 0.0, atol=1e-12)
+    dx0 = O.layer_norm_bwd(x, 0.0, dy)
+    np.testing.assert_allclose((dx0 * x).sum(axis=1), 0.0, atol=1e-11)
+
+
+def _jag(lengths, taus, mask=O.CAUSAL, num_candidates=None):
+    offs = np.zeros(len(lengths) + 1, dtype=np.int64)
+    offs[1:] = np.cumsum(lengths)
+    return dict(seq_offsets=offs, timestamps=np.asarray(taus, np.int64), mask=mask,
+                num_candidates=None if num_candidates is None else np.asarray(num_candidates),
+                attn_scale=None)
+
+
+def _case(seed, lengths, D=6, H=2, Dh=3, P=5, Tb=6, R=1, biases=True):
+    rng = np.random.default_rng(seed)
+    T = sum(lengths)
+    hd = H * Dh
+    x = rng.standard_normal((T, D))
+    w1 = rng.normal(0, 0.6, (4 * hd, D))
+    w2 = rng.normal(0, 0.6, (D, hd))
+    b1 = rng.normal(0, 0.3, 4 * hd) if biases else None
+    b2 = rng.normal(0, 0.3, D) if biases else None
+    wp, wt = rng.normal(0, 0.5, (R, P)), rng.normal(0, 0.5, (R, Tb))
+    dy = rng.standard_normal((T, D))
+    taus = np.concatenate([1_700_000_000 + np.cumsum(rng.integers(1, 40, size=n)) for n in lengths])
+    return x, w1, b1, w2, b2, wp, wt, dy, taus
+
+
+@pytest.mark.parametrize("mask,lengths,m,R,ln_output,biases", [
+    (O.CAUSAL, [5, 1, 4], None, 1, False, True),
+    (O.CAUSAL, [6, 3], None, 2, True, True),
+    (O.CAUSAL_CANDIDATES, [6, 4], [2, 1], 1, True, False),
+])
+def test_layer_gradients_match_finite_differences(mask, lengths, m, R, ln_output, biases):
+    H, Dh, eps = 2, 3, 1e-3
+    x, w1, b1, w2, b2, wp, wt, dy, tau = _case(7 + R + len(lengths), lengths, H=H, Dh=Dh, R=R,
+                                                 biases=biases)
+    jag = _jag(lengths, tau, mask, m)
+    got = O.layer_bwd(x, jag, w1, b1, w2, b2, wp, wt, H, Dh, eps, ln_output, dy)
+
+    def loss():
+        y = O.layer_fwd(x, jag, w1, b1, w2, b2, wp, wt, H, Dh, eps, ln_output)
+        return float(np.sum(y * dy))
+
+    pairs = [("dx", x), ("d_w_uvqk", w1), ("d_w_out", w2), ("d_pos_bias", wp), ("d_time_bias", wt)]
+    if biases:
+        pairs += [("d_b_uvqk", b1), ("d_b_out", b2)]
+    for name, arr in pairs:
+        want = _fd(loss, arr)
+        np.testing.assert_allclose(got[name], want, rtol=2e-6, atol=2e-7, err_msg=name)
+    if not biases:
+        # the bias gradients do not depend on whether the biases are zero or absent
+        hd = H * Dh
+        b1z, b2z = np.zeros(4 * hd), np.zeros(x.shape[1])
+        got_z = O.layer_bwd(x, jag, w1, b1z, w2, b2z, wp, wt, H, Dh, eps, ln_output, dy)
+        for name in ("d_b_uvqk", "d_b_out"):
+            want = _fd(lambda: float(np.sum(O.layer_fwd(x, jag, w1, b1z, w2, b2z, wp, wt, H, Dh, eps,
+                                                          ln_output) * dy)),
+                       b1z if name == "d_b_uvqk" else b2z)
+            np.testing.assert_allclose(got[name], want, rtol=2e-6, atol=2e-7, err_msg=name)
+            np.testing.assert_allclose(got_z[name], got[name], rtol=1e-12, atol=1e-14)
+
+
+def test_zero_output_weights_pass_the_gradient_straight_through():
+    """With W2 = 0 the branch's output is the constant b2: dx = dy (no post-LN), and nothing
+    upstream of the output projection receives a gradient."""
+    x, w1, b1, w2, b2, wp, wt, dy, tau = _case(11, [4, 5])
+    jag = _jag([4, 5], tau)
+    got = O.layer_bwd(x, jag, w1, b1, np.zeros_like(w2), b2, wp, wt, 2, 3, 1e-3, False, dy)
+    np.testing.assert_array_equal(got["dx"], dy)
+    for name in ("d_w_uvqk", "d_b_uvqk", "d_pos_bias", "d_time_bias"):
+        assert not np.any(got[name]), name
+    np.testing.assert_allclose(got["d_b_out"], dy.sum(axis=0), rtol=1e-14)
