@@ -47,6 +47,11 @@ class LayerWeightsT(ctypes.Structure):
                 ("ln_eps", c_f32), ("ln_output", c_i32), ("act_split", c_i32)]
 
 
+class LayerGradsT(ctypes.Structure):
+    _fields_ = [("d_w_uvqk", c_vp), ("d_b_uvqk", c_vp), ("d_w_out", c_vp), ("d_b_out", c_vp), ("d_pos_bias", c_vp),
+                ("d_time_bias", c_vp)]
+
+
 _lib = None
 
 
@@ -96,6 +101,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_layer_fwd.restype = ctypes.c_int
     lib.hstu_layer_fwd.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT), ctypes.POINTER(LayerWeightsT),
                                    ctypes.c_int, ctypes.c_int, c_vp, ctypes.c_int, c_vp, c_vp, c_sz, c_vp]
+    lib.hstu_layer_bwd_workspace_bytes.restype = c_sz
+    lib.hstu_layer_bwd_workspace_bytes.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT),
+                                                   ctypes.POINTER(LayerWeightsT), ctypes.c_int]
+    lib.hstu_layer_bwd.restype = ctypes.c_int
+    lib.hstu_layer_bwd.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT), ctypes.POINTER(LayerWeightsT),
+                                   ctypes.c_int, ctypes.c_int, c_vp, ctypes.c_int, c_vp, c_vp,
+                                   ctypes.POINTER(LayerGradsT), c_vp, c_sz, c_vp]
     lib.hstu_gather_rows.restype = ctypes.c_int
     lib.hstu_gather_rows.argtypes = [c_vp, c_i64, c_i32, ctypes.c_int, c_vp, c_i32, c_vp, c_vp]
     if path is None:
@@ -240,6 +252,53 @@ def layer_fwd(x, seq_offsets, timestamps, w_uvqk, w_out, pos_bias, time_bias, nu
     _check(lib.hstu_layer_fwd(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), dt, _dtype_code(x), _ptr(x),
                               _dtype_code(y), _ptr(y), _ptr(workspace), workspace.numel(), _stream(stream)))
     return y
+
+
+def layer_bwd_workspace_bytes(x, seq_offsets, timestamps, w_uvqk, w_out, pos_bias, time_bias, num_heads, head_dim, *,
+                              max_seq_len: int, ln_output: bool = False, mask: int = MASK_CAUSAL,
+                              num_candidates=None) -> int:
+    lib = load_library()
+    jag = make_jagged(seq_offsets, timestamps, max_seq_len, num_candidates, None)
+    desc = make_desc(num_heads, head_dim, pos_bias, time_bias, mask)
+    w = LayerWeightsT(x.shape[1], _ptr(w_uvqk), None, _ptr(w_out), None, 1e-6, int(bool(ln_output)), 0)
+    return int(lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w),
+                                                  _dtype_code(w_uvqk)))
+
+
+def layer_bwd(x, dy, seq_offsets, timestamps, w_uvqk, w_out, pos_bias, time_bias, num_heads: int, head_dim: int, *,
+              max_seq_len: int, b_uvqk=None, b_out=None, ln_eps: float = 1e-6, ln_output: bool = False,
+              mask: int = MASK_CAUSAL, num_candidates=None, attn_scale=None, act_split: bool = False,
+              bias_grads: bool = True, workspace=None, dx=None, grads=None, stream=None):
+    """hstu_layer_bwd(...): gradients of layer_fwd for the upstream gradient dy (dy's dtype is the
+    gradient dtype, fp32 or the weights' dtype).  Returns a dict with dx [T, D] (dy's dtype) and fp32
+    d_w_uvqk, d_b_uvqk, d_w_out, d_b_out (None unless bias_grads), d_pos_bias, d_time_bias; `grads`
+    may supply any of the fp32 gradient tensors to write into."""
+    lib = load_library()
+    T, D = x.shape
+    dev = x.device
+    if dx is None:
+        dx = torch.empty((T, D), dtype=dy.dtype, device=dev)
+    hd = num_heads * head_dim
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dx=dx, d_w_uvqk=torch.empty((4 * hd, D), **f32), d_w_out=torch.empty((D, hd), **f32),
+               d_b_uvqk=torch.empty(4 * hd, **f32) if bias_grads else None,
+               d_b_out=torch.empty(D, **f32) if bias_grads else None,
+               d_pos_bias=torch.empty(pos_bias.shape, **f32), d_time_bias=torch.empty(time_bias.shape, **f32))
+    out.update(grads or {})
+    jag = make_jagged(seq_offsets, timestamps, max_seq_len, num_candidates, attn_scale)
+    desc = make_desc(num_heads, head_dim, pos_bias, time_bias, mask)
+    w = LayerWeightsT(D, _ptr(w_uvqk), _ptr(b_uvqk), _ptr(w_out), _ptr(b_out), float(ln_eps), int(bool(ln_output)),
+                      int(bool(act_split)))
+    grads = LayerGradsT(_ptr(out["d_w_uvqk"]), _ptr(out["d_b_uvqk"]), _ptr(out["d_w_out"]), _ptr(out["d_b_out"]),
+                        _ptr(out["d_pos_bias"]), _ptr(out["d_time_bias"]))
+    dt = _dtype_code(w_uvqk)
+    nws = int(lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), dt))
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    _check(lib.hstu_layer_bwd(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), dt, _dtype_code(x), _ptr(x),
+                              _dtype_code(dy), _ptr(dy), _ptr(dx), ctypes.byref(grads), _ptr(workspace),
+                              workspace.numel(), _stream(stream)))
+    return out
 
 
 def gather_rows(table: torch.Tensor, ids: torch.Tensor, out=None, stream=None):

@@ -474,6 +474,256 @@ hstu_status_t hstu_layer_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
   }
 }
 
+namespace {
+
+// Layer-backward workspace regions (256-byte aligned).  Recomputed forward: W1^T, W2^T (dtype), U
+// (fp32), V, Q, K (dtype), Z = the projection's pre-activation (dtype; overwritten by dz), O (fp32)
+// and its per-head statistics, the timestamp ranges, the pre-LayerNorm sum r (fp32, ln_output only;
+// overwritten by dr).  Backward: dg (fp32), g and dO (dtype), dQ, dK, dV (fp32), the attention
+// backward's bias-gradient bins, the token-contiguous transposes x^T, dr^T, g^T, dz^T (dtype, T padded
+// to Tp, a multiple of 32) and the split-K partial products of the weight gradients.
+struct LayerBwdWs {
+  size_t w1t, w2t, u, v, q, k, z, o, ostat, stats, r32, dg, g, d_o, dq, dk, dv, bins, xt, drt, gt, dzt, part, total;
+  int64_t Tp;
+  int split_w1, split_w2;
+};
+
+LayerBwdWs layer_bwd_ws(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, int64_t D, hstu_dtype_t dt,
+                        bool ln_output) {
+  LayerBwdWs w{};
+  const int64_t T = jag->total_tokens, B = jag->num_seqs, H = desc->num_heads;
+  const int64_t HD = H * desc->head_dim;
+  const size_t es = esize(dt);
+  const int dtc = dt == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
+  w.Tp = (T + 31) / 32 * 32;
+  w.split_w1 = hstu::gemm_plain_splits(4 * HD, D, w.Tp, dtc, 0);
+  w.split_w2 = hstu::gemm_plain_splits(D, HD, w.Tp, dtc, 0);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += round_up(bytes, 256);
+    return at;
+  };
+  w.w1t = take((size_t)4 * HD * D * es);
+  w.w2t = take((size_t)HD * D * es);
+  w.u = take((size_t)T * HD * 4);
+  w.v = take((size_t)T * HD * es);
+  w.q = take((size_t)T * HD * es);
+  w.k = take((size_t)T * HD * es);
+  w.z = take((size_t)T * 4 * HD * es);
+  w.o = take((size_t)T * HD * 4);
+  w.ostat = take((size_t)T * H * 8);
+  w.stats = take(hstu::attn_tau_stats_bytes(T, B));
+  w.r32 = take(ln_output ? (size_t)T * D * 4 : 0);
+  w.dg = take((size_t)T * HD * 4);
+  w.g = take((size_t)T * HD * es);
+  w.d_o = take((size_t)T * HD * es);
+  w.dq = take((size_t)T * HD * 4);
+  w.dk = take((size_t)T * HD * 4);
+  w.dv = take((size_t)T * HD * 4);
+  w.bins = take((size_t)hstu::attn_bwd_partial_floats(B, H, jag->max_seq_len, desc->num_pos_buckets) * 4);
+  w.xt = take((size_t)D * w.Tp * es);
+  w.drt = take((size_t)D * w.Tp * es);
+  w.gt = take((size_t)HD * w.Tp * es);
+  w.dzt = take((size_t)4 * HD * w.Tp * es);
+  const size_t p1 = w.split_w1 > 1 ? (size_t)w.split_w1 * 4 * HD * D : 0;
+  const size_t p2 = w.split_w2 > 1 ? (size_t)w.split_w2 * D * HD : 0;
+  w.part = take((p1 > p2 ? p1 : p2) * 4);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+size_t hstu_layer_bwd_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc,
+                                      const hstu_layer_weights_t *w, hstu_dtype_t dtype) {
+  if (!jag || !desc || !w || jag->total_tokens < 0 || jag->num_seqs < 0 || desc->num_heads < 1 ||
+      desc->head_dim < 1 || desc->num_pos_buckets < 1 || w->d_model < 1 || !valid_dtype(dtype))
+    return 0;
+  return layer_bwd_ws(jag, desc, w->d_model, dtype, w->ln_output != 0).total;
+}
+
+hstu_status_t hstu_layer_bwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, const hstu_layer_weights_t *w,
+                             hstu_dtype_t dtype, hstu_dtype_t x_dtype, const void *x, hstu_dtype_t grad_dtype,
+                             const void *dy, void *dx, const hstu_layer_grads_t *grads, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  try {
+    hstu_status_t st = check_jagged_desc(jag, desc);
+    if (st != HSTU_OK) return st;
+    if (!w) return fail(HSTU_ERR_INVALID_ARGUMENT, "weights is NULL");
+    if (!grads) return fail(HSTU_ERR_INVALID_ARGUMENT, "grads is NULL");
+    if (!valid_dtype(dtype)) return fail(HSTU_ERR_INVALID_ARGUMENT, "dtype = %d invalid", (int)dtype);
+    if (!valid_dtype(x_dtype) || (x_dtype != dtype && x_dtype != HSTU_F32))
+      return fail(HSTU_ERR_UNSUPPORTED, "x_dtype = %d must be HSTU_F32 or dtype", (int)x_dtype);
+    if (!valid_dtype(grad_dtype) || (grad_dtype != dtype && grad_dtype != HSTU_F32))
+      return fail(HSTU_ERR_UNSUPPORTED, "grad_dtype = %d must be HSTU_F32 or dtype", (int)grad_dtype);
+    const int64_t T = jag->total_tokens;
+    const int64_t D = w->d_model;
+    const int64_t H = desc->num_heads, HD = H * desc->head_dim;
+    if (D < 1 || D % 8 != 0 || D > 4096)
+      return fail(HSTU_ERR_UNSUPPORTED, "d_model = %lld must be a multiple of 8 in [8, 4096]", (long long)D);
+    if (!(w->ln_eps > 0.0f)) return fail(HSTU_ERR_INVALID_ARGUMENT, "ln_eps must be > 0");
+    if (!w->w_uvqk || !w->w_out) return fail(HSTU_ERR_INVALID_ARGUMENT, "w_uvqk/w_out is NULL");
+    if (!aligned16(w->w_uvqk) || !aligned16(w->w_out))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "weights must be 16-byte aligned");
+    if (!grads->d_w_uvqk || !grads->d_w_out || !grads->d_pos_bias || !grads->d_time_bias)
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "d_w_uvqk/d_w_out/d_pos_bias/d_time_bias is NULL");
+    if (!aligned16(grads->d_w_uvqk) || !aligned16(grads->d_w_out))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "d_w_uvqk/d_w_out must be 16-byte aligned");
+    const int ityp = dtype == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
+    const size_t lds = std::max(hstu::attn_bwd_dq_lds_bytes(ityp, desc->head_dim, desc->num_pos_buckets),
+                                hstu::attn_bwd_dkdv_lds_bytes(ityp, desc->head_dim, desc->num_pos_buckets));
+    if (lds > 160 * 1024)
+      return fail(HSTU_ERR_UNSUPPORTED, "num_pos_buckets = %d needs %zu bytes of LDS in the backward (160 KB max)",
+                  desc->num_pos_buckets, lds);
+    const bool ln_out = w->ln_output != 0;
+    const LayerBwdWs ws = layer_bwd_ws(jag, desc, D, dtype, ln_out);
+    if (workspace_bytes < ws.total)
+      return fail(HSTU_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, ws.total);
+    if (!workspace) return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if (!aligned16(workspace)) return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    if (T > 0) {
+      if (!x || !dy || !dx) return fail(HSTU_ERR_INVALID_ARGUMENT, "x/dy/dx is NULL");
+      if (!aligned16(x) || !aligned16(dy) || !aligned16(dx))
+        return fail(HSTU_ERR_INVALID_ARGUMENT, "x/dy/dx must be 16-byte aligned");
+    }
+    const size_t R = desc->rab_rows, P = desc->num_pos_buckets, Tb = desc->num_time_buckets, es = esize(dtype);
+    const size_t nx = (size_t)T * D * esize(x_dtype), ng = (size_t)T * D * esize(grad_dtype);
+    const void *ins[8] = {x, dy, w->w_uvqk, w->b_uvqk, w->w_out, w->b_out, desc->pos_bias, desc->time_bias};
+    const size_t in_n[8] = {nx, ng, (size_t)4 * HD * D * es, (size_t)4 * HD * es, (size_t)D * HD * es, (size_t)D * es,
+                            R * P * 4, R * Tb * 4};
+    const void *outs[8] = {dx, grads->d_w_uvqk, grads->d_b_uvqk, grads->d_w_out, grads->d_b_out, grads->d_pos_bias,
+                           grads->d_time_bias, workspace};
+    const size_t out_n[8] = {ng, (size_t)4 * HD * D * 4, (size_t)4 * HD * 4, (size_t)D * HD * 4, (size_t)D * 4,
+                             R * P * 4, R * Tb * 4, ws.total};
+    for (int o = 0; o < 8; ++o) {
+      for (int i = 0; i < 8; ++i)
+        if (overlaps(outs[o], out_n[o], ins[i], in_n[i]))
+          return fail(HSTU_ERR_INVALID_ARGUMENT, "an output or the workspace overlaps an input");
+      for (int o2 = o + 1; o2 < 8; ++o2)
+        if (overlaps(outs[o], out_n[o], outs[o2], out_n[o2]))
+          return fail(HSTU_ERR_INVALID_ARGUMENT, "two outputs (or an output and the workspace) overlap");
+    }
+
+    hipStream_t s = (hipStream_t)stream;
+    char *wsb = (char *)workspace;
+    const int dt = ityp, f32w = dtype == HSTU_F32;
+    const int x_f32 = x_dtype == HSTU_F32, g_f32 = grad_dtype == HSTU_F32;
+    const bool split = dtype == HSTU_BF16 && w->act_split != 0;
+    hipError_t e;
+#define HSTU_TRY(call, what)                 \
+  do {                                       \
+    e = (call);                              \
+    if (e != hipSuccess) return from_hip(e, what); \
+  } while (0)
+
+    hstu::AttnArgs a = attn_args(jag, desc);
+    a.row_stride = HD; a.out_row_stride = HD;
+    a.in_dtype = dt;
+    a.out_dtype = hstu::kF32;
+    a.tau_stats = (int64_t *)(wsb + ws.stats);
+    if (T == 0) {
+      // no tokens: every gradient is 0 (the attention backward clears its two tables itself)
+      HSTU_TRY(hstu::launch_fill_zero(grads->d_w_uvqk, 4 * HD * D, s), "zero fill");
+      HSTU_TRY(hstu::launch_fill_zero(grads->d_b_uvqk, grads->d_b_uvqk ? 4 * HD : 0, s), "zero fill");
+      HSTU_TRY(hstu::launch_fill_zero(grads->d_w_out, D * HD, s), "zero fill");
+      HSTU_TRY(hstu::launch_fill_zero(grads->d_b_out, grads->d_b_out ? D : 0, s), "zero fill");
+      a.d_pos_bias = grads->d_pos_bias; a.d_time_bias = grads->d_time_bias;
+      HSTU_TRY(hstu::launch_attn_bwd_dq(a, s), "attention backward launch");
+      return ok();
+    }
+
+    // ---- recompute the forward
+    HSTU_TRY(hstu::launch_transpose(w->w_uvqk, f32w, wsb + ws.w1t, f32w, (int)(4 * HD), (int)D, (int)(4 * HD), s),
+             "W1 transpose");
+    HSTU_TRY(hstu::launch_transpose(w->w_out, f32w, wsb + ws.w2t, f32w, (int)D, (int)HD, (int)D, s), "W2 transpose");
+    hstu::GemmUvqkArgs g1{};
+    g1.x = x; g1.w = w->w_uvqk; g1.bias = w->b_uvqk;
+    g1.u = (float *)(wsb + ws.u); g1.v = wsb + ws.v; g1.q = wsb + ws.q; g1.k = wsb + ws.k; g1.z = wsb + ws.z;
+    g1.M = (int32_t)T; g1.K = (int32_t)D; g1.HD = (int32_t)HD;
+    g1.dtype = dt; g1.x_f32 = x_f32; g1.split = split;
+    HSTU_TRY(hstu::launch_gemm_uvqk(g1, s), "projection GEMM launch");
+    a.q = wsb + ws.q; a.k = wsb + ws.k; a.v = wsb + ws.v; a.out = wsb + ws.o;
+    a.row_stats = (float *)(wsb + ws.ostat);
+    HSTU_TRY(hstu::launch_attn_fwd(a, s), "attention launch");
+
+    // ---- dr
+    const void *dr = dy;
+    int dr_f32 = g_f32;
+    if (ln_out) {
+      hstu::GemmOutArgs g2{};
+      g2.o = (const float *)(wsb + ws.o); g2.u = (const float *)(wsb + ws.u);
+      g2.row_stats = (const float *)(wsb + ws.ostat);
+      g2.heads = (int32_t)H; g2.head_dim = desc->head_dim; g2.eps = w->ln_eps;
+      g2.w = w->w_out; g2.bias = w->b_out; g2.x = x;
+      g2.y = nullptr; g2.y32 = (float *)(wsb + ws.r32);
+      g2.M = (int32_t)T; g2.N = (int32_t)D; g2.K = (int32_t)HD;
+      g2.dtype = dt; g2.split = split; g2.x_f32 = x_f32; g2.y_f32 = 1;
+      HSTU_TRY(hstu::launch_gemm_out(g2, s), "output GEMM launch");
+      hstu::LnBwdArgs lb{};
+      lb.r = (float *)(wsb + ws.r32); lb.dy = dy; lb.M = (int32_t)T; lb.N = (int32_t)D; lb.dy_f32 = g_f32;
+      lb.eps = w->ln_eps;
+      HSTU_TRY(hstu::launch_ln_bwd_rows(lb, s), "LayerNorm backward launch");
+      dr = wsb + ws.r32;
+      dr_f32 = 1;
+    }
+
+    // ---- dg = dr W2, then the norm-gate backward (g, dO, dz_U)
+    hstu::GemmPlainArgs pg{};
+    pg.a = dr; pg.a_f32 = dr_f32; pg.b = wsb + ws.w2t; pg.c = wsb + ws.dg; pg.c_f32 = 1;
+    pg.M = (int32_t)T; pg.N = (int32_t)HD; pg.K = (int32_t)D; pg.dtype = dt; pg.splits = 1;
+    HSTU_TRY(hstu::launch_gemm_plain(pg, s), "dg GEMM launch");
+    hstu::NormGateBwdArgs nb{};
+    nb.o = (const float *)(wsb + ws.o); nb.u = (const float *)(wsb + ws.u); nb.dg = (const float *)(wsb + ws.dg);
+    nb.z = wsb + ws.z; nb.g = wsb + ws.g; nb.d_o = wsb + ws.d_o;
+    nb.M = (int32_t)T; nb.N = (int32_t)HD; nb.dtype = dt; nb.eps = w->ln_eps;
+    HSTU_TRY(hstu::launch_norm_gate_bwd(nb, s), "norm-gate backward launch");
+
+    // ---- attention backward, then dz for the V, Q, K slices
+    a.d_out = wsb + ws.d_o;
+    a.out = wsb + ws.dq; a.dk = (float *)(wsb + ws.dk); a.dv = (float *)(wsb + ws.dv);
+    a.d_pos_bias = grads->d_pos_bias; a.d_time_bias = grads->d_time_bias;
+    a.partial = (float *)(wsb + ws.bins);
+    a.row_stats = nullptr;
+    HSTU_TRY(hstu::launch_attn_bwd_dq(a, s), "attention backward dq launch");
+    HSTU_TRY(hstu::launch_attn_bwd_dkdv(a, s), "attention backward dk/dv launch");
+    HSTU_TRY(hstu::launch_silu_grad_vqk((const float *)(wsb + ws.dv), (const float *)(wsb + ws.dq),
+                                        (const float *)(wsb + ws.dk), wsb + ws.z, (int)T, (int)HD, dt, s),
+             "SiLU gradient launch");
+
+    // ---- dx = dr + dz W1
+    hstu::GemmPlainArgs px{};
+    px.a = wsb + ws.z; px.a_f32 = f32w; px.b = wsb + ws.w1t; px.resid = dr; px.resid_f32 = dr_f32;
+    px.c = dx; px.c_f32 = g_f32;
+    px.M = (int32_t)T; px.N = (int32_t)D; px.K = (int32_t)(4 * HD); px.dtype = dt; px.splits = 1;
+    HSTU_TRY(hstu::launch_gemm_plain(px, s), "dx GEMM launch");
+
+    // ---- weight and bias gradients from token-contiguous transposes
+    const int Tp = (int)ws.Tp;
+    HSTU_TRY(hstu::launch_transpose(x, x_f32, wsb + ws.xt, f32w, (int)T, (int)D, Tp, s), "x transpose");
+    HSTU_TRY(hstu::launch_transpose(dr, dr_f32, wsb + ws.drt, f32w, (int)T, (int)D, Tp, s), "dr transpose");
+    HSTU_TRY(hstu::launch_transpose(wsb + ws.g, f32w, wsb + ws.gt, f32w, (int)T, (int)HD, Tp, s), "g transpose");
+    HSTU_TRY(hstu::launch_transpose(wsb + ws.z, f32w, wsb + ws.dzt, f32w, (int)T, (int)(4 * HD), Tp, s),
+             "dz transpose");
+    hstu::GemmPlainArgs pw{};
+    pw.a = wsb + ws.dzt; pw.a_f32 = f32w; pw.b = wsb + ws.xt; pw.c = grads->d_w_uvqk; pw.c_f32 = 1;
+    pw.M = (int32_t)(4 * HD); pw.N = (int32_t)D; pw.K = Tp; pw.dtype = dt;
+    pw.splits = ws.split_w1; pw.partial = (float *)(wsb + ws.part);
+    HSTU_TRY(hstu::launch_gemm_plain(pw, s), "d_w_uvqk GEMM launch");
+    pw.a = wsb + ws.drt; pw.b = wsb + ws.gt; pw.c = grads->d_w_out;
+    pw.M = (int32_t)D; pw.N = (int32_t)HD; pw.splits = ws.split_w2;
+    HSTU_TRY(hstu::launch_gemm_plain(pw, s), "d_w_out GEMM launch");
+    if (grads->d_b_uvqk)
+      HSTU_TRY(hstu::launch_row_sum(wsb + ws.dzt, f32w, grads->d_b_uvqk, (int)(4 * HD), Tp, s), "d_b_uvqk launch");
+    if (grads->d_b_out)
+      HSTU_TRY(hstu::launch_row_sum(wsb + ws.drt, f32w, grads->d_b_out, (int)D, Tp, s), "d_b_out launch");
+#undef HSTU_TRY
+    return ok();
+  } catch (...) {
+    return fail(HSTU_ERR_DEVICE, "unexpected C++ exception in hstu_layer_bwd");
+  }
+}
+
 hstu_status_t hstu_gather_rows(const void *table, int64_t table_rows, int32_t d, hstu_dtype_t dtype,
                                const int64_t *ids, int32_t T, void *out, void *stream) {
   try {

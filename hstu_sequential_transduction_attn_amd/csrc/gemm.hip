@@ -64,8 +64,10 @@ struct GemmParams {
   const void *bias;    // [N] (TM) or null
   const void *resid;   // [M][N] residual (output epilogue), fp32 if resid_f32 else TM
   void *out0, *out1, *out2, *out3;  // projection: U (fp32), V, Q, K (TM), [M][HD]; output: y or null
-  float *out32;        // output epilogue: fp32 result (pre-LayerNorm) or null
+  void *zout;          // projection: the pre-activation x W1^T + b1, [M][N] (TM), or null
+  float *out32;        // output epilogue: fp32 result (pre-LayerNorm; per split with split-K) or null
   int M, N, K, HD;
+  int splits, kt_per_split;  // split-K (large-tile kernel only): k-tiles [s * kt_per_split, ...) per split
   int resid_f32, y_f32;
   const float *gate_u;     // fused gate: U [M][K] fp32
   const float *row_stats;  // fused gate: [M][heads][2] per-head mean and sum of squared deviations of O
@@ -258,10 +260,12 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(const GemmParams p) {
         for (int e = 0; e < 16; ++e) {
           const int m = m0 + wm + 32 * i + 8 * (e / 4) + 4 * half + (e % 4);
           if (m < p.M) {
-            const float s = silu_f32(acc[i][j][e] + bias);
+            const float z = acc[i][j][e] + bias;
+            const float s = silu_f32(z);
             const int64_t idx = (int64_t)m * p.HD + col;
             if (part == 0) ((float *)dst)[idx] = s;
             else ((TM *)dst)[idx] = from_f32<TM>(s);
+            if (p.zout) ((TM *)p.zout)[(int64_t)m * p.N + n] = from_f32<TM>(z);
           }
         }
     } else {
@@ -273,7 +277,8 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(const GemmParams p) {
         for (int e = 0; e < 16; ++e) {
           const int m = imin(m0 + wm + 32 * i + 8 * (e / 4) + 4 * half + (e % 4), p.M - 1);
           const int64_t idx = (int64_t)m * p.N + n;
-          r[e] = p.resid_f32 ? ((const float *)p.resid)[idx] : to_f32(((const TM *)p.resid)[idx]);
+          if (!p.resid) r[e] = 0.0f;
+          else r[e] = p.resid_f32 ? ((const float *)p.resid)[idx] : to_f32(((const TM *)p.resid)[idx]);
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -361,6 +366,13 @@ __device__ __forceinline__ u32x4 residual_bf16x8(floatx4 x0, floatx4 x1, u32x4 h
   return to_bf16x8(r0, r1);
 }
 
+// A workgroup-uniform pointer, moved into scalar registers
+__device__ __forceinline__ const char *uniform_ptr(const char *p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 template <class C, int EPI>
 __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
@@ -369,10 +381,13 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, FM = C::FM, FN = C::FN;
 
   // ---- tile: XCD-contiguous ranges, groups of GM row blocks, row block fastest inside a group
-  const int nN = (p.N + BN - 1) / BN, nM = (p.M + BM - 1) / BM, total = nN * nM;
+  const int nN = (p.N + BN - 1) / BN, nM = (p.M + BM - 1) / BM, tiles = nN * nM, total = tiles * p.splits;
   const int per = (total + 7) / 8;
-  const int w = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  if (w >= total) return;
+  const int ws = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (ws >= total) return;
+  const int split = ws / tiles, w = ws % tiles;      // split-K: each split is a full set of tiles
+  const int kt0 = split * p.kt_per_split;
+  float *const out32 = p.out32 ? p.out32 + (int64_t)split * p.M * p.N : nullptr;
   const int grp = w / (C::GM * nN), gi = w % (C::GM * nN);
   const int gm = imin(C::GM, nM - grp * C::GM);
   const int m0 = (grp * C::GM + gi % gm) * BM, n0 = (gi / gm) * BN;
@@ -397,9 +412,10 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
     const int q = wave + t * C::kWaves, g = q / (BN / 16), r = (q % (BN / 16)) * 16 + lrow;
     boff[t] = (uint32_t)imin(r, b_rows - 1) * b_rb + (uint32_t)g * 64u + lpiece;
   }
-  const char *abase = (const char *)p.a + (int64_t)m0 * a_rb;
-  const char *ubase = (const char *)p.gate_u + (int64_t)m0 * a_rb;
-  const char *bbase = (const char *)p.b + (int64_t)n0 * b_rb;
+  // workgroup-uniform operand bases (scalar registers: the direct-to-LDS loads take them as SGPR pairs)
+  const char *abase = uniform_ptr((const char *)p.a + (int64_t)m0 * a_rb + (int64_t)kt0 * BK * C::kEA);
+  const char *ubase = uniform_ptr((const char *)p.gate_u + (int64_t)m0 * a_rb + (int64_t)kt0 * BK * 4);
+  const char *bbase = uniform_ptr((const char *)p.b + (int64_t)n0 * b_rb + (int64_t)kt0 * BK * 2);
 
   auto issue = [&](int kt, int slot) {
     const uint32_t st = smem_addr + (uint32_t)(slot * C::kStage);
@@ -490,7 +506,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
   };
 
   // ---- k loop over an S-stage ring
-  const int nk = p.K / BK;
+  const int nk = imax(imin(p.K / BK - kt0, p.kt_per_split), 0);
   constexpr int kAhead = C::S - 1;
   for (int t = 0; t < kAhead; ++t)
     if (t < nk) issue(t, t);
@@ -526,10 +542,12 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
         for (int e = 0; e < 16; ++e) {
           const int m = m0 + wm + 32 * i + 8 * (e / 4) + 4 * half + (e % 4);
           if (m < p.M) {
-            const float s = silu_f32(acc[i][j][e] + bias);
+            const float z = acc[i][j][e] + bias;
+            const float s = silu_f32(z);
             const int64_t idx = (int64_t)m * p.HD + col;
             if (part == 0) ((float *)dst)[idx] = s;
             else ((__bf16 *)dst)[idx] = f32_to_bf16(s);
+            if (p.zout) ((__bf16 *)p.zout)[(int64_t)m * p.N + n] = f32_to_bf16(z);
           }
         }
     } else {
@@ -541,7 +559,8 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
         for (int e = 0; e < 16; ++e) {
           const int m = imin(m0 + wm + 32 * i + 8 * (e / 4) + 4 * half + (e % 4), p.M - 1);
           const int64_t idx = (int64_t)m * p.N + n;
-          r[e] = p.resid_f32 ? ((const float *)p.resid)[idx] : to_f32(((const __bf16 *)p.resid)[idx]);
+          if (!p.resid) r[e] = 0.0f;
+          else r[e] = p.resid_f32 ? ((const float *)p.resid)[idx] : to_f32(((const __bf16 *)p.resid)[idx]);
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -549,7 +568,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
           if (m < p.M) {
             const int64_t idx = (int64_t)m * p.N + n;
             const float y = acc[i][j][e] + bias + r[e];
-            if (p.out32) p.out32[idx] = y;
+            if (out32) out32[idx] = y;
             else if (p.y_f32) ((float *)p.out0)[idx] = y;
             else ((__bf16 *)p.out0)[idx] = f32_to_bf16(y);
           }
@@ -560,8 +579,8 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
 }
 
 template <class C, int EPI>
-hipError_t launch_big(const GemmParams &p, hipStream_t s) {
-  if (p.M == 0 || p.N == 0) return hipSuccess;
+hipError_t launch_big(const GemmParams &p0, hipStream_t s) {
+  if (p0.M == 0 || p0.N == 0) return hipSuccess;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void *)gemm_big_kernel<C, EPI>,
@@ -569,9 +588,30 @@ hipError_t launch_big(const GemmParams &p, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const long long nt = (long long)((p.N + C::BN - 1) / C::BN) * ((p.M + C::BM - 1) / C::BM);
+  GemmParams p = p0;
+  p.splits = p.splits > 1 ? p.splits : 1;
+  const int nkt = p.K / C::BK;
+  p.kt_per_split = (nkt + p.splits - 1) / p.splits;
+  const long long nt = (long long)((p.N + C::BN - 1) / C::BN) * ((p.M + C::BM - 1) / C::BM) * p.splits;
   hipLaunchKernelGGL((gemm_big_kernel<C, EPI>), dim3((unsigned)((nt + 7) / 8 * 8)), dim3(C::kThreads), C::kLds, s, p);
   return hipGetLastError();
+}
+
+// out[i] = sum over s of part[s][i], s in increasing order (deterministic split-K reduction)
+__global__ void __launch_bounds__(256) split_sum_kernel(const float *__restrict__ part, float *__restrict__ out,
+                                                        int64_t n, int splits) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (4 * i + 3 < n) {
+    floatx4 acc = *(const floatx4 *)(part + 4 * i);
+    for (int sp = 1; sp < splits; ++sp) acc += *(const floatx4 *)(part + (int64_t)sp * n + 4 * i);
+    *(floatx4 *)(out + 4 * i) = acc;
+  } else {
+    for (int64_t j = 4 * i; j < n; ++j) {
+      float acc = part[j];
+      for (int sp = 1; sp < splits; ++sp) acc += part[(int64_t)sp * n + j];
+      out[j] = acc;
+    }
+  }
 }
 
 template <typename TM, typename TA, int SPLIT, int EPI, bool GATE>
@@ -590,11 +630,17 @@ using CfgF32Split = BigCfg<128, 256, 32, 2, 2, 2, kAkF32, 2, 8, 2>;
 using CfgGate = BigCfg<64, 256, 32, 2, 2, 2, kAkGate, 1, 4, 2>;
 using CfgGateSplit = BigCfg<64, 256, 32, 2, 2, 2, kAkGate, 2, 4, 2>;
 
-// The large-tile kernel needs K to be a whole number of k-tiles and enough tiles to fill the chip.
+// The large-tile kernel needs K to be a whole number of k-tiles, per-lane source offsets (row within
+// the tile times the row's bytes) that fit 32 bits, and enough tiles to fill the chip.
+template <class C>
+bool offsets_fit(int64_t K) {
+  const int64_t rows = C::BM > C::BN ? C::BM : C::BN;
+  return K * 4 * rows < (int64_t(1) << 32);
+}
 template <class C>
 bool big_fits(const GemmParams &p) {
   const long long tiles = (long long)((p.N + C::BN - 1) / C::BN) * ((p.M + C::BM - 1) / C::BM);
-  return p.K % C::BK == 0 && tiles >= 256;
+  return p.K % C::BK == 0 && tiles >= 256 && offsets_fit<C>(p.K);
 }
 
 template <int EPI, bool GATE>
@@ -619,8 +665,9 @@ hipError_t dispatch(const GemmParams &p, int dtype, int a_f32, int split, hipStr
 hipError_t launch_gemm_uvqk(const GemmUvqkArgs &a, hipStream_t s) {
   GemmParams p{};
   p.a = a.x; p.b = a.w; p.bias = a.bias; p.resid = nullptr;
-  p.out0 = a.u; p.out1 = a.v; p.out2 = a.q; p.out3 = a.k; p.out32 = nullptr;
+  p.out0 = a.u; p.out1 = a.v; p.out2 = a.q; p.out3 = a.k; p.out32 = nullptr; p.zout = a.z;
   p.M = a.M; p.N = 4 * a.HD; p.K = a.K; p.HD = a.HD;
+  p.splits = 1;
   return dispatch<kEpiUvqk, false>(p, a.dtype, a.x_f32, a.split, s);
 }
 
@@ -631,7 +678,43 @@ hipError_t launch_gemm_out(const GemmOutArgs &a, hipStream_t s) {
   p.M = a.M; p.N = a.N; p.K = a.K; p.HD = 0;
   p.resid_f32 = a.x_f32; p.y_f32 = a.y_f32;
   p.gate_u = a.u; p.row_stats = a.row_stats; p.heads = a.heads; p.head_dim = a.head_dim; p.eps = a.eps;
+  p.splits = 1;
   return dispatch<kEpiOut, true>(p, a.dtype, 1, a.split, s);
+}
+
+int gemm_plain_splits(int64_t M, int64_t N, int64_t K, int dtype, int a_f32) {
+  if (dtype != kBF16 || a_f32 || K % CfgBf16::BK != 0 || M <= 0 || N <= 0 || !offsets_fit<CfgBf16>(K)) return 1;
+  const int64_t tiles = ((N + CfgBf16::BN - 1) / CfgBf16::BN) * ((M + CfgBf16::BM - 1) / CfgBf16::BM);
+  if (tiles >= 512) return 1;
+  const int64_t by_fill = (1024 + tiles - 1) / tiles;     // about four workgroups per CU
+  const int64_t by_depth = K / CfgBf16::BK / 16;           // at least 16 k-tiles per split
+  const int64_t sp = by_fill < by_depth ? by_fill : by_depth;
+  return sp > 1 ? (int)(sp < 64 ? sp : 64) : 1;
+}
+
+hipError_t launch_gemm_plain(const GemmPlainArgs &a, hipStream_t s) {
+  GemmParams p{};
+  p.a = a.a; p.b = a.b; p.bias = nullptr; p.resid = a.resid;
+  p.out0 = a.c; p.out1 = p.out2 = p.out3 = nullptr;
+  p.M = a.M; p.N = a.N; p.K = a.K; p.HD = 0;
+  p.resid_f32 = a.resid_f32; p.y_f32 = a.c_f32;
+  p.splits = 1;
+  if (a.splits > 1) {
+    // split-K: fp32 partial products per split, then a fixed-order sum into c
+    if (a.dtype != kBF16 || a.a_f32 || a.resid || !a.c_f32 || !a.partial || a.K % CfgBf16::BK != 0 ||
+        !offsets_fit<CfgBf16>(a.K) || ((int64_t)a.M * a.N) % 4 != 0)
+      return hipErrorInvalidValue;
+    if (a.M == 0 || a.N == 0) return hipSuccess;
+    p.splits = a.splits;
+    p.out32 = a.partial;
+    hipError_t e = launch_big<CfgBf16, kEpiOut>(p, s);
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)a.M * a.N;
+    hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, a.partial,
+                       (float *)a.c, n, a.splits);
+    return hipGetLastError();
+  }
+  return dispatch<kEpiOut, false>(p, a.dtype, a.a_f32, 0, s);
 }
 
 }  // namespace hstu

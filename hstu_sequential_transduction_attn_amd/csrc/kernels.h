@@ -81,6 +81,7 @@ struct GemmUvqkArgs {
   const void *bias;               // [4*HD] dtype or null
   float *u;                       // [M][HD] fp32
   void *v, *q, *k;                // each [M][HD] dtype
+  void *z;                        // [M][4*HD] dtype: the pre-activation x W1^T + b1, or null
   int32_t M, K, HD;
   int32_t dtype, x_f32, split;
 };
@@ -115,6 +116,49 @@ struct RowLnArgs {
   int32_t out_f32;
 };
 hipError_t launch_row_layernorm(const RowLnArgs &a, hipStream_t stream);
+
+// Plain product c = A B^T (+ resid), A [M][K] (fp32 if a_f32 else dtype), B [N][K] dtype, c fp32 if c_f32
+// else dtype, resid [M][N] (fp32 if resid_f32 else dtype) or null.  splits > 1 (bf16 A and B, K a
+// multiple of 32, no resid, fp32 c): K is cut into `splits` ranges whose fp32 products go to
+// partial [splits][M][N] and are then summed in split order.
+struct GemmPlainArgs {
+  const void *a, *b, *resid;
+  void *c;
+  float *partial;
+  int32_t M, N, K, dtype, a_f32, resid_f32, c_f32, splits;
+};
+hipError_t launch_gemm_plain(const GemmPlainArgs &a, hipStream_t stream);
+int gemm_plain_splits(int64_t M, int64_t N, int64_t K, int dtype, int a_f32);
+
+// ---- layer backward, HBM-bound pieces
+// dr = LN'(r) dy in place over r: r fp32 [M][N] (the pre-LayerNorm sum), dy [M][N] fp32 if dy_f32 else bf16.
+struct LnBwdArgs {
+  float *r;
+  const void *dy;
+  int32_t M, N, dy_f32;
+  float eps;
+};
+hipError_t launch_ln_bwd_rows(const LnBwdArgs &a, hipStream_t stream);
+
+// Norm-gate backward: o, u, dg fp32 [M][N]; z dtype [M][4N] (its U slice becomes dz_U); g, d_o dtype [M][N].
+struct NormGateBwdArgs {
+  const float *o, *u, *dg;
+  void *z, *g, *d_o;
+  int32_t M, N, dtype;
+  float eps;
+};
+hipError_t launch_norm_gate_bwd(const NormGateBwdArgs &a, hipStream_t stream);
+
+// z[:, N:4N] <- [dv | dq | dk] * SiLU'(z[:, N:4N]) (dv, dq, dk fp32 [M][N]; z dtype [M][4N]; N % 4 == 0).
+hipError_t launch_silu_grad_vqk(const float *dv, const float *dq, const float *dk, void *z, int M, int N, int dtype,
+                                hipStream_t stream);
+// dst [C][Rp] = src[R][C]^T with rows R..Rp-1 zero (C % 4 == 0, Rp % 4 == 0, Rp >= R).
+hipError_t launch_transpose(const void *src, int src_f32, void *dst, int dst_f32, int R, int C, int Rp,
+                            hipStream_t stream);
+// out[c] = sum of row c of src [rows][Rp] (Rp % 4 == 0), fixed summation order.
+hipError_t launch_row_sum(const void *src, int src_f32, float *out, int rows, int Rp, hipStream_t stream);
+// p[0..n) = 0 (a kernel, not a memset, so that a captured graph replays it faithfully).
+hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t stream);
 
 hipError_t launch_gather_rows(const void *table, int64_t table_rows, int32_t row_bytes, const int64_t *ids,
                               int32_t T, void *out, hipStream_t stream);

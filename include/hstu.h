@@ -1,5 +1,6 @@
 /*
- * hstu.h -- C ABI of libhstu, the MI355X (gfx950) HSTU layer forward.
+ * hstu.h -- C ABI of libhstu, the MI355X (gfx950) HSTU layer: forward, cached-history candidate
+ * scoring, and the backward of the attention and of the whole layer.
  *
  * What it computes.  The HSTU layer as the pages describe it: "DLRMv4：MLPerfの推薦システム訓練
  * ベンチマークがシーケンス化時代へ", section "モデルアーキテクチャ：HSTUが従来の特徴インタラクション
@@ -49,7 +50,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 3
+#define HSTU_ABI_VERSION 4
 
 typedef enum {
   HSTU_OK = 0,
@@ -220,6 +221,46 @@ hstu_status_t hstu_layer_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
                              const hstu_layer_weights_t *w, hstu_dtype_t dtype, hstu_dtype_t x_dtype,
                              const void *x, hstu_dtype_t y_dtype, void *y, void *workspace,
                              size_t workspace_bytes, void *stream);
+
+/* Gradients of one layer's parameters: fp32 (device), written, not accumulated into. */
+typedef struct {
+  float *d_w_uvqk;               /* [4*H*Dh][D]                                                   */
+  float *d_b_uvqk;               /* [4*H*Dh], or NULL: not computed                               */
+  float *d_w_out;                /* [D][H*Dh]                                                     */
+  float *d_b_out;                /* [D], or NULL: not computed                                    */
+  float *d_pos_bias;             /* [R][P]                                                        */
+  float *d_time_bias;            /* [R][Tb]                                                       */
+} hstu_layer_grads_t;
+
+/* Workspace needed by hstu_layer_bwd (bytes).  Depends only on host fields. */
+size_t hstu_layer_bwd_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc,
+                                      const hstu_layer_weights_t *w, hstu_dtype_t dtype);
+
+/*
+ * Backward of hstu_layer_fwd (the layer is trained: "DLRMv4" page, the benchmark is a training
+ * benchmark; the layer is the one of its section on the model architecture).  For an upstream
+ * gradient dy of y, with r = x + W2 g + b2 (y = LN(r) when ln_output, else y = r), g = LN(o) * U,
+ * o = concat_h O and z = W1 x + b1 (U|V|Q|K = SiLU(z)):
+ *   dr = LN'(r) dy (or dy);  d_b_out = sum_t dr;  d_w_out = dr^T g;  dg = dr W2
+ *   dU = dg * LN(o);  do = LN'(o) (dg * U);  dQ, dK, dV and the bias-table gradients as hstu_attn_bwd
+ *   dz = [dU | dV | dQ | dK] * SiLU'(z);  d_b_uvqk = sum_t dz;  d_w_uvqk = dz^T x;  dx = dr + dz W1
+ * where LN'(a) b = rstd (b - mean(b) - a_hat mean(b * a_hat)) applies the LayerNorm Jacobian.
+ * Nothing is saved from the forward: the call recomputes z, U, V, Q, K, O and g from x (in
+ * the forward's numerics, act_split included) and keeps them in the workspace.
+ * dtype, x_dtype, x, w, jag, desc: exactly as given to hstu_layer_fwd.
+ * dy, dx: [T][D] (device), element type grad_dtype in {HSTU_F32, dtype}; dx may not overlap an input.
+ * grads: d_w_uvqk, d_w_out, d_pos_bias, d_time_bias required; the bias gradients may be NULL.
+ * bf16: every product runs on bf16 MFMA with fp32 accumulation (its operands rounded to bf16:
+ * z, dz, g, dO and the transposed dr and x); the weight gradients are sums over all T tokens, split
+ * over workgroups and added in a fixed order.  The result is bitwise deterministic.
+ * Errors: as hstu_layer_fwd and hstu_attn_bwd; a NULL required gradient pointer or any overlap of an
+ * output with an input, another output or the workspace is HSTU_ERR_INVALID_ARGUMENT.
+ */
+hstu_status_t hstu_layer_bwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc,
+                             const hstu_layer_weights_t *w, hstu_dtype_t dtype, hstu_dtype_t x_dtype,
+                             const void *x, hstu_dtype_t grad_dtype, const void *dy, void *dx,
+                             const hstu_layer_grads_t *grads, void *workspace, size_t workspace_bytes,
+                             void *stream);
 
 /*
  * Embedding gather (input staging before the first layer):  out[t][:] = table[ids[t]][:].

@@ -191,10 +191,12 @@ def silu_grad(z: np.ndarray) -> np.ndarray:
     return sig * (1.0 + z * (1.0 - sig))
 
 
-def attn_bwd(jag: dict, q, k, v, pos_bias, time_bias, d_out):
+def attn_bwd(jag: dict, q, k, v, pos_bias, time_bias, d_out, return_sq=False):
     """Gradients of the pointwise attention (the forward of attn_fwd) for an upstream gradient d_out.
 
-    Returns (dq, dk, dv, d_pos_bias, d_time_bias) in float64: [T, H, Dh] x 3, [R, P], [R, Tb].
+    Returns (dq, dk, dv, d_pos_bias, d_time_bias) in float64: [T, H, Dh] x 3, [R, P], [R, Tb]; with
+    return_sq also the per-bin sums of squares of the summed terms, sum of dS_ij^2 ([R, P] and
+    [R, Tb]): the scale of a bin's rounding noise when each term carries an independent error.
     With a_ij = SiLU(s_ij) on allowed pairs and O_i = c_b sum_j a_ij v_j:
         dv_j = c_b sum_i a_ij dO_i,   dA_ij = c_b dO_i . v_j,   dS_ij = dA_ij SiLU'(s_ij) (allowed pairs),
         dq_i = sum_j dS_ij k_j,   dk_j = sum_i dS_ij q_i,
@@ -210,6 +212,7 @@ def attn_bwd(jag: dict, q, k, v, pos_bias, time_bias, d_out):
     R, P, Tb = wp.shape[0], wp.shape[1], wt.shape[1]
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     dwp, dwt = np.zeros_like(wp), np.zeros_like(wt)
+    sqp, sqt = np.zeros_like(wp), np.zeros_like(wt)
     B = len(jag["seq_offsets"]) - 1
     for b in range(B):
         o0, o1, n, n_hist, mask, scale = _seq_params(jag, b)
@@ -230,6 +233,11 @@ def attn_bwd(jag: dict, q, k, v, pos_bias, time_bias, d_out):
             dk[o0:o1, h] = ds.T @ qh
             dwp[r] += np.bincount(bp[ok], weights=ds[ok], minlength=P)
             dwt[r] += np.bincount(bt[ok], weights=ds[ok], minlength=Tb)
+            if return_sq:
+                sqp[r] += np.bincount(bp[ok], weights=ds[ok] ** 2, minlength=P)
+                sqt[r] += np.bincount(bt[ok], weights=ds[ok] ** 2, minlength=Tb)
+    if return_sq:
+        return dq, dk, dv, dwp, dwt, sqp, sqt
     return dq, dk, dv, dwp, dwt
 
 
@@ -331,11 +339,12 @@ def layer_norm_bwd(x, eps, dy):
 
 
 def layer_bwd(x, jag, w_uvqk, b_uvqk, w_out, b_out, pos_bias, time_bias, num_heads, head_dim,
-              ln_eps, ln_output, dy):
+              ln_eps, ln_output, dy, return_sq=False):
     """Gradients of layer_fwd for an upstream gradient dy of its output y (the layer is trained:
     [DLRMv4] describes a training benchmark).  Returns a dict of float64 arrays:
         dx [T, D], d_w_uvqk [4*H*Dh, D], d_b_uvqk [4*H*Dh], d_w_out [D, H*Dh], d_b_out [D],
-        d_pos_bias [R, P], d_time_bias [R, Tb].
+        d_pos_bias [R, P], d_time_bias [R, Tb]
+    (with return_sq also d_pos_bias_sq, d_time_bias_sq: attn_bwd's per-bin sums of squares).
     The chain, from the output back (r = x + g W2^T + b2 is the pre-LayerNorm sum, g = LN(o) * U):
         dr = layer_norm_bwd(r, dy) if ln_output else dy
         d_b_out = sum_t dr;  d_w_out = dr^T g;  dg = dr W2
@@ -371,11 +380,15 @@ def layer_bwd(x, jag, w_uvqk, b_uvqk, w_out, b_out, pos_bias, time_bias, num_hea
     dg = dr @ w2
     du = dg * on
     do = layer_norm_bwd(o, ln_eps, dg * uf)
-    dq, dk, dv, dwp, dwt = attn_bwd(jag, q, k, v, pos_bias, time_bias, do.reshape(T, num_heads, head_dim))
+    res = attn_bwd(jag, q, k, v, pos_bias, time_bias, do.reshape(T, num_heads, head_dim), return_sq=return_sq)
+    dq, dk, dv, dwp, dwt = res[:5]
     ds = np.concatenate([du, dv.reshape(T, hd), dq.reshape(T, hd), dk.reshape(T, hd)], axis=1)
     dz = ds * silu_grad(z)
-    return dict(dx=dr + dz @ w1, d_w_uvqk=dz.T @ x, d_b_uvqk=dz.sum(axis=0), d_w_out=d_w_out,
-                d_b_out=d_b_out, d_pos_bias=dwp, d_time_bias=dwt)
+    out = dict(dx=dr + dz @ w1, d_w_uvqk=dz.T @ x, d_b_uvqk=dz.sum(axis=0), d_w_out=d_w_out,
+               d_b_out=d_b_out, d_pos_bias=dwp, d_time_bias=dwt)
+    if return_sq:
+        out.update(d_pos_bias_sq=res[5], d_time_bias_sq=res[6])
+    return out
 
 
 def stack_fwd(x, jag, layers, num_heads, head_dim):

@@ -39,7 +39,7 @@ def _attn(jag, desc, in_dt=L.HSTU_BF16, out_dt=L.HSTU_BF16, q=P16 + 0x10000, k=P
 
 def test_exports_every_declared_symbol():
     names = L.exported_functions_in_header()
-    assert len(names) == 12
+    assert len(names) == 14
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib()
-    assert lib.hstu_abi_version() == 3
+    assert lib.hstu_abi_version() == 4
     assert lib.hstu_status_string(OK) == b"HSTU_OK"
     assert lib.hstu_status_string(WS_SMALL) == b"HSTU_ERR_WORKSPACE_TOO_SMALL"
     assert lib.hstu_status_string(99) == b"HSTU_STATUS_UNKNOWN"
@@ -250,3 +250,64 @@ def test_bwd_workspace_holds_bins_per_workgroup():
     assert n >= workgroups * (256 + 65) * 4 and n % 256 == 0
     assert lib.hstu_attn_bwd_workspace_bytes(ctypes.byref(_jag(B=2, T=0, max_len=0)), ctypes.byref(desc),
                                              L.HSTU_BF16) == 0
+
+
+def _layer_bwd(jag, desc, w, grads, dt=L.HSTU_BF16, x_dt=L.HSTU_BF16, x=P16 + 0x100000, g_dt=L.HSTU_BF16,
+               dy=P16 + 0x200000, dx=P16 + 0x300000, ws=P16 + 0x10000000, nws=1 << 40):
+    lib = _lib()
+    st = lib.hstu_layer_bwd(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w) if w else None, dt, x_dt, x, g_dt,
+                            dy, dx, ctypes.byref(grads) if grads else None, ws, nws, None)
+    return st, lib.hstu_last_error().decode()
+
+
+def test_layer_bwd_argument_errors():
+    jag, desc = _jag(B=2, T=100, max_len=60), _desc(H=2, Dh=64, P=32, Tb=32)
+    good_w = dict(d_model=256, w_uvqk=P16 + 0x400000, b_uvqk=None, w_out=P16 + 0x500000, b_out=None, ln_eps=1e-6,
+                  ln_output=0, act_split=0)
+    good_g = dict(d_w_uvqk=P16 + 0x600000, d_b_uvqk=None, d_w_out=P16 + 0x700000, d_b_out=None,
+                  d_pos_bias=P16 + 0x800000, d_time_bias=P16 + 0x810000)
+    w = lambda **kw: L.LayerWeightsT(**{**good_w, **kw})
+    g = lambda **kw: L.LayerGradsT(**{**good_g, **kw})
+    assert _layer_bwd(jag, desc, None, g())[0] == INVALID
+    st, msg = _layer_bwd(jag, desc, w(), None)
+    assert st == INVALID and "grads" in msg
+    st, msg = _layer_bwd(jag, desc, w(), g(d_w_out=None))
+    assert st == INVALID and "d_w_out" in msg
+    assert _layer_bwd(jag, desc, w(), g(d_time_bias=None))[0] == INVALID
+    st, msg = _layer_bwd(jag, desc, w(), g(d_w_uvqk=P16 + 0x600008))
+    assert st == INVALID and "aligned" in msg
+    assert _layer_bwd(jag, desc, w(d_model=20), g())[0] == UNSUPPORTED
+    assert _layer_bwd(jag, desc, w(ln_eps=-1.0), g())[0] == INVALID
+    assert _layer_bwd(jag, desc, w(), g(), dt=L.HSTU_F32, x_dt=L.HSTU_BF16)[0] == UNSUPPORTED
+    assert _layer_bwd(jag, desc, w(), g(), dt=L.HSTU_F32, x_dt=L.HSTU_F32, g_dt=L.HSTU_BF16)[0] == UNSUPPORTED
+    st, msg = _layer_bwd(jag, desc, w(), g(), dx=None)
+    assert st == INVALID and "NULL" in msg
+    st, msg = _layer_bwd(jag, desc, w(), g(), dx=P16 + 0x100000 + 64)             # dx on top of x
+    assert st == INVALID and "overlaps" in msg
+    st, msg = _layer_bwd(jag, desc, w(), g(d_w_out=P16 + 0x600000 + 256))         # two weight gradients overlap
+    assert st == INVALID and "overlap" in msg
+    st, msg = _layer_bwd(jag, desc, w(), g(d_pos_bias=P16 + 0x3000))               # gradient on the bias table
+    assert st == INVALID and "overlaps" in msg
+    st, msg = _layer_bwd(jag, _desc(H=2, Dh=128, P=4096, Tb=64), w(), g(), dt=L.HSTU_F32, x_dt=L.HSTU_F32,
+                         g_dt=L.HSTU_F32)
+    assert st == UNSUPPORTED and "LDS" in msg
+
+
+def test_layer_bwd_workspace_sizing():
+    lib = _lib()
+    desc = _desc(H=2, Dh=64, P=32, Tb=32)
+    jag = _jag(B=2, T=100, max_len=60)
+    w = L.LayerWeightsT(256, P16, None, P16, None, 1e-6, 0, 0)
+    w_ln = L.LayerWeightsT(256, P16, None, P16, None, 1e-6, 1, 0)
+    g = L.LayerGradsT(P16 + 0x600000, None, P16 + 0x700000, None, P16 + 0x800000, P16 + 0x810000)
+    need = lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), L.HSTU_BF16)
+    need_ln = lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w_ln),
+                                                 L.HSTU_BF16)
+    assert need > 0 and need % 256 == 0
+    assert need_ln >= need + 100 * 256 * 4      # the pre-LayerNorm sum r (fp32) is kept only with ln_output
+    # every [T, 4*H*Dh] activation is at least there: the projection's pre-activation and its transpose
+    assert need >= 2 * 100 * 4 * 128 * 2
+    st, msg = _layer_bwd(jag, desc, w, g, nws=need - 1)
+    assert st == WS_SMALL and str(need) in msg
+    f32 = lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), L.HSTU_F32)
+    assert f32 > need

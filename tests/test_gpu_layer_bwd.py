@@ -1,0 +1,164 @@
+"""GPU parity of hstu_layer_bwd (the whole layer's backward) against the float64 oracle gradients.
+
+The oracle's layer gradients are pinned to finite differences of the forward oracle
+(test_oracle_layer_backward).  Cases: fp32 and bf16, with and without the post-layer LayerNorm,
+nonzero biases, ragged batches with empty and one-token sequences, odd model widths (plain GEMM
+tails), batches large enough for the large-tile and split-K weight-gradient GEMMs, the candidate
+mask, an fp32 gradient stream with fp32 activations, an empty batch, and bitwise determinism.
+"""
+import numpy as np
+import pytest
+
+from hstu_sequential_transduction_attn_amd import inputs as I
+from oracle import hstu_oracle as O
+
+from _util import dev, host, jag_dev, max_abs, oracle_jag, rel_l2
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+NAMES = ["dx", "d_w_uvqk", "d_b_uvqk", "d_w_out", "d_b_out", "d_pos_bias", "d_time_bias"]
+
+
+def _dy(case, seed, dtype):
+    rng = np.random.default_rng(seed)
+    return I.Tensor.make(rng.standard_normal(case.x.shape).astype(np.float32), dtype)
+
+
+def _gpu(case, dy, ln_output, x_f32=False, act_split=False):
+    from hstu_sequential_transduction_attn_amd import _lib as ops
+    jd = jag_dev(case.jagged)
+    L = case.layers[0]
+    x = dev(case.x) if not x_f32 else torch.from_numpy(case.x.values.copy()).cuda()
+    out = ops.layer_bwd(x, dev(dy), jd["seq_offsets"], jd["timestamps"], dev(L.w_uvqk), dev(L.w_out),
+                        dev(L.rab.pos_bias), dev(L.rab.time_bias), case.num_heads, case.head_dim,
+                        max_seq_len=jd["max_seq_len"], b_uvqk=None if L.b_uvqk is None else dev(L.b_uvqk),
+                        b_out=None if L.b_out is None else dev(L.b_out), ln_eps=L.ln_eps, ln_output=ln_output,
+                        mask=jd["mask"], num_candidates=jd["num_candidates"], attn_scale=jd["attn_scale"],
+                        act_split=act_split)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in out.items()}
+
+
+def _oracle(case, dy, ln_output):
+    L = case.layers[0]
+    return O.layer_bwd(case.x.values, oracle_jag(case.jagged), L.w_uvqk.values,
+                       None if L.b_uvqk is None else L.b_uvqk.values, L.w_out.values,
+                       None if L.b_out is None else L.b_out.values, L.rab.pos_bias, L.rab.time_bias,
+                       case.num_heads, case.head_dim, L.ln_eps, ln_output, dy.values, return_sq=True)
+
+
+def _check(got, want, dtype, what):
+    """Norm-wise bar, as for the attention gradients: rel-L2 5e-3 (bf16) or 1e-5 (fp32) and, for bf16,
+    max-abs within 2e-2 + 2^-7 max|want| (every product's operands carry a bf16 rounding, 2^-9
+    relative, and the weight gradients are sums over all tokens).
+    The bias-table gradients sum dS over every pair of a bin, with cancellation; in the layer the
+    attention's inputs q, k, v and dO are themselves bf16 roundings of values the oracle keeps in
+    float64, so each summed term carries its own rounding error.  Their bar adds the noise of
+    independent 2^-8 relative errors per term, 2^-8 sqrt(sum of dS^2) per bin: norm-wise
+    ||err|| <= 5e-3 ||want|| + 2^-8 ||s||, elementwise |err| <= 2e-2 + 2^-7 (max|want| + s)."""
+    for name in NAMES:
+        x, y = got[name], want[name]
+        assert np.all(np.isfinite(x)), f"{what} {name}: non-finite"
+        r, m = rel_l2(x, y), max_abs(x, y)
+        print(f"  {name:12s} rel_l2={r:.3e} max_abs={m:.3e} max|want|={float(np.abs(y).max()):.3e}")
+        if dtype != "bf16":
+            assert r <= 1e-5, f"{what} {name}: rel_l2={r:.3e} max_abs={m:.3e}"
+            continue
+        ymax = float(np.abs(y).max() if y.size else 0.0)
+        if name in ("d_pos_bias", "d_time_bias"):
+            sq = np.sqrt(want[name + "_sq"])
+            err = np.abs(np.asarray(x, np.float64) - y)
+            norm_bound = 5e-3 * np.linalg.norm(y) + 2.0 ** -8 * np.linalg.norm(sq)
+            assert np.linalg.norm(err) <= norm_bound, f"{what} {name}: ||err||={np.linalg.norm(err):.3e} > {norm_bound:.3e}"
+            excess = err - (2e-2 + 2.0 ** -7 * (ymax + sq))
+            assert excess.max() <= 0, f"{what} {name}: elementwise bound exceeded by {excess.max():.3e}"
+        else:
+            bound = 2e-2 + 2.0 ** -7 * ymax
+            assert r <= 5e-3 and m <= bound, f"{what} {name}: rel_l2={r:.3e} max_abs={m:.3e} (bound {bound:.3e})"
+
+
+@pytest.mark.parametrize("ln_output", [False, True])
+def test_layer_bwd_f32_small(ln_output):
+    print(f"\n[case] layer bwd f32 small ln_output={ln_output}", flush=True)
+    case = I.jagged_layer_case("lbwd32", 1300, [5, 1, 0, 70, 128, 33], D=64, H=2, Dh=32, P=32, Tb=32, dtype="f32",
+                               bias_std=0.3)
+    dy = _dy(case, 1301, "f32")
+    _check(_gpu(case, dy, ln_output), _oracle(case, dy, ln_output), "f32", "f32 small")
+
+
+@pytest.mark.parametrize("ln_output", [False, True])
+def test_layer_bwd_bf16_ragged_odd_width(ln_output):
+    """D = 72 and H*Dh = 192: no GEMM dimension is a multiple of the large tiles."""
+    print(f"\n[case] layer bwd bf16 ragged D=72 ln_output={ln_output}", flush=True)
+    case = I.jagged_layer_case("lbwd", 1310, [1, 0, 129, 64, 200, 31], D=72, H=3, Dh=64, P=50, Tb=30, dtype="bf16",
+                               bias_std=0.3)
+    dy = _dy(case, 1311, "bf16")
+    _check(_gpu(case, dy, ln_output), _oracle(case, dy, ln_output), "bf16", "bf16 ragged")
+
+
+def test_layer_bwd_bf16_large_tiles_split_k():
+    """About 20k tokens at D = 512, H*Dh = 512: the dg and dx GEMMs take the large-tile kernel, the
+    weight gradients (K = the padded token count) are split over K."""
+    print("\n[case] layer bwd bf16 large tiles + split-K", flush=True)
+    rng = np.random.default_rng(1320)
+    lengths = [int(v) for v in rng.integers(1, 1025, size=40)]
+    case = I.jagged_layer_case("lbwdL", 1320, lengths, D=512, H=4, Dh=128, P=128, Tb=128, dtype="bf16",
+                               bias_std=0.1)
+    print(f"  T={sum(lengths)}", flush=True)
+    dy = _dy(case, 1321, "bf16")
+    _check(_gpu(case, dy, True), _oracle(case, dy, True), "bf16", "bf16 large")
+
+
+def test_layer_bwd_candidates():
+    print("\n[case] layer bwd bf16 candidates", flush=True)
+    case = I.jagged_layer_case("lbwdc", 1330, [150, 40, 300, 1], D=128, H=2, Dh=128, P=64, Tb=64, dtype="bf16",
+                               bias_std=0.2)
+    case.jagged.mask = I.CAUSAL_CANDIDATES
+    case.jagged.num_candidates = np.array([50, 1, 100, 1], np.int32)
+    dy = _dy(case, 1331, "bf16")
+    _check(_gpu(case, dy, False), _oracle(case, dy, False), "bf16", "candidates")
+
+
+@pytest.mark.parametrize("act_split", [False, True])
+def test_layer_bwd_fp32_gradient_stream(act_split):
+    """bf16 weights, fp32 x and fp32 dy / dx (the fp32 residual stream of a stack)."""
+    print(f"\n[case] layer bwd fp32 stream act_split={act_split}", flush=True)
+    case = I.jagged_layer_case("lbwdf", 1340, [70, 1, 300, 129], D=256, H=2, Dh=128, P=64, Tb=64, dtype="bf16",
+                               bias_std=0.2)
+    case.x = I.Tensor.make(case.x.values, "f32")   # the oracle reads the same fp32 x
+    dy = _dy(case, 1341, "f32")
+    _check(_gpu(case, dy, True, x_f32=True, act_split=act_split), _oracle(case, dy, True), "bf16", "fp32 stream")
+
+
+def test_layer_bwd_empty_batch_zeroes_every_gradient():
+    from hstu_sequential_transduction_attn_amd import _lib as ops
+    print("\n[case] layer bwd empty batch", flush=True)
+    case = I.jagged_layer_case("lbwd0", 1350, [0, 0], D=64, H=2, Dh=64, P=16, Tb=16, dtype="bf16", bias_std=0.1)
+    L = case.layers[0]
+    jd = jag_dev(case.jagged)
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    grads = dict(d_w_uvqk=torch.full((512, 64), 7.0, **f32), d_b_uvqk=torch.full((512,), 7.0, **f32),
+                 d_w_out=torch.full((64, 128), 7.0, **f32), d_b_out=torch.full((64,), 7.0, **f32),
+                 d_pos_bias=torch.full((1, 16), 7.0, **f32), d_time_bias=torch.full((1, 16), 7.0, **f32))
+    out = ops.layer_bwd(x, x.clone(), jd["seq_offsets"], jd["timestamps"], dev(L.w_uvqk), dev(L.w_out),
+                        dev(L.rab.pos_bias), dev(L.rab.time_bias), 2, 64, max_seq_len=0,
+                        b_uvqk=dev(L.b_uvqk), b_out=dev(L.b_out), grads=grads)
+    torch.cuda.synchronize()
+    assert out["dx"].shape == (0, 64)
+    for k, v in grads.items():
+        assert out[k] is v
+        assert not torch.any(v != 0).item(), k
+
+
+def test_layer_bwd_is_bitwise_deterministic():
+    print("\n[case] layer bwd determinism", flush=True)
+    rng = np.random.default_rng(1360)
+    lengths = [int(v) for v in rng.integers(1, 700, size=12)]
+    case = I.jagged_layer_case("lbwdd", 1360, lengths, D=256, H=2, Dh=128, P=64, Tb=64, dtype="bf16", bias_std=0.1)
+    dy = _dy(case, 1361, "bf16")
+    a = _gpu(case, dy, True)
+    b = _gpu(case, dy, True)
+    for name in NAMES:
+        assert np.array_equal(a[name], b[name]), name

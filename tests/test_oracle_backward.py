@@ -86,3 +86,23 @@ def test_zero_upstream_gradient_gives_zero():
     jag = _jag(lengths, tau)
     for x in O.attn_bwd(jag, q, k, v, wp, wt, np.zeros_like(g)):
         assert not np.any(x)
+
+
+def test_bin_sums_of_squares():
+    """Every allowed pair adds its dS^2 to one position bin and one time bin (equal totals, each bin at
+    least its sum squared over its pair count), and a one-token sequence has the single pair's dS^2."""
+    lengths = [9, 3, 12]
+    q, k, v, g, wp, wt, tau = _inputs(6, lengths, H=2, P=4, Tb=3, R=1)
+    jag = _jag(lengths, tau)
+    dq, dk, dv, dwp, dwt, sqp, sqt = O.attn_bwd(jag, q, k, v, wp, wt, g, return_sq=True)
+    np.testing.assert_allclose(sqp.sum(), sqt.sum(), rtol=1e-12)
+    assert np.all(sqp >= 0) and np.all(sqt >= 0)
+    n_pairs = 2 * sum(n * (n + 1) // 2 for n in lengths)
+    assert np.all(sqp * n_pairs >= dwp ** 2 - 1e-12)
+    q1, k1, v1, g1, wp1, wt1, tau1 = _inputs(7, [1], H=1, P=4, Tb=3, R=1)
+    jag1 = _jag([1], tau1)
+    *_, sqp1, sqt1 = O.attn_bwd(jag1, q1, k1, v1, wp1, wt1, g1, return_sq=True)
+    s = q1[0, 0] @ k1[0, 0] + wp1[0, 0] + wt1[0, 0]
+    ds = (g1[0, 0] @ v1[0, 0]) * O.silu_grad(s)
+    np.testing.assert_allclose(sqp1[0, 0], ds ** 2, rtol=1e-12)
+    np.testing.assert_allclose(sqt1[0, 0], ds ** 2, rtol=1e-12)
