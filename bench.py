@@ -1,6 +1,7 @@
 """Benchmark of the HSTU attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--extended]
+    python bench.py --only {layers,cached,attn_bwd,layer_bwd}
 
 A step is one hstu_attn_fwd call (QK^T, bias, SiLU, mask and AV of every allowed pair) over the
 L = 8192 workload: 8 sequences of 8192 events, 4 heads x 128, P = Tb = 256 bias buckets, causal,
@@ -10,7 +11,8 @@ covers allowed (causal, non-padded) pairs only: sum_b H * n_b (n_b + 1) / 2 * 4 
 Prints one JSON line.  `roofline` compares the kernel's average duration (HIP events on the stream
 it runs on) with the MI355X dense bf16 MFMA peak; `cpu_baseline` times the float64 oracle on a
 bounded sample of the same workload on the host cores.  --extended also prints, to stderr, the
-per-config timings of the other workloads (layer, stack, candidate-masked forward).
+timings of the other workloads (layer, stack and candidate-masked forwards, cached-history scoring,
+attention backward, layer backward); --only runs one of those legs alone.
 """
 from __future__ import annotations
 
@@ -153,7 +155,7 @@ def run(args):
         extended(args, dev)
 
 
-def extended(args, dev):
+def extended(args, dev, layers_only=False):
     """Layer workloads (stderr, informational): layer_bf16, stack8_bf16 and mfalcon_bf16 with every input
     and weight resident on the device; one forward = gather (when the workload stages its input from an
     embedding table) + every layer.  Timed with HIP events on the stream the kernels run on."""
@@ -219,8 +221,78 @@ def extended(args, dev):
         print(f"[extended] {name}: {ms:.3f} ms per forward ({len(layers)} layers, T={T}, D={D}, H={H}x{Dh}); "
               f"{flop:.3e} algorithmic FLOP -> {flop / ms / 1e9:.1f} TFLOP/s", file=sys.stderr, flush=True)
         del table, ws
+    if layers_only:
+        return
     cached_scoring(dev)
     attn_backward(dev)
+    layer_backward(dev)
+
+
+def layer_backward(dev):
+    """Layer backward (stderr, informational): hstu_layer_bwd on one layer of layer_bf16 (bf16 stream,
+    no output LayerNorm) and of stack8_bf16 (its first layer: fp32 activations and gradients, output
+    LayerNorm, split activations), for a random upstream gradient.  One call recomputes the forward
+    (nothing is saved) and forms dx and every parameter gradient.  Algorithmic FLOP: the forward's
+    GEMMs and attention, plus dg, dW2, dx, dW1 (2 T D HD each for the H*Dh-wide ones, 2 T D 4HD for the
+    projection's) and 2.5x the attention's pair products."""
+    import torch
+    from hstu_sequential_transduction_attn_amd import configs as C
+    from hstu_sequential_transduction_attn_amd import inputs as I
+    from hstu_sequential_transduction_attn_amd import _lib as ops
+
+    def t(x, f32=False):
+        if isinstance(x, I.Tensor):
+            if x.dtype == "bf16" and not f32:
+                return torch.from_numpy(np.ascontiguousarray(x.bits).view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(x.values)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    for name, mk, stream32, ln_output in [("layer_bf16", C.layer_bf16, False, False),
+                                          ("stack8_bf16 layer 0", lambda: C.stack8_bf16(num_layers=1), True, True)]:
+        case = mk()
+        j = case.jagged
+        L = case.layers[0]
+        offs, tau = t(j.seq_offsets.astype(np.int32)), t(j.timestamps.astype(np.int64))
+        T, D, H, Dh = j.total_tokens, case.d_model, case.num_heads, case.head_dim
+        gen = torch.Generator(device=dev).manual_seed(7)
+        dt = torch.float32 if stream32 else torch.bfloat16
+        x = torch.randn((T, D), device=dev, generator=gen).to(dt)
+        dy = torch.randn((T, D), device=dev, generator=gen).to(dt)
+        w1, w2, wp, wt = t(L.w_uvqk), t(L.w_out), t(L.rab.pos_bias), t(L.rab.time_bias)
+        nws = ops.layer_bwd_workspace_bytes(x, offs, tau, w1, w2, wp, wt, H, Dh, max_seq_len=j.max_seq_len,
+                                            ln_output=ln_output, mask=j.mask)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        dx = torch.empty_like(dy)
+        f32 = dict(dtype=torch.float32, device=dev)
+        grads = dict(d_w_uvqk=torch.empty(w1.shape, **f32), d_b_uvqk=torch.empty(w1.shape[0], **f32),
+                     d_w_out=torch.empty(w2.shape, **f32), d_b_out=torch.empty(D, **f32),
+                     d_pos_bias=torch.empty(wp.shape, **f32), d_time_bias=torch.empty(wt.shape, **f32))
+
+        def run():
+            ops.layer_bwd(x, dy, offs, tau, w1, w2, wp, wt, H, Dh, max_seq_len=j.max_seq_len, ln_eps=L.ln_eps,
+                          ln_output=ln_output, mask=j.mask, act_split=stream32, workspace=ws, dx=dx, grads=grads)
+
+        stream = torch.cuda.current_stream()
+        for _ in range(2):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        HD = H * Dh
+        pairs = I.allowed_pairs(j)
+        attn = pairs * H * 4 * Dh
+        fwd = 2 * T * D * 4 * HD + attn + (2 * T * HD * D if ln_output else 0)
+        bwd = 2 * (2 * T * D * HD) + 2 * (2 * T * D * 4 * HD) + 2.5 * attn
+        flop = fwd + bwd
+        print(f"[extended] layer_bwd {name}: {ms:.3f} ms per backward (T={T}, D={D}, H={H}x{Dh}, forward "
+              f"recomputed); {flop:.3e} algorithmic FLOP ({bwd:.3e} backward + {fwd:.3e} recompute) -> "
+              f"{flop / ms / 1e9:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        del ws, x, dy, dx, grads
 
 
 def attn_backward(dev):
@@ -351,6 +423,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extended", action="store_true")
+    ap.add_argument("--only", choices=["layers", "cached", "attn_bwd", "layer_bwd"],
+                    help="run only this informational leg of --extended (stderr), without the metric line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (torch copy_) five times, to scale "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE against a kernel of known traffic")
@@ -361,6 +435,14 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.only:
+        import torch
+        from hstu_sequential_transduction_attn_amd import _lib as ops
+        ops.load_library()
+        dev = torch.device("cuda:0")
+        {"layers": lambda: extended(args, dev, layers_only=True), "cached": lambda: cached_scoring(dev),
+         "attn_bwd": lambda: attn_backward(dev), "layer_bwd": lambda: layer_backward(dev)}[args.only]()
         return
     run(args)
 
