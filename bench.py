@@ -220,6 +220,30 @@ def extended(args, dev, layers_only=False):
         flop = len(layers) * (2 * T * D * 4 * HD + pairs * H * 4 * Dh + 2 * T * HD * D)
         print(f"[extended] {name}: {ms:.3f} ms per forward ({len(layers)} layers, T={T}, D={D}, H={H}x{Dh}); "
               f"{flop:.3e} algorithmic FLOP -> {flop / ms / 1e9:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        if table is not None:
+            # the same forward as one hstu_stack_fwd call: gather and inter-layer LayerNorms fused into the GEMMs
+            sl = [dict(w_uvqk=L["w1"], w_out=L["w2"], pos_bias=L["wp"], time_bias=L["wt"], ln_eps=L["eps"])
+                  for L in layers]
+            y32 = torch.empty((j.total_tokens, case.d_model), dtype=torch.float32, device=dev)
+            nsws = ops.stack_workspace_bytes(table, offs, tau, sl, H, Dh, max_seq_len=j.max_seq_len, mask=j.mask,
+                                             num_candidates=ncand)
+            sws = torch.empty(max(nsws, 1), dtype=torch.uint8, device=dev)
+
+            def stacked():
+                return ops.stack_fwd(table, ids, offs, tau, sl, H, Dh, max_seq_len=j.max_seq_len, mask=j.mask,
+                                     num_candidates=ncand, act_split=act_split, y=y32, workspace=sws)
+            for _ in range(2):
+                stacked()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                stacked()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms2 = e0.elapsed_time(e1) / reps
+            print(f"[extended] {name} (hstu_stack_fwd, gather and LayerNorms fused): {ms2:.3f} ms per forward; "
+                  f"{flop / ms2 / 1e9:.1f} TFLOP/s", file=sys.stderr, flush=True)
+            del sws, y32
         del table, ws
     if layers_only:
         return

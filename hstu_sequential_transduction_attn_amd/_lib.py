@@ -108,6 +108,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_layer_bwd.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT), ctypes.POINTER(LayerWeightsT),
                                    ctypes.c_int, ctypes.c_int, c_vp, ctypes.c_int, c_vp, c_vp,
                                    ctypes.POINTER(LayerGradsT), c_vp, c_sz, c_vp]
+    lib.hstu_stack_workspace_bytes.restype = c_sz
+    lib.hstu_stack_workspace_bytes.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT),
+                                               ctypes.POINTER(LayerWeightsT), c_i32, ctypes.c_int]
+    lib.hstu_stack_fwd.restype = ctypes.c_int
+    lib.hstu_stack_fwd.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT), ctypes.POINTER(LayerWeightsT),
+                                   c_i32, ctypes.c_int, c_vp, c_i64, c_vp, ctypes.c_int, c_vp, c_vp, c_sz, c_vp]
     lib.hstu_gather_rows.restype = ctypes.c_int
     lib.hstu_gather_rows.argtypes = [c_vp, c_i64, c_i32, ctypes.c_int, c_vp, c_i32, c_vp, c_vp]
     if path is None:
@@ -299,6 +305,46 @@ def layer_bwd(x, dy, seq_offsets, timestamps, w_uvqk, w_out, pos_bias, time_bias
                               _dtype_code(dy), _ptr(dy), _ptr(dx), ctypes.byref(grads), _ptr(workspace),
                               workspace.numel(), _stream(stream)))
     return out
+
+
+def _stack_structs(table, seq_offsets, timestamps, layers, num_heads, head_dim, max_seq_len, mask, num_candidates,
+                   attn_scale, act_split):
+    jag = make_jagged(seq_offsets, timestamps, max_seq_len, num_candidates, attn_scale)
+    n = len(layers)
+    D = int(table.shape[1])
+    descs = (AttnDescT * n)(*[make_desc(num_heads, head_dim, L["pos_bias"], L["time_bias"], mask) for L in layers])
+    ws = (LayerWeightsT * n)(*[LayerWeightsT(D, _ptr(L["w_uvqk"]), _ptr(L.get("b_uvqk")), _ptr(L["w_out"]),
+                                             _ptr(L.get("b_out")), float(L.get("ln_eps", 1e-6)), 0,
+                                             int(bool(act_split))) for L in layers])
+    return jag, descs, ws, _dtype_code(layers[0]["w_uvqk"])
+
+
+def stack_workspace_bytes(table, seq_offsets, timestamps, layers, num_heads: int, head_dim: int, *, max_seq_len: int,
+                          mask: int = MASK_CAUSAL, num_candidates=None) -> int:
+    jag, descs, ws, dt = _stack_structs(table, seq_offsets, timestamps, layers, num_heads, head_dim, max_seq_len,
+                                        mask, num_candidates, None, False)
+    return int(load_library().hstu_stack_workspace_bytes(ctypes.byref(jag), descs, ws, len(layers), dt))
+
+
+def stack_fwd(table, ids, seq_offsets, timestamps, layers, num_heads: int, head_dim: int, *, max_seq_len: int,
+              mask: int = MASK_CAUSAL, num_candidates=None, attn_scale=None, act_split: bool = False,
+              y_dtype: Optional[torch.dtype] = None, workspace=None, y=None, stream=None):
+    """y = hstu_stack_fwd(...): the layers over x_0 = table[ids] (table itself when ids is None).
+    layers: list of dicts with w_uvqk, w_out, pos_bias, time_bias and optional b_uvqk, b_out, ln_eps."""
+    lib = load_library()
+    T = int(timestamps.numel())   # total tokens (the table may hold more rows than that)
+    D = int(table.shape[1])
+    if y is None:
+        y = torch.empty((T, D), dtype=y_dtype or table.dtype, device=table.device)
+    jag, descs, ws, dt = _stack_structs(table, seq_offsets, timestamps, layers, num_heads, head_dim, max_seq_len,
+                                        mask, num_candidates, attn_scale, act_split)
+    n = len(layers)
+    nws = int(lib.hstu_stack_workspace_bytes(ctypes.byref(jag), descs, ws, n, dt))
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=table.device)
+    _check(lib.hstu_stack_fwd(ctypes.byref(jag), descs, ws, n, dt, _ptr(table), int(table.shape[0]), _ptr(ids),
+                              _dtype_code(y), _ptr(y), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return y
 
 
 def gather_rows(table: torch.Tensor, ids: torch.Tensor, out=None, stream=None):

@@ -747,4 +747,189 @@ hstu_status_t hstu_gather_rows(const void *table, int64_t table_rows, int32_t d,
   }
 }
 
+namespace {
+
+// Stack workspace.  Fused path (bf16, large-tile shapes): U (fp32), V, Q, K (bf16), O (fp32) and its
+// per-head statistics, the timestamp ranges, two fp32 pre-LayerNorm sums r (ping-pong between layers),
+// the per-tile row statistics of the output GEMM and two per-row (mean, rstd) arrays.  Otherwise: the
+// gathered x0 (dtype), two fp32 inter-layer activations and one layer workspace.
+struct StackWs {
+  bool fused;
+  size_t u, v, q, k, o, ostat, stats, r32[2], tstats, rowstat[2];
+  size_t x0, act[2], layer, layer_bytes;
+  size_t total;
+};
+
+StackWs stack_ws(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc0, int64_t D, hstu_dtype_t dt) {
+  StackWs w{};
+  const int64_t T = jag->total_tokens, B = jag->num_seqs, H = desc0->num_heads, HD = H * desc0->head_dim;
+  w.fused = dt == HSTU_BF16 && T > 0 && hstu::stack_gemms_fit(T, D, HD);
+  if (T == 0) return w;                 // nothing to stage
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += round_up(bytes, 256);
+    return at;
+  };
+  if (w.fused) {
+    w.u = take((size_t)T * HD * 4);
+    w.v = take((size_t)T * HD * 2);
+    w.q = take((size_t)T * HD * 2);
+    w.k = take((size_t)T * HD * 2);
+    w.o = take((size_t)T * HD * 4);
+    w.ostat = take((size_t)T * H * 8);
+    w.stats = take(hstu::attn_tau_stats_bytes(T, B));
+    w.r32[0] = take((size_t)T * D * 4);
+    w.r32[1] = take((size_t)T * D * 4);
+    w.tstats = take((size_t)T * hstu::stack_out_col_tiles(D) * 8);
+    w.rowstat[0] = take((size_t)T * 8);
+    w.rowstat[1] = take((size_t)T * 8);
+  } else {
+    w.x0 = take((size_t)T * D * esize(dt));
+    w.act[0] = take((size_t)T * D * 4);
+    w.act[1] = take((size_t)T * D * 4);
+    w.layer_bytes = layer_ws(T, B, H, HD, D, dt, true).total;
+    w.layer = take(w.layer_bytes);
+  }
+  w.total = off;
+  return w;
+}
+
+// Checks shared by the stack's size query and the stack call: every layer's descriptor and weights,
+// one d_model and one H x Dh for all layers.
+hstu_status_t check_stack(const hstu_jagged_t *jag, const hstu_attn_desc_t *descs, const hstu_layer_weights_t *ws,
+                          int32_t L, hstu_dtype_t dtype) {
+  if (L < 1) return fail(HSTU_ERR_INVALID_ARGUMENT, "num_layers = %d < 1", L);
+  if (!descs || !ws) return fail(HSTU_ERR_INVALID_ARGUMENT, "descs/weights is NULL");
+  if (!valid_dtype(dtype)) return fail(HSTU_ERR_INVALID_ARGUMENT, "dtype = %d invalid", (int)dtype);
+  for (int32_t l = 0; l < L; ++l) {
+    hstu_status_t st = check_jagged_desc(jag, &descs[l]);
+    if (st != HSTU_OK) return st;
+    if (descs[l].num_heads != descs[0].num_heads || descs[l].head_dim != descs[0].head_dim)
+      return fail(HSTU_ERR_UNSUPPORTED, "layer %d: num_heads/head_dim differ from layer 0", l);
+    if (descs[l].mask != descs[0].mask) return fail(HSTU_ERR_INVALID_ARGUMENT, "layer %d: mask differs", l);
+    const hstu_layer_weights_t &w = ws[l];
+    if (w.d_model != ws[0].d_model) return fail(HSTU_ERR_INVALID_ARGUMENT, "layer %d: d_model differs", l);
+    if (w.d_model < 8 || w.d_model % 8 != 0 || w.d_model > 4096)
+      return fail(HSTU_ERR_UNSUPPORTED, "d_model = %d must be a multiple of 8 in [8, 4096]", w.d_model);
+    if (!(w.ln_eps > 0.0f)) return fail(HSTU_ERR_INVALID_ARGUMENT, "layer %d: ln_eps must be > 0", l);
+    if (!w.w_uvqk || !w.w_out) return fail(HSTU_ERR_INVALID_ARGUMENT, "layer %d: w_uvqk/w_out is NULL", l);
+    if (!aligned16(w.w_uvqk) || !aligned16(w.w_out))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "layer %d: weights must be 16-byte aligned", l);
+  }
+  return HSTU_OK;
+}
+
+}  // namespace
+
+size_t hstu_stack_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_t *descs,
+                                  const hstu_layer_weights_t *weights, int32_t num_layers, hstu_dtype_t dtype) {
+  if (!jag || !descs || !weights || num_layers < 1 || jag->total_tokens < 0 || jag->num_seqs < 0 ||
+      descs[0].num_heads < 1 || descs[0].head_dim < 1 || weights[0].d_model < 1 || !valid_dtype(dtype))
+    return 0;
+  return stack_ws(jag, &descs[0], weights[0].d_model, dtype).total;
+}
+
+hstu_status_t hstu_stack_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *descs,
+                             const hstu_layer_weights_t *weights, int32_t num_layers, hstu_dtype_t dtype,
+                             const void *table, int64_t table_rows, const int64_t *ids, hstu_dtype_t y_dtype,
+                             void *y, void *workspace, size_t workspace_bytes, void *stream) {
+  try {
+    hstu_status_t st = check_stack(jag, descs, weights, num_layers, dtype);
+    if (st != HSTU_OK) return st;
+    if (!valid_dtype(y_dtype) || (y_dtype != dtype && y_dtype != HSTU_F32))
+      return fail(HSTU_ERR_UNSUPPORTED, "y_dtype = %d must be HSTU_F32 or dtype", (int)y_dtype);
+    const int64_t T = jag->total_tokens, D = weights[0].d_model;
+    const int64_t H = descs[0].num_heads, HD = H * descs[0].head_dim;
+    if (ids ? table_rows < 1 : table_rows < T)
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "table_rows = %lld too small", (long long)table_rows);
+    const StackWs ws = stack_ws(jag, &descs[0], D, dtype);
+    if (workspace_bytes < ws.total)
+      return fail(HSTU_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, ws.total);
+    if (T == 0) return ok();
+    if (!table || !y || !workspace) return fail(HSTU_ERR_INVALID_ARGUMENT, "table/y/workspace is NULL");
+    if (!aligned16(table) || !aligned16(y) || !aligned16(workspace))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "table/y/workspace must be 16-byte aligned");
+    const size_t ntab = (size_t)table_rows * D * esize(dtype), ny = (size_t)T * D * esize(y_dtype);
+    if (overlaps(y, ny, table, ntab)) return fail(HSTU_ERR_INVALID_ARGUMENT, "y overlaps the table");
+    if (overlaps(workspace, ws.total, table, ntab) || overlaps(workspace, ws.total, y, ny))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace overlaps the table or y");
+    if (ids && overlaps(workspace, ws.total, ids, (size_t)T * 8))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace overlaps ids");
+
+    hipStream_t s = (hipStream_t)stream;
+    char *wsb = (char *)workspace;
+    const int L = num_layers;
+    if (!ws.fused) {
+      // gather once, then one layer at a time through hstu_layer_fwd with fp32 activations between layers
+      const void *x = table;
+      if (ids) {
+        hstu_status_t g = hstu_gather_rows(table, table_rows, (int32_t)D, dtype, ids, (int32_t)T, wsb + ws.x0, stream);
+        if (g != HSTU_OK) return g;
+        x = wsb + ws.x0;
+      }
+      hstu_dtype_t x_dt = dtype;
+      for (int l = 0; l < L; ++l) {
+        hstu_layer_weights_t w = weights[l];
+        const bool last = l == L - 1;
+        w.ln_output = last ? 0 : 1;
+        void *out = last ? y : (void *)(wsb + ws.act[l % 2]);
+        hstu_status_t r = hstu_layer_fwd(jag, &descs[l], &w, dtype, x_dt, x, last ? y_dtype : HSTU_F32, out,
+                                         wsb + ws.layer, ws.layer_bytes, stream);
+        if (r != HSTU_OK) return r;
+        x = out;
+        x_dt = HSTU_F32;
+      }
+      return ok();
+    }
+
+    hipError_t e;
+    for (int l = 0; l < L; ++l) {
+      const hstu_layer_weights_t &w = weights[l];
+      const bool last = l == L - 1;
+      const int prev = (l + 1) % 2;   // buffers written by layer l - 1
+      hstu::GemmStackProjArgs g1{};
+      g1.a_mode = l == 0 ? (ids ? 1 : 0) : 2;
+      g1.a = l == 0 ? table : (const void *)(wsb + ws.r32[prev]);
+      g1.ids = ids;
+      g1.a_rowstat = (const float *)(wsb + ws.rowstat[prev]);
+      g1.w = w.w_uvqk; g1.bias = w.b_uvqk;
+      g1.u = (float *)(wsb + ws.u); g1.v = wsb + ws.v; g1.q = wsb + ws.q; g1.k = wsb + ws.k;
+      g1.M = (int32_t)T; g1.K = (int32_t)D; g1.HD = (int32_t)HD; g1.split = w.act_split != 0;
+      e = hstu::launch_gemm_stack_proj(g1, s);
+      if (e != hipSuccess) return from_hip(e, "projection GEMM launch");
+
+      hstu::AttnArgs a = attn_args(jag, &descs[l]);
+      a.q = wsb + ws.q; a.k = wsb + ws.k; a.v = wsb + ws.v; a.out = wsb + ws.o;
+      a.row_stride = HD; a.out_row_stride = HD;
+      a.in_dtype = hstu::kBF16; a.out_dtype = hstu::kF32;
+      a.tau_stats = (int64_t *)(wsb + ws.stats);
+      a.row_stats = (float *)(wsb + ws.ostat);
+      e = hstu::launch_attn_fwd(a, s);
+      if (e != hipSuccess) return from_hip(e, "attention launch");
+
+      hstu::GemmStackOutArgs g2{};
+      g2.o = (const float *)(wsb + ws.o); g2.u = (const float *)(wsb + ws.u);
+      g2.row_stats = (const float *)(wsb + ws.ostat);
+      g2.heads = (int32_t)H; g2.head_dim = descs[0].head_dim; g2.eps = w.ln_eps;
+      g2.w = w.w_out; g2.bias = w.b_out;
+      g2.resid_mode = g1.a_mode; g2.resid = g1.a; g2.ids = ids; g2.resid_rowstat = g1.a_rowstat;
+      g2.y32 = last ? nullptr : (float *)(wsb + ws.r32[l % 2]);
+      g2.out_stats = last ? nullptr : (float *)(wsb + ws.tstats);
+      g2.y = last ? y : nullptr; g2.y_f32 = y_dtype == HSTU_F32;
+      g2.M = (int32_t)T; g2.N = (int32_t)D; g2.K = (int32_t)HD; g2.split = w.act_split != 0;
+      e = hstu::launch_gemm_stack_out(g2, s);
+      if (e != hipSuccess) return from_hip(e, "output GEMM launch");
+      if (!last) {
+        e = hstu::launch_row_stats_combine((const float *)(wsb + ws.tstats), (float *)(wsb + ws.rowstat[l % 2]),
+                                           (int)T, (int)D, w.ln_eps, s);
+        if (e != hipSuccess) return from_hip(e, "row statistics launch");
+      }
+    }
+    return ok();
+  } catch (...) {
+    return fail(HSTU_ERR_DEVICE, "unexpected C++ exception in hstu_stack_fwd");
+  }
+}
+
 }  // extern "C"

@@ -66,6 +66,10 @@ __device__ __forceinline__ void dma16(const void *base, uint32_t lane_off, uint3
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3"
                : : "s"(m0), "v"(lane_off), "s"(base), "i"(IMM) : "memory");
 }
+// The same 16-byte load from a per-lane 64-bit address (rows gathered from anywhere in memory).
+__device__ __forceinline__ void dma16_at(const void *addr, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m0), "v"(addr) : "memory");
+}
 __device__ __forceinline__ void dma4(const void *base, uint32_t lane_off, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" : : "s"(m0), "v"(lane_off), "s"(base)
                : "memory");

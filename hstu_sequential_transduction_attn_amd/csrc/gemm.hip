@@ -32,7 +32,9 @@ namespace {
 constexpr int kBM = 128, kBN = 128, kBK = 32;
 constexpr int kThreads = 256;
 
-enum Epi : int { kEpiUvqk = 0, kEpiOut = 1 };
+// Epilogues: the projection's SiLU + U|V|Q|K split; the output's bias + residual (plain rows); the
+// stack's output (residual rows gathered or LayerNorm-ed, per-row tile statistics for the next LN).
+enum Epi : int { kEpiUvqk = 0, kEpiOut = 1, kEpiOutStack = 2 };
 
 // TM: MFMA operand / weight type.  TA: storage type of the activation A.  SPLIT: 1 or 2 A terms.
 template <typename TM, typename TA, int SPLIT>
@@ -73,6 +75,13 @@ struct GemmParams {
   const float *row_stats;  // fused gate: [M][heads][2] per-head mean and sum of squared deviations of O
   int heads, head_dim;
   float eps;
+  // large-tile kernel only:
+  const int64_t *ids;      // gathered rows: A row m (kAkGather) and residual row m (resid_mode 1) are row
+                           // ids[m] of a [rows][K] (A) or [rows][N] (residual) bf16 table
+  const float *a_rowstat;  // kAkLn: [M][2] (mean, rstd) of A's rows
+  int resid_mode;          // 0: resid [M][N]; 1: bf16 table rows resid[ids[m]]; 2: LN of fp32 resid rows
+  const float *resid_rowstat;  // resid_mode 2: [M][2] (mean, rstd)
+  float *out_stats;        // output epilogue with out32: [M][ceil(N/BN)][2] per-row (mean, M2) of each column tile
 };
 
 // Staging registers of one 16-byte LDS chunk of A: the global source is 16 bytes (TA == TM) or
@@ -313,15 +322,19 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(const GemmParams p) {
 // The configurations below use 128 x 256 tiles (64 x 256 for the gate, whose A operand is 8 bytes per
 // element) with 2 x 2 waves and two workgroups per CU: one workgroup's barrier waits, prologue and
 // epilogue overlap the other's MFMA work, which single-workgroup 256 x 256 tiles cannot hide.
-enum AKind : int { kAkBf16 = 0, kAkF32 = 1, kAkGate = 2 };
+// A operand kinds: bf16 rows; fp32 rows; the gate LN(O) * U from fp32 O and U; bf16 rows gathered
+// through a row-index array (an embedding table); fp32 rows normalised per row with precomputed
+// (mean, rstd) (a LayerNorm applied while the operand is read).
+enum AKind : int { kAkBf16 = 0, kAkF32 = 1, kAkGate = 2, kAkGather = 3, kAkLn = 4 };
 
 template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, int AK_, int SPLIT_, int GM_, int OCC_ = 1>
 struct BigCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_, AK = AK_, GM = GM_;
   static constexpr int kOcc = OCC_;                                 // workgroups per CU
-  static constexpr int kTerms = (AK != kAkBf16 && SPLIT_ == 2) ? 2 : 1;
+  static constexpr bool kA16 = AK == kAkBf16 || AK == kAkGather;   // A staged as bf16
+  static constexpr int kTerms = (!kA16 && SPLIT_ == 2) ? 2 : 1;
   static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
-  static constexpr int kEA = AK == kAkBf16 ? 2 : 4;                 // A element bytes (global and LDS)
+  static constexpr int kEA = kA16 ? 2 : 4;                          // A element bytes (global and LDS)
   static constexpr int kABytes = BM * BK * kEA;
   static constexpr int kUBytes = AK == kAkGate ? BM * BK * 4 : 0;
   static constexpr int kBBytes = BN * BK * 2;
@@ -414,14 +427,30 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
   }
   // workgroup-uniform operand bases (scalar registers: the direct-to-LDS loads take them as SGPR pairs)
   const char *abase = uniform_ptr((const char *)p.a + (int64_t)m0 * a_rb + (int64_t)kt0 * BK * C::kEA);
+  // gathered A rows: per-lane 64-bit source addresses (the table can exceed 4 GB)
+  const char *aptr[C::AK == kAkGather ? C::kDA : 1];
+  if constexpr (C::AK == kAkGather) {
+#pragma unroll
+    for (int t = 0; t < C::kDA; ++t) {
+      const int q = wave + t * C::kWaves, g = q / (BM / 16), r = (q % (BM / 16)) * 16 + lrow;
+      const int64_t row = p.ids[m0 + imin(r, a_rows - 1)];
+      aptr[t] = (const char *)p.a + row * (int64_t)a_rb + (int64_t)kt0 * BK * 2 + g * 64 + lpiece;
+    }
+  }
   const char *ubase = uniform_ptr((const char *)p.gate_u + (int64_t)m0 * a_rb + (int64_t)kt0 * BK * 4);
   const char *bbase = uniform_ptr((const char *)p.b + (int64_t)n0 * b_rb + (int64_t)kt0 * BK * 2);
 
   auto issue = [&](int kt, int slot) {
     const uint32_t st = smem_addr + (uint32_t)(slot * C::kStage);
-    const char *ab = abase + (int64_t)kt * BK * C::kEA;
+    if constexpr (C::AK == kAkGather) {
 #pragma unroll
-    for (int t = 0; t < C::kDA; ++t) dma16<0>(ab, aoff[t], st + (uint32_t)((wave + t * C::kWaves) * 1024));
+      for (int t = 0; t < C::kDA; ++t)
+        dma16_at(aptr[t] + (int64_t)kt * BK * 2, st + (uint32_t)((wave + t * C::kWaves) * 1024));
+    } else {
+      const char *ab = abase + (int64_t)kt * BK * C::kEA;
+#pragma unroll
+      for (int t = 0; t < C::kDA; ++t) dma16<0>(ab, aoff[t], st + (uint32_t)((wave + t * C::kWaves) * 1024));
+    }
     if constexpr (C::AK == kAkGate) {
       const char *ub = ubase + (int64_t)kt * BK * 4;
 #pragma unroll
@@ -435,7 +464,17 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
   };
 
   // ---- gate: LayerNorm statistics of this lane's A rows, from the per-head (mean, M2) pairs
-  float rstd[C::AK == kAkGate ? FM : 1], nmr[C::AK == kAkGate ? FM : 1];
+  constexpr bool kNorm = C::AK == kAkGate || C::AK == kAkLn;
+  float rstd[kNorm ? FM : 1], nmr[kNorm ? FM : 1];
+  if constexpr (C::AK == kAkLn) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = imin(m0 + wm + 32 * i + l32, p.M - 1);
+      const float mean = p.a_rowstat[2 * (int64_t)m], rs = p.a_rowstat[2 * (int64_t)m + 1];
+      rstd[i] = rs;
+      nmr[i] = -mean * rs;
+    }
+  }
   if constexpr (C::AK == kAkGate) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -474,7 +513,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
       for (int i = 0; i < FM; ++i) {
         const int r = wm + 32 * i + l32;
         bf16x8 ahi, alo;
-        if constexpr (C::AK == kAkBf16) {
+        if constexpr (C::kA16) {
           ahi = *(const HSTU_LDS bf16x8 *)(As + cg_at<BM>(r, st >> 1, 2 * (st & 1) + half));
         } else {
           u32x4 h, l;
@@ -487,6 +526,12 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
             for (int e = 0; e < 4; ++e) {
               x0[e] = fmaf(x0[e], rstd[i], nmr[i]) * u0[e];
               x1[e] = fmaf(x1[e], rstd[i], nmr[i]) * u1[e];
+            }
+          } else if constexpr (C::AK == kAkLn) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x0[e] = fmaf(x0[e], rstd[i], nmr[i]);
+              x1[e] = fmaf(x1[e], rstd[i], nmr[i]);
             }
           }
           h = to_bf16x8(x0, x1);
@@ -528,6 +573,28 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
   }
 
   // ---- epilogue: acc[i][j] element e -> row m0 + wm + 32i + 8(e/4) + 4 half + e%4, column n0 + wn + 32j + l32
+  // stack output: the residual's per-row parameters, loaded once per row (resid_mode 1: the table row as
+  // two 32-bit halves; 2: mean and rstd as bits)
+  uint32_t rp0[EPI == kEpiOutStack ? FM : 1][16], rp1[EPI == kEpiOutStack ? FM : 1][16];
+  if constexpr (EPI == kEpiOutStack) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = imin(m0 + wm + 32 * i + 8 * (e / 4) + 4 * half + (e % 4), p.M - 1);
+        if (p.resid_mode == 1) {
+          const uint64_t row = (uint64_t)p.ids[m];
+          rp0[i][e] = (uint32_t)row;
+          rp1[i][e] = (uint32_t)(row >> 32);
+        } else if (p.resid_mode == 2) {
+          const float2 st = *(const float2 *)(p.resid_rowstat + 2 * (int64_t)m);
+          rp0[i][e] = __builtin_bit_cast(uint32_t, st.x);
+          rp1[i][e] = __builtin_bit_cast(uint32_t, st.y);
+        } else {
+          rp0[i][e] = rp1[i][e] = 0u;
+        }
+      }
+  }
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int n = n0 + wn + 32 * j + l32;
@@ -553,25 +620,107 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
     } else {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        // the 16 residuals of the fragment are loaded (rows clamped into the matrix) before any is used
+        // the 16 residuals of the fragment are loaded (rows clamped into the matrix) before any is used:
+        // the residual kind is decided once per fragment, so each branch issues its 16 loads back to back
         float r[16];
+        auto idx_of = [&](int e) {
+          return (int64_t)imin(m0 + wm + 32 * i + 8 * (e / 4) + 4 * half + (e % 4), p.M - 1) * p.N + n;
+        };
+        const float *rf = (const float *)p.resid;
+        const __bf16 *rb = (const __bf16 *)p.resid;
+        if constexpr (EPI == kEpiOutStack) {
+          if (p.resid_mode == 1) {               // gathered bf16 rows
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = imin(m0 + wm + 32 * i + 8 * (e / 4) + 4 * half + (e % 4), p.M - 1);
-          const int64_t idx = (int64_t)m * p.N + n;
-          if (!p.resid) r[e] = 0.0f;
-          else r[e] = p.resid_f32 ? ((const float *)p.resid)[idx] : to_f32(((const __bf16 *)p.resid)[idx]);
+            for (int e = 0; e < 16; ++e) r[e] = to_f32(rb[(((int64_t)rp1[i][e] << 32) | rp0[i][e]) * p.N + n]);
+          } else if (p.resid_mode == 2) {        // LayerNorm of fp32 rows
+#pragma unroll
+            for (int e = 0; e < 16; ++e) r[e] = rf[idx_of(e)];
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              r[e] = (r[e] - __builtin_bit_cast(float, rp0[i][e])) * __builtin_bit_cast(float, rp1[i][e]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) r[e] = to_f32(rb[idx_of(e)]);
+          }
+        } else {
+          if (!p.resid) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) r[e] = 0.0f;
+          } else if (p.resid_f32) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) r[e] = rf[idx_of(e)];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) r[e] = to_f32(rb[idx_of(e)]);
+          }
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int m = m0 + wm + 32 * i + 8 * (e / 4) + 4 * half + (e % 4);
+          const float y = acc[i][j][e] + bias + r[e];
+          if constexpr (EPI == kEpiOutStack) acc[i][j][e] = y;   // kept for the row statistics below
           if (m < p.M) {
             const int64_t idx = (int64_t)m * p.N + n;
-            const float y = acc[i][j][e] + bias + r[e];
             if (out32) out32[idx] = y;
             else if (p.y_f32) ((float *)p.out0)[idx] = y;
             else ((__bf16 *)p.out0)[idx] = f32_to_bf16(y);
           }
+        }
+      }
+    }
+  }
+
+  // ---- per-row (mean, M2) of this tile's columns, for a LayerNorm applied by the next consumer.
+  // Two passes over the values in registers (mean, then squared deviations); each pass sums a lane's
+  // columns, then every lane's partial goes to LDS and one thread per row adds the WN x 32 partials in
+  // order.  The LDS ring is idle by now (the barrier below waits for the last stage's readers).
+  if constexpr (EPI == kEpiOutStack) {
+    if (p.out_stats) {
+      constexpr int kParts = C::WN * 32;
+      static_assert(BM * (kParts + 1) * 4 <= C::kLds, "row statistics fit in the LDS ring");
+      HSTU_LDS float *red = (HSTU_LDS float *)smem;    // [BM][kParts]
+      HSTU_LDS float *rmean = red + BM * kParts;       // [BM]
+      const int cnt = imin(BN, p.N - n0);
+      const int wn_i = wave % C::WN;
+      float mean_r[FM][16];
+      for (int pass = 0; pass < 2; ++pass) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int row = wm + 32 * i + 8 * (e / 4) + 4 * half + (e % 4);
+            float v = 0.0f;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const bool ok = n0 + wn + 32 * j + l32 < p.N;
+              const float d = pass == 0 ? acc[i][j][e] : acc[i][j][e] - mean_r[i][e];
+              v += ok ? (pass == 0 ? d : d * d) : 0.0f;
+            }
+            red[row * kParts + wn_i * 32 + l32] = v;
+          }
+        __syncthreads();
+        if (tid < BM) {
+          float sum = 0.0f;
+          for (int q = 0; q < kParts; ++q) sum += red[tid * kParts + q];
+          if (pass == 0) {
+            rmean[tid] = sum / (float)cnt;
+          } else {
+            const int m = m0 + tid;
+            if (m < p.M) {
+              const int nN = (p.N + BN - 1) / BN;
+              float *st = p.out_stats + 2 * ((int64_t)m * nN + n0 / BN);
+              st[0] = rmean[tid];
+              st[1] = sum;
+            }
+          }
+        }
+        if (pass == 0) {
+          __syncthreads();
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mean_r[i][e] = rmean[wm + 32 * i + 8 * (e / 4) + 4 * half + (e % 4)];
         }
       }
     }
@@ -629,6 +778,9 @@ using CfgF32 = BigCfg<128, 256, 32, 2, 2, 2, kAkF32, 1, 8, 2>;
 using CfgF32Split = BigCfg<128, 256, 32, 2, 2, 2, kAkF32, 2, 8, 2>;
 using CfgGate = BigCfg<64, 256, 32, 2, 2, 2, kAkGate, 1, 4, 2>;
 using CfgGateSplit = BigCfg<64, 256, 32, 2, 2, 2, kAkGate, 2, 4, 2>;
+using CfgGather = BigCfg<128, 256, 32, 2, 2, 2, kAkGather, 1, 4, 2>;
+using CfgLn = BigCfg<128, 256, 32, 2, 2, 2, kAkLn, 1, 8, 2>;
+using CfgLnSplit = BigCfg<128, 256, 32, 2, 2, 2, kAkLn, 2, 8, 2>;
 
 // The large-tile kernel needs K to be a whole number of k-tiles, per-lane source offsets (row within
 // the tile times the row's bytes) that fit 32 bits, and enough tiles to fill the chip.
@@ -690,6 +842,41 @@ int gemm_plain_splits(int64_t M, int64_t N, int64_t K, int dtype, int a_f32) {
   const int64_t by_depth = K / CfgBf16::BK / 16;           // at least 16 k-tiles per split
   const int64_t sp = by_fill < by_depth ? by_fill : by_depth;
   return sp > 1 ? (int)(sp < 64 ? sp : 64) : 1;
+}
+
+bool stack_gemms_fit(int64_t M, int64_t D, int64_t HD) {
+  GemmParams p{};
+  p.M = (int)M; p.N = (int)(4 * HD); p.K = (int)D;
+  if (!big_fits<CfgGather>(p) || !big_fits<CfgLn>(p)) return false;
+  p.N = (int)D; p.K = (int)HD;
+  return big_fits<CfgGate>(p);
+}
+
+int stack_out_col_tiles(int64_t N) { return (int)((N + CfgGate::BN - 1) / CfgGate::BN); }
+
+hipError_t launch_gemm_stack_proj(const GemmStackProjArgs &a, hipStream_t s) {
+  GemmParams p{};
+  p.a = a.a; p.b = a.w; p.bias = a.bias; p.resid = nullptr;
+  p.out0 = a.u; p.out1 = a.v; p.out2 = a.q; p.out3 = a.k; p.out32 = nullptr; p.zout = nullptr;
+  p.M = a.M; p.N = 4 * a.HD; p.K = a.K; p.HD = a.HD;
+  p.splits = 1;
+  p.ids = a.ids; p.a_rowstat = a.a_rowstat;
+  if (a.a_mode == 1) return launch_big<CfgGather, kEpiUvqk>(p, s);
+  if (a.a_mode == 2) return a.split ? launch_big<CfgLnSplit, kEpiUvqk>(p, s) : launch_big<CfgLn, kEpiUvqk>(p, s);
+  return launch_big<CfgBf16, kEpiUvqk>(p, s);
+}
+
+hipError_t launch_gemm_stack_out(const GemmStackOutArgs &a, hipStream_t s) {
+  GemmParams p{};
+  p.a = a.o; p.b = a.w; p.bias = a.bias; p.resid = a.resid;
+  p.out0 = a.y; p.out1 = p.out2 = p.out3 = nullptr; p.out32 = a.y32;
+  p.M = a.M; p.N = a.N; p.K = a.K; p.HD = 0;
+  p.resid_f32 = 0; p.y_f32 = a.y_f32;
+  p.gate_u = a.u; p.row_stats = a.row_stats; p.heads = a.heads; p.head_dim = a.head_dim; p.eps = a.eps;
+  p.splits = 1;
+  p.resid_mode = a.resid_mode; p.ids = a.ids; p.resid_rowstat = a.resid_rowstat;
+  p.out_stats = a.y32 ? a.out_stats : nullptr;
+  return a.split ? launch_big<CfgGateSplit, kEpiOutStack>(p, s) : launch_big<CfgGate, kEpiOutStack>(p, s);
 }
 
 hipError_t launch_gemm_plain(const GemmPlainArgs &a, hipStream_t s) {

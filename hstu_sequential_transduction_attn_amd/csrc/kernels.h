@@ -130,6 +130,46 @@ struct GemmPlainArgs {
 hipError_t launch_gemm_plain(const GemmPlainArgs &a, hipStream_t stream);
 int gemm_plain_splits(int64_t M, int64_t N, int64_t K, int dtype, int a_f32);
 
+// ---- fused stack (bf16 weights, large-tile kernels only: stack_gemms_fit must hold)
+// Projection with its A operand read as bf16 rows of `a` (a_mode 0), bf16 table rows a[ids[m]]
+// (a_mode 1: the embedding gather), or LN of fp32 rows of `a` with per-row (mean, rstd) a_rowstat
+// (a_mode 2: the previous layer's post-LayerNorm; split: bf16 hi + lo).  Outputs as GemmUvqkArgs.
+struct GemmStackProjArgs {
+  int32_t a_mode;
+  const void *a;
+  const int64_t *ids;
+  const float *a_rowstat;
+  const void *w, *bias;
+  float *u;
+  void *v, *q, *k;
+  int32_t M, K, HD, split;
+};
+hipError_t launch_gemm_stack_proj(const GemmStackProjArgs &a, hipStream_t stream);
+// Gated output projection (A as GemmOutArgs) with the residual read as bf16 rows (resid_mode 0),
+// gathered bf16 table rows resid[ids[m]] (1), or LN of fp32 rows with resid_rowstat (2).  Either the
+// fp32 sum y32 plus per-row (mean, M2) of every 256-column tile (out_stats [M][stack_out_col_tiles(N)][2])
+// for a LayerNorm that the next layer applies, or y (bf16, or fp32 if y_f32).
+struct GemmStackOutArgs {
+  const float *o, *u, *row_stats;
+  int32_t heads, head_dim;
+  float eps;
+  const void *w, *bias;
+  int32_t resid_mode;
+  const void *resid;
+  const int64_t *ids;
+  const float *resid_rowstat;
+  float *y32, *out_stats;
+  void *y;
+  int32_t y_f32, M, N, K, split;
+};
+hipError_t launch_gemm_stack_out(const GemmStackOutArgs &a, hipStream_t stream);
+bool stack_gemms_fit(int64_t M, int64_t D, int64_t HD);
+int stack_out_col_tiles(int64_t N);
+// rowstat[m] = (mean, 1/sqrt(var + eps)) of row m from its column tiles' (mean, M2) (tile c holds
+// min(256, N - 256 c) columns), combined in tile order.
+hipError_t launch_row_stats_combine(const float *tile_stats, float *rowstat, int M, int N, float eps,
+                                    hipStream_t stream);
+
 // ---- layer backward, HBM-bound pieces
 // dr = LN'(r) dy in place over r: r fp32 [M][N] (the pre-LayerNorm sum), dy [M][N] fp32 if dy_f32 else bf16.
 struct LnBwdArgs {

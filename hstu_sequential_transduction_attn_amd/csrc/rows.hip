@@ -74,6 +74,25 @@ __global__ void __launch_bounds__(256) gather_kernel(const u32x4 *__restrict__ t
   out[i] = table[ids[t] * chunks_per_row + c];
 }
 
+// Chan's pairwise combination of per-tile (mean, M2) in tile order; one thread per row.
+__global__ void __launch_bounds__(256) row_stats_combine_kernel(const float *__restrict__ ts, float *__restrict__ rs,
+                                                                int M, int N, int tiles, float eps) {
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  if (m >= M) return;
+  const float *t = ts + (int64_t)m * tiles * 2;
+  float n = 0.0f, mean = 0.0f, m2 = 0.0f;
+  for (int c = 0; c < tiles; ++c) {
+    const float nc = (float)min(256, N - 256 * c);
+    const float d = t[2 * c] - mean;
+    const float tot = n + nc;
+    mean += d * (nc / tot);
+    m2 += t[2 * c + 1] + d * d * (n * nc / tot);
+    n = tot;
+  }
+  rs[2 * (int64_t)m] = mean;
+  rs[2 * (int64_t)m + 1] = 1.0f / sqrtf(m2 / (float)N + eps);
+}
+
 // Row width is bounded by 256 * MAXC (checked on the host: width <= 4096, width % 4 == 0).
 template <typename TO>
 hipError_t launch_ln(const RowLnArgs &a, hipStream_t s) {
@@ -90,6 +109,14 @@ hipError_t launch_ln(const RowLnArgs &a, hipStream_t s) {
 hipError_t launch_row_layernorm(const RowLnArgs &a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   return a.out_f32 ? launch_ln<float>(a, s) : launch_ln<__bf16>(a, s);
+}
+
+hipError_t launch_row_stats_combine(const float *tile_stats, float *rowstat, int M, int N, float eps, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int tiles = (N + 255) / 256;
+  hipLaunchKernelGGL(row_stats_combine_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, tile_stats,
+                     rowstat, M, N, tiles, eps);
+  return hipGetLastError();
 }
 
 hipError_t launch_gather_rows(const void *table, int64_t table_rows, int32_t row_bytes, const int64_t *ids, int32_t T,

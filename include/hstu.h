@@ -1,6 +1,7 @@
 /*
- * hstu.h -- C ABI of libhstu, the MI355X (gfx950) HSTU layer: forward, cached-history candidate
- * scoring, and the backward of the attention and of the whole layer.
+ * hstu.h -- C ABI of libhstu, the MI355X (gfx950) HSTU layer: forward, a fused layer stack over
+ * embedding-table input, cached-history candidate scoring, and the backward of the attention and of
+ * the whole layer.
  *
  * What it computes.  The HSTU layer as the pages describe it: "DLRMv4：MLPerfの推薦システム訓練
  * ベンチマークがシーケンス化時代へ", section "モデルアーキテクチャ：HSTUが従来の特徴インタラクション
@@ -50,7 +51,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 4
+#define HSTU_ABI_VERSION 5
 
 typedef enum {
   HSTU_OK = 0,
@@ -221,6 +222,32 @@ hstu_status_t hstu_layer_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
                              const hstu_layer_weights_t *w, hstu_dtype_t dtype, hstu_dtype_t x_dtype,
                              const void *x, hstu_dtype_t y_dtype, void *y, void *workspace,
                              size_t workspace_bytes, void *stream);
+
+/* Workspace needed by hstu_stack_fwd (bytes).  Depends only on host fields. */
+size_t hstu_stack_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_t *descs,
+                                  const hstu_layer_weights_t *weights, int32_t num_layers, hstu_dtype_t dtype);
+
+/*
+ * A stack of num_layers layers over rows of an embedding table ("DLRMv4" page, section on the model
+ * architecture: the layer input is looked up from embedding tables; the layers are stacked with a
+ * residual and a LayerNorm between them):
+ *   x_0[t] = table[ids[t]]  (table[t] when ids is NULL)
+ *   x_{l+1} = LN(x_l + branch_l(x_l)) for l < num_layers - 1,   y = x_L-1 + branch_L-1(x_L-1),
+ * with branch_l the layer of hstu_layer_fwd (weights[l], descs[l]; weights[l].ln_output is not read).
+ * Every layer has the same jag, d_model, num_heads, head_dim and mask; tables and weights are per layer.
+ * table: [table_rows][D] dtype (device); ids: [T] int64 in [0, table_rows) (device) or NULL (then
+ * table_rows >= T); y: [T][D], y_dtype in {HSTU_F32, dtype} (device), may not overlap the table.
+ * bf16 with large-tile shapes: the gather is done by layer 0's projection and output GEMMs while they
+ * load their operands (x_0 is never stored); each output GEMM before a LayerNorm writes its fp32 sum
+ * and per-row statistics of every 256-column tile, and the next layer applies the LayerNorm while its
+ * GEMMs load that sum (x_{l+1} is never stored).  Otherwise the call gathers x_0 and runs
+ * hstu_layer_fwd per layer with fp32 activations in between.  Both keep the residual stream in fp32.
+ * Errors: as hstu_layer_fwd; layers that differ in d_model, num_heads, head_dim or mask are rejected.
+ */
+hstu_status_t hstu_stack_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *descs,
+                             const hstu_layer_weights_t *weights, int32_t num_layers, hstu_dtype_t dtype,
+                             const void *table, int64_t table_rows, const int64_t *ids, hstu_dtype_t y_dtype,
+                             void *y, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Gradients of one layer's parameters: fp32 (device), written, not accumulated into. */
 typedef struct {

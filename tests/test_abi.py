@@ -39,7 +39,7 @@ def _attn(jag, desc, in_dt=L.HSTU_BF16, out_dt=L.HSTU_BF16, q=P16 + 0x10000, k=P
 
 def test_exports_every_declared_symbol():
     names = L.exported_functions_in_header()
-    assert len(names) == 14
+    assert len(names) == 16
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib()
-    assert lib.hstu_abi_version() == 4
+    assert lib.hstu_abi_version() == 5
     assert lib.hstu_status_string(OK) == b"HSTU_OK"
     assert lib.hstu_status_string(WS_SMALL) == b"HSTU_ERR_WORKSPACE_TOO_SMALL"
     assert lib.hstu_status_string(99) == b"HSTU_STATUS_UNKNOWN"
@@ -311,3 +311,41 @@ def test_layer_bwd_workspace_sizing():
     assert st == WS_SMALL and str(need) in msg
     f32 = lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), L.HSTU_F32)
     assert f32 > need
+
+
+def _stack(jag, descs, ws, L, dt=L.HSTU_BF16, table=P16 + 0x1000000, rows=1000, ids=P16 + 0x5000, y_dt=L.HSTU_BF16,
+           y=P16 + 0x8000000, wsp=P16 + 0x10000000, nws=1 << 40):
+    lib = _lib()
+    st = lib.hstu_stack_fwd(ctypes.byref(jag), descs, ws, L, dt, table, rows, ids, y_dt, y, wsp, nws, None)
+    return st, lib.hstu_last_error().decode()
+
+
+def test_stack_argument_errors():
+    jag = _jag(B=2, T=100, max_len=60)
+    mkd = lambda n, **kw: (L.AttnDescT * n)(*[_desc(**{**dict(H=2, Dh=64, P=32, Tb=32), **kw}) for _ in range(n)])
+    mkw = lambda n, **kw: (L.LayerWeightsT * n)(*[L.LayerWeightsT(**{**dict(
+        d_model=256, w_uvqk=P16 + 0x400000, b_uvqk=None, w_out=P16 + 0x500000, b_out=None, ln_eps=1e-6,
+        ln_output=0, act_split=0), **kw}) for _ in range(n)])
+    assert _stack(jag, mkd(2), mkw(2), 0)[0] == INVALID                      # no layers
+    descs = mkd(2)
+    descs[1].head_dim = 32
+    st, msg = _stack(jag, descs, mkw(2), 2)
+    assert st == UNSUPPORTED and "layer 1" in msg
+    ws = mkw(2)
+    ws[1].d_model = 128
+    st, msg = _stack(jag, mkd(2), ws, 2)
+    assert st == INVALID and "d_model" in msg
+    ws = mkw(2)
+    ws[1].w_out = None
+    assert _stack(jag, mkd(2), ws, 2)[0] == INVALID
+    assert _stack(jag, mkd(2), mkw(2), 2, y_dt=7)[0] == UNSUPPORTED
+    st, msg = _stack(jag, mkd(2), mkw(2), 2, ids=None, rows=50)               # identity rows need rows >= T
+    assert st == INVALID and "table_rows" in msg
+    st, msg = _stack(jag, mkd(2), mkw(2), 2, y=P16 + 0x1000000 + 512)          # y on top of the table
+    assert st == INVALID and "overlaps" in msg
+    need = _lib().hstu_stack_workspace_bytes(ctypes.byref(jag), mkd(2), mkw(2), 2, L.HSTU_BF16)
+    assert need > 0
+    st, msg = _stack(jag, mkd(2), mkw(2), 2, nws=need - 1)
+    assert st == WS_SMALL and str(need) in msg
+    # zero tokens: nothing to do
+    assert _stack(_jag(B=2, T=0, max_len=0), mkd(2), mkw(2), 2, table=None, y=None, wsp=None, nws=0)[0] == OK
