@@ -32,11 +32,16 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0          # MI355X dense bf16 MFMA (no sparsity)
 HBM_PEAK_GBS = 8000.0
 METRIC = "HSTU attn fwd TFLOP/s (causal, jagged) at L=8192 bf16; % MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_L8192_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "hstu_sequential_transduction_attn_amd", "csrc", "attn_fwd.hip")
+# every source the attention forward kernel is compiled from (its traffic figure is void once any changes)
+KERNEL_SOURCES = [os.path.join(ROOT, "hstu_sequential_transduction_attn_amd", "csrc", f)
+                  for f in ("attn_fwd.hip", "attn_common.hpp", "device_common.hpp", "kernels.h")]
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():

@@ -9,6 +9,13 @@
 //    section) computed while the A operand is loaded: the rows' LayerNorm statistics are combined
 //    from the per-head partial statistics the attention kernel stored next to O, and each A element
 //    is (o - mean) * rstd * u.  G is never stored.
+//  * stack:       the projection and output GEMMs of a layer stack over embedding-table rows (the layer
+//    input is looked up from embedding tables, same section): layer 0 reads its operand and residual
+//    rows through the row ids (the gather is never stored); a layer followed by a LayerNorm writes its
+//    fp32 sum with per-row statistics of each 256-column tile, and the next layer normalises those rows
+//    while loading them (the LayerNorm output is never stored).
+//  * plain:       c = A B^T (+ residual), optionally split over K into fp32 partial products that are
+//    summed in split order (the weight gradients of the layer backward, whose K is the token count).
 //
 // Both operands are K-contiguous (row-major activations, torch-Linear [out][in] weights), which is the
 // native operand form of the 32x32 MFMAs.  Two kernels:
