@@ -72,13 +72,14 @@ __device__ __forceinline__ void adjust_block_keys(floatx16 &s, const KeyCtx &c, 
   }
 }
 
-// One 32-query block of a tile for one wave.  BODY: kUniform (bias c1 folded into the exponent),
-// kGen64 (per-score bias), kGen64M (per-score bias and mask).
-template <typename T, int DH, int BODY>
+// One 32-query block of a tile for one wave.  body: kUniform (bias c1 folded into the exponent),
+// kGen64 (per-score bias), kGen64M (per-score bias and mask).  Every class shares one copy of the MFMA
+// code, so the dK^T and dV^T accumulators stay in the same registers whatever the class.
+template <typename T, int DH>
 __device__ __forceinline__ void dkdv_block(OAcc<Layout<T, DH>::kDB> &dk, OAcc<Layout<T, DH>::kDB> &dv,
                                            const typename QFrag<T>::type (&kf)[Layout<T, DH>::kQSteps],
                                            const typename QFrag<T>::type (&vf)[Layout<T, DH>::kQSteps],
-                                           const KeyCtx &c, float c1, int qb, int lane) {
+                                           const KeyCtx &c, int body, float c1, int qb, int lane) {
   using L = Layout<T, DH>;
   const int l32 = lane & 31, half = lane >> 5;
   const HSTU_LDS char *lQ = c.stage + L::kOffK;
@@ -86,7 +87,8 @@ __device__ __forceinline__ void dkdv_block(OAcc<Layout<T, DH>::kDB> &dk, OAcc<La
   floatx16 s, dp;
   score_block<T, DH>(s, lQ, qb, l32, half, kf);
   score_block<T, DH>(dp, lG, qb, l32, half, vf);
-  if constexpr (BODY != kUniform) adjust_block_keys<T, DH, BODY == kGen64M>(s, c, qb, half);
+  if (body == kGen64) adjust_block_keys<T, DH, false>(s, c, qb, half);
+  else if (body == kGen64M) adjust_block_keys<T, DH, true>(s, c, qb, half);
   float a[16], ds[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -100,20 +102,23 @@ __device__ __forceinline__ void dkdv_block(OAcc<Layout<T, DH>::kDB> &dk, OAcc<La
   av_block_in<T, DH, true>(dk, ds, lQ, qb, lane);
 }
 
-template <typename T, int DH, int BODY>
+template <typename T, int DH>
 __device__ __forceinline__ void dkdv_tile(OAcc<Layout<T, DH>::kDB> &dk, OAcc<Layout<T, DH>::kDB> &dv,
                                           const typename QFrag<T>::type (&kf)[Layout<T, DH>::kQSteps],
                                           const typename QFrag<T>::type (&vf)[Layout<T, DH>::kQSteps],
-                                          const KeyCtx &c, float c1, int lane) {
-  dkdv_block<T, DH, BODY>(dk, dv, kf, vf, c, c1, 0, lane);
-  dkdv_block<T, DH, BODY>(dk, dv, kf, vf, c, c1, 1, lane);
+                                          const KeyCtx &c, int body, float c1, int lane) {
+  dkdv_block<T, DH>(dk, dv, kf, vf, c, body, c1, 0, lane);
+  dkdv_block<T, DH>(dk, dv, kf, vf, c, body, c1, 1, lane);
 }
 
 __device__ __forceinline__ int64_t smin64(int64_t a, int64_t b) { return a < b ? a : b; }
 __device__ __forceinline__ int64_t smax64(int64_t a, int64_t b) { return a > b ? a : b; }
 
+// bf16: two waves per SIMD (<= 256 registers; at Dh = 128 a few spill); fp32 operands take twice the
+// fragment registers and run one wave per SIMD.
 template <typename T, int DH>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, sizeof(T) == 2 ? 2 : 1)))
 attn_bwd_dkdv_kernel(const AttnArgs p, const int n_kblocks) {
   using L = Layout<T, DH>;
   using Frag = typename QFrag<T>::type;
@@ -276,9 +281,7 @@ attn_bwd_dkdv_kernel(const AttnArgs p, const int n_kblocks) {
     if (body != kNone) {
       c.q0 = q0;
       c.stage = smem + (i % L::kStages) * L::kStageBytes;
-      if (body == kUniform) dkdv_tile<T, DH, kUniform>(dk, dv, kf, vf, c, c1, lane);
-      else if (body == kGen64) dkdv_tile<T, DH, kGen64>(dk, dv, kf, vf, c, 0.0f, lane);
-      else dkdv_tile<T, DH, kGen64M>(dk, dv, kf, vf, c, 0.0f, lane);
+      dkdv_tile<T, DH>(dk, dv, kf, vf, c, body, c1, lane);
     }
   }
 
