@@ -7,11 +7,9 @@ magnitudes never reach), so the outputs must be exactly twice the originals, bit
 that mixed up rows, dropped a tile, or read memory it does not own would break this equality or the
 run-to-run determinism checked alongside it.
 """
-import numpy as np
 import pytest
 
 from hstu_sequential_transduction_attn_amd import configs as C
-from hstu_sequential_transduction_attn_amd import inputs as I
 
 from _util import dev, jag_dev
 
@@ -49,7 +47,8 @@ def test_attn_bwd_L8192_linear_in_d_out_exactly():
     jd = jag_dev(case.jagged)
     q, k, v = dev(case.q), dev(case.k), dev(case.v)
     wp, wt = dev(case.rab.pos_bias), dev(case.rab.time_bias)
-    g = torch.randn(q.shape, device="cuda", generator=torch.Generator(device="cuda").manual_seed(11)).to(torch.bfloat16)
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    g = torch.randn(q.shape, device="cuda", generator=gen).to(torch.bfloat16)
     run = lambda gg: ops.attn_bwd(jd["seq_offsets"], jd["timestamps"], q, k, v, gg, wp, wt,
                                   max_seq_len=jd["max_seq_len"])
     r1 = run(g)
