@@ -321,7 +321,42 @@ def layer_backward(dev):
         print(f"[extended] layer_bwd {name}: {ms:.3f} ms per backward (T={T}, D={D}, H={H}x{Dh}, forward "
               f"recomputed); {flop:.3e} algorithmic FLOP ({bwd:.3e} backward + {fwd:.3e} recompute) -> "
               f"{flop / ms / 1e9:.1f} TFLOP/s", file=sys.stderr, flush=True)
-        del ws, x, dy, dx, grads
+
+        # one layer's training step both ways: forward + backward that recomputes the forward, and
+        # forward that keeps its activations + backward that reads them
+        fkw = dict(max_seq_len=j.max_seq_len, ln_eps=L.ln_eps, ln_output=ln_output, mask=j.mask, act_split=stream32)
+        y = torch.empty_like(x)
+        fws = torch.empty(max(ops.layer_workspace_bytes(x, offs, tau, w1, w2, wp, wt, H, Dh, max_seq_len=j.max_seq_len,
+                                                        ln_output=ln_output, mask=j.mask, act_split=stream32), 1),
+                          dtype=torch.uint8, device=dev)
+        nsv = ops.layer_saved_bytes(x, offs, tau, w1, w2, wp, wt, H, Dh, max_seq_len=j.max_seq_len,
+                                    ln_output=ln_output, mask=j.mask)
+        saved = torch.empty(nsv, dtype=torch.uint8, device=dev)
+
+        def step_recompute():
+            ops.layer_fwd(x, offs, tau, w1, w2, wp, wt, H, Dh, workspace=fws, y=y, **fkw)
+            run()
+
+        def step_saved():
+            ops.layer_fwd(x, offs, tau, w1, w2, wp, wt, H, Dh, y=y, saved=saved, **fkw)
+            ops.layer_bwd(x, dy, offs, tau, w1, w2, wp, wt, H, Dh, workspace=ws, dx=dx, grads=grads, saved=saved,
+                          **fkw)
+
+        res = {}
+        for label, fn in (("recompute", step_recompute), ("saved", step_saved)):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(5):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[label] = e0.elapsed_time(e1) / 5
+        print(f"[extended] layer_train_step {name}: forward + backward {res['recompute']:.3f} ms recomputing the "
+              f"forward, {res['saved']:.3f} ms from saved activations ({nsv / 1e9:.2f} GB kept)",
+              file=sys.stderr, flush=True)
+        del ws, x, dy, dx, grads, saved, fws, y
 
 
 def attn_backward(dev):

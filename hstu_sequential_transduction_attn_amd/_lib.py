@@ -114,6 +114,17 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_stack_fwd.restype = ctypes.c_int
     lib.hstu_stack_fwd.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT), ctypes.POINTER(LayerWeightsT),
                                    c_i32, ctypes.c_int, c_vp, c_i64, c_vp, ctypes.c_int, c_vp, c_vp, c_sz, c_vp]
+    lib.hstu_layer_saved_bytes.restype = c_sz
+    lib.hstu_layer_saved_bytes.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT),
+                                           ctypes.POINTER(LayerWeightsT), ctypes.c_int]
+    lib.hstu_layer_fwd_save.restype = ctypes.c_int
+    lib.hstu_layer_fwd_save.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT),
+                                        ctypes.POINTER(LayerWeightsT), ctypes.c_int, ctypes.c_int, c_vp, ctypes.c_int,
+                                        c_vp, c_vp, c_sz, c_vp]
+    lib.hstu_layer_bwd_saved.restype = ctypes.c_int
+    lib.hstu_layer_bwd_saved.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT),
+                                         ctypes.POINTER(LayerWeightsT), ctypes.c_int, ctypes.c_int, c_vp, ctypes.c_int,
+                                         c_vp, c_vp, ctypes.POINTER(LayerGradsT), c_vp, c_sz, c_vp, c_sz, c_vp]
     lib.hstu_gather_rows.restype = ctypes.c_int
     lib.hstu_gather_rows.argtypes = [c_vp, c_i64, c_i32, ctypes.c_int, c_vp, c_i32, c_vp, c_vp]
     if path is None:
@@ -240,9 +251,11 @@ def layer_workspace_bytes(x, seq_offsets, timestamps, w_uvqk, w_out, pos_bias, t
 def layer_fwd(x, seq_offsets, timestamps, w_uvqk, w_out, pos_bias, time_bias, num_heads: int, head_dim: int, *,
               max_seq_len: int, b_uvqk=None, b_out=None, ln_eps: float = 1e-6, ln_output: bool = False,
               mask: int = MASK_CAUSAL, num_candidates=None, attn_scale=None, y_dtype: Optional[torch.dtype] = None,
-              act_split: bool = False, workspace=None, y=None, stream=None):
+              act_split: bool = False, workspace=None, y=None, saved=None, stream=None):
     """y = hstu_layer_fwd(...): x [T, D] (fp32 or the weights' dtype); returns y [T, D] in y_dtype
-    (default: x's dtype).  The weights' dtype (bf16 or f32) sets the MFMA operand type."""
+    (default: x's dtype).  The weights' dtype (bf16 or f32) sets the MFMA operand type.  With `saved`
+    (a uint8 device tensor of layer_saved_bytes), hstu_layer_fwd_save keeps the activations there for
+    layer_bwd(..., saved=saved)."""
     lib = load_library()
     T, D = x.shape
     if y is None:
@@ -252,6 +265,10 @@ def layer_fwd(x, seq_offsets, timestamps, w_uvqk, w_out, pos_bias, time_bias, nu
     w = LayerWeightsT(D, _ptr(w_uvqk), _ptr(b_uvqk), _ptr(w_out), _ptr(b_out), float(ln_eps), int(bool(ln_output)),
                       int(bool(act_split)))
     dt = _dtype_code(w_uvqk)
+    if saved is not None:
+        _check(lib.hstu_layer_fwd_save(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), dt, _dtype_code(x),
+                                       _ptr(x), _dtype_code(y), _ptr(y), _ptr(saved), saved.numel(), _stream(stream)))
+        return y
     nws = int(lib.hstu_layer_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), dt))
     if workspace is None or workspace.numel() < nws:
         workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device)
@@ -271,10 +288,20 @@ def layer_bwd_workspace_bytes(x, seq_offsets, timestamps, w_uvqk, w_out, pos_bia
                                                   _dtype_code(w_uvqk)))
 
 
+def layer_saved_bytes(x, seq_offsets, timestamps, w_uvqk, w_out, pos_bias, time_bias, num_heads, head_dim, *,
+                      max_seq_len: int, ln_output: bool = False, mask: int = MASK_CAUSAL, num_candidates=None) -> int:
+    lib = load_library()
+    jag = make_jagged(seq_offsets, timestamps, max_seq_len, num_candidates, None)
+    desc = make_desc(num_heads, head_dim, pos_bias, time_bias, mask)
+    w = LayerWeightsT(x.shape[1], _ptr(w_uvqk), None, _ptr(w_out), None, 1e-6, int(bool(ln_output)), 0)
+    return int(lib.hstu_layer_saved_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w),
+                                          _dtype_code(w_uvqk)))
+
+
 def layer_bwd(x, dy, seq_offsets, timestamps, w_uvqk, w_out, pos_bias, time_bias, num_heads: int, head_dim: int, *,
               max_seq_len: int, b_uvqk=None, b_out=None, ln_eps: float = 1e-6, ln_output: bool = False,
               mask: int = MASK_CAUSAL, num_candidates=None, attn_scale=None, act_split: bool = False,
-              bias_grads: bool = True, workspace=None, dx=None, grads=None, stream=None):
+              bias_grads: bool = True, workspace=None, dx=None, grads=None, saved=None, stream=None):
     """hstu_layer_bwd(...): gradients of layer_fwd for the upstream gradient dy (dy's dtype is the
     gradient dtype, fp32 or the weights' dtype).  Returns a dict with dx [T, D] (dy's dtype) and fp32
     d_w_uvqk, d_b_uvqk, d_w_out, d_b_out (None unless bias_grads), d_pos_bias, d_time_bias; `grads`
@@ -299,8 +326,16 @@ def layer_bwd(x, dy, seq_offsets, timestamps, w_uvqk, w_out, pos_bias, time_bias
                         _ptr(out["d_pos_bias"]), _ptr(out["d_time_bias"]))
     dt = _dtype_code(w_uvqk)
     nws = int(lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), dt))
+    if saved is not None:   # the saved activations stand in for the workspace's recompute block
+        nws -= int(lib.hstu_layer_saved_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), dt))
     if workspace is None or workspace.numel() < nws:
         workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    if saved is not None:
+        _check(lib.hstu_layer_bwd_saved(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), dt, _dtype_code(x),
+                                        _ptr(x), _dtype_code(dy), _ptr(dy), _ptr(dx), ctypes.byref(grads),
+                                        _ptr(saved), saved.numel(), _ptr(workspace), workspace.numel(),
+                                        _stream(stream)))
+        return out
     _check(lib.hstu_layer_bwd(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), dt, _dtype_code(x), _ptr(x),
                               _dtype_code(dy), _ptr(dy), _ptr(dx), ctypes.byref(grads), _ptr(workspace),
                               workspace.numel(), _stream(stream)))

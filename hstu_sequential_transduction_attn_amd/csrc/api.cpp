@@ -476,20 +476,52 @@ hstu_status_t hstu_layer_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
 
 namespace {
 
-// Layer-backward workspace regions (256-byte aligned).  Recomputed forward: W1^T, W2^T (dtype), U
-// (fp32), V, Q, K (dtype), Z = the projection's pre-activation (dtype; overwritten by dz), O (fp32)
-// and its per-head statistics, the timestamp ranges, the pre-LayerNorm sum r (fp32, ln_output only;
-// overwritten by dr).  Backward: dg (fp32), g and dO (dtype), dQ, dK, dV (fp32), the attention
-// backward's bias-gradient bins, the token-contiguous transposes x^T, dr^T, g^T, dz^T (dtype, T padded
-// to Tp, a multiple of 32) and the split-K partial products of the weight gradients.
+// The forward activations the layer backward needs (256-byte aligned regions): U (fp32), V, Q, K
+// (dtype), Z = the projection's pre-activation (dtype; overwritten by dz), O (fp32) and its per-head
+// statistics, the timestamp ranges, the pre-LayerNorm sum r (fp32, ln_output only; overwritten by dr).
+// hstu_layer_fwd_save leaves them in the caller's saved buffer; hstu_layer_bwd recomputes them at the
+// start of its workspace.
+struct LayerSaved {
+  size_t u, v, q, k, z, o, ostat, stats, r32, total;
+};
+
+LayerSaved layer_saved(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, int64_t D, hstu_dtype_t dt,
+                       bool ln_output) {
+  LayerSaved w{};
+  const int64_t T = jag->total_tokens, B = jag->num_seqs, H = desc->num_heads;
+  const int64_t HD = H * desc->head_dim;
+  const size_t es = esize(dt);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += round_up(bytes, 256);
+    return at;
+  };
+  w.u = take((size_t)T * HD * 4);
+  w.v = take((size_t)T * HD * es);
+  w.q = take((size_t)T * HD * es);
+  w.k = take((size_t)T * HD * es);
+  w.z = take((size_t)T * 4 * HD * es);
+  w.o = take((size_t)T * HD * 4);
+  w.ostat = take((size_t)T * H * 8);
+  w.stats = take(hstu::attn_tau_stats_bytes(T, B));
+  w.r32 = take(ln_output ? (size_t)T * D * 4 : 0);
+  w.total = off;
+  return w;
+}
+
+// Layer-backward workspace regions (256-byte aligned): without saved activations, first the
+// LayerSaved block; then W1^T, W2^T (dtype), dg (fp32), g and dO (dtype), dQ, dK, dV (fp32), the
+// attention backward's bias-gradient bins, the token-contiguous transposes x^T, dr^T, g^T, dz^T
+// (dtype, T padded to Tp, a multiple of 32) and the split-K partial products of the weight gradients.
 struct LayerBwdWs {
-  size_t w1t, w2t, u, v, q, k, z, o, ostat, stats, r32, dg, g, d_o, dq, dk, dv, bins, xt, drt, gt, dzt, part, total;
+  size_t fwd, w1t, w2t, dg, g, d_o, dq, dk, dv, bins, xt, drt, gt, dzt, part, total;
   int64_t Tp;
   int split_w1, split_w2;
 };
 
 LayerBwdWs layer_bwd_ws(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, int64_t D, hstu_dtype_t dt,
-                        bool ln_output) {
+                        bool ln_output, bool with_saved = false) {
   LayerBwdWs w{};
   const int64_t T = jag->total_tokens, B = jag->num_seqs, H = desc->num_heads;
   const int64_t HD = H * desc->head_dim;
@@ -504,17 +536,9 @@ LayerBwdWs layer_bwd_ws(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, 
     off += round_up(bytes, 256);
     return at;
   };
+  w.fwd = take(with_saved ? 0 : layer_saved(jag, desc, D, dt, ln_output).total);
   w.w1t = take((size_t)4 * HD * D * es);
   w.w2t = take((size_t)HD * D * es);
-  w.u = take((size_t)T * HD * 4);
-  w.v = take((size_t)T * HD * es);
-  w.q = take((size_t)T * HD * es);
-  w.k = take((size_t)T * HD * es);
-  w.z = take((size_t)T * 4 * HD * es);
-  w.o = take((size_t)T * HD * 4);
-  w.ostat = take((size_t)T * H * 8);
-  w.stats = take(hstu::attn_tau_stats_bytes(T, B));
-  w.r32 = take(ln_output ? (size_t)T * D * 4 : 0);
   w.dg = take((size_t)T * HD * 4);
   w.g = take((size_t)T * HD * es);
   w.d_o = take((size_t)T * HD * es);
@@ -543,10 +567,61 @@ size_t hstu_layer_bwd_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_
   return layer_bwd_ws(jag, desc, w->d_model, dtype, w->ln_output != 0).total;
 }
 
-hstu_status_t hstu_layer_bwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, const hstu_layer_weights_t *w,
+namespace {
+
+// The layer forward into the LayerSaved block at fb: the projection (also storing z), the attention,
+// and the output projection where it is needed: into r (fp32) when the output LayerNorm follows, then
+// y = LN(r) if y is given; otherwise straight into y if y is given.
+hstu_status_t run_layer_forward(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, const hstu_layer_weights_t *w,
+                                hstu_dtype_t dtype, hstu_dtype_t x_dtype, const void *x, char *fb, const LayerSaved &sv,
+                                void *y, hstu_dtype_t y_dtype, hipStream_t s) {
+  const int64_t T = jag->total_tokens, D = w->d_model, H = desc->num_heads, HD = H * desc->head_dim;
+  const int dt = dtype == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
+  const int x_f32 = x_dtype == HSTU_F32;
+  const bool split = dtype == HSTU_BF16 && w->act_split != 0;
+  const bool ln_out = w->ln_output != 0;
+  hstu::GemmUvqkArgs g1{};
+  g1.x = x; g1.w = w->w_uvqk; g1.bias = w->b_uvqk;
+  g1.u = (float *)(fb + sv.u); g1.v = fb + sv.v; g1.q = fb + sv.q; g1.k = fb + sv.k; g1.z = fb + sv.z;
+  g1.M = (int32_t)T; g1.K = (int32_t)D; g1.HD = (int32_t)HD;
+  g1.dtype = dt; g1.x_f32 = x_f32; g1.split = split;
+  hipError_t e = hstu::launch_gemm_uvqk(g1, s);
+  if (e != hipSuccess) return from_hip(e, "projection GEMM launch");
+  hstu::AttnArgs a = attn_args(jag, desc);
+  a.q = fb + sv.q; a.k = fb + sv.k; a.v = fb + sv.v; a.out = fb + sv.o;
+  a.row_stride = HD; a.out_row_stride = HD;
+  a.in_dtype = dt; a.out_dtype = hstu::kF32;
+  a.tau_stats = (int64_t *)(fb + sv.stats);
+  a.row_stats = (float *)(fb + sv.ostat);
+  e = hstu::launch_attn_fwd(a, s);
+  if (e != hipSuccess) return from_hip(e, "attention launch");
+  if (!ln_out && !y) return HSTU_OK;
+  hstu::GemmOutArgs g2{};
+  g2.o = (const float *)(fb + sv.o); g2.u = (const float *)(fb + sv.u);
+  g2.row_stats = (const float *)(fb + sv.ostat);
+  g2.heads = (int32_t)H; g2.head_dim = desc->head_dim; g2.eps = w->ln_eps;
+  g2.w = w->w_out; g2.bias = w->b_out; g2.x = x;
+  g2.y = y; g2.y32 = ln_out ? (float *)(fb + sv.r32) : nullptr;
+  g2.M = (int32_t)T; g2.N = (int32_t)D; g2.K = (int32_t)HD;
+  g2.dtype = dt; g2.split = split; g2.x_f32 = x_f32; g2.y_f32 = y_dtype == HSTU_F32;
+  e = hstu::launch_gemm_out(g2, s);
+  if (e != hipSuccess) return from_hip(e, "output GEMM launch");
+  if (ln_out && y) {
+    hstu::RowLnArgs ln{};
+    ln.in = (const float *)(fb + sv.r32); ln.out = y; ln.M = (int32_t)T; ln.N = (int32_t)D;
+    ln.eps = w->ln_eps; ln.out_f32 = y_dtype == HSTU_F32;
+    e = hstu::launch_row_layernorm(ln, s);
+    if (e != hipSuccess) return from_hip(e, "output LayerNorm launch");
+  }
+  return HSTU_OK;
+}
+
+// The layer backward; saved: the activations of a hstu_layer_fwd_save call (consumed), or NULL to
+// recompute them in the workspace.
+hstu_status_t layer_bwd_impl(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, const hstu_layer_weights_t *w,
                              hstu_dtype_t dtype, hstu_dtype_t x_dtype, const void *x, hstu_dtype_t grad_dtype,
-                             const void *dy, void *dx, const hstu_layer_grads_t *grads, void *workspace,
-                             size_t workspace_bytes, void *stream) {
+                             const void *dy, void *dx, const hstu_layer_grads_t *grads, void *saved,
+                             size_t saved_bytes, void *workspace, size_t workspace_bytes, void *stream) {
   try {
     hstu_status_t st = check_jagged_desc(jag, desc);
     if (st != HSTU_OK) return st;
@@ -577,9 +652,13 @@ hstu_status_t hstu_layer_bwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
       return fail(HSTU_ERR_UNSUPPORTED, "num_pos_buckets = %d needs %zu bytes of LDS in the backward (160 KB max)",
                   desc->num_pos_buckets, lds);
     const bool ln_out = w->ln_output != 0;
-    const LayerBwdWs ws = layer_bwd_ws(jag, desc, D, dtype, ln_out);
+    const LayerSaved sv = layer_saved(jag, desc, D, dtype, ln_out);
+    const LayerBwdWs ws = layer_bwd_ws(jag, desc, D, dtype, ln_out, saved != nullptr);
     if (workspace_bytes < ws.total)
       return fail(HSTU_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, ws.total);
+    if (saved && saved_bytes < sv.total)
+      return fail(HSTU_ERR_WORKSPACE_TOO_SMALL, "saved %zu < %zu bytes", saved_bytes, sv.total);
+    if (saved && !aligned16(saved)) return fail(HSTU_ERR_INVALID_ARGUMENT, "saved must be 16-byte aligned");
     if (!workspace) return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace is NULL");
     if (!aligned16(workspace)) return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
     if (T > 0) {
@@ -592,15 +671,15 @@ hstu_status_t hstu_layer_bwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
     const void *ins[8] = {x, dy, w->w_uvqk, w->b_uvqk, w->w_out, w->b_out, desc->pos_bias, desc->time_bias};
     const size_t in_n[8] = {nx, ng, (size_t)4 * HD * D * es, (size_t)4 * HD * es, (size_t)D * HD * es, (size_t)D * es,
                             R * P * 4, R * Tb * 4};
-    const void *outs[8] = {dx, grads->d_w_uvqk, grads->d_b_uvqk, grads->d_w_out, grads->d_b_out, grads->d_pos_bias,
-                           grads->d_time_bias, workspace};
-    const size_t out_n[8] = {ng, (size_t)4 * HD * D * 4, (size_t)4 * HD * 4, (size_t)D * HD * 4, (size_t)D * 4,
-                             R * P * 4, R * Tb * 4, ws.total};
-    for (int o = 0; o < 8; ++o) {
+    const void *outs[9] = {dx, grads->d_w_uvqk, grads->d_b_uvqk, grads->d_w_out, grads->d_b_out, grads->d_pos_bias,
+                           grads->d_time_bias, workspace, saved};
+    const size_t out_n[9] = {ng, (size_t)4 * HD * D * 4, (size_t)4 * HD * 4, (size_t)D * HD * 4, (size_t)D * 4,
+                             R * P * 4, R * Tb * 4, ws.total, saved ? sv.total : 0};
+    for (int o = 0; o < 9; ++o) {
       for (int i = 0; i < 8; ++i)
         if (overlaps(outs[o], out_n[o], ins[i], in_n[i]))
-          return fail(HSTU_ERR_INVALID_ARGUMENT, "an output or the workspace overlaps an input");
-      for (int o2 = o + 1; o2 < 8; ++o2)
+          return fail(HSTU_ERR_INVALID_ARGUMENT, "an output, the workspace or the saved activations overlaps an input");
+      for (int o2 = o + 1; o2 < 9; ++o2)
         if (overlaps(outs[o], out_n[o], outs[o2], out_n[o2]))
           return fail(HSTU_ERR_INVALID_ARGUMENT, "two outputs (or an output and the workspace) overlap");
     }
@@ -617,11 +696,12 @@ hstu_status_t hstu_layer_bwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
     if (e != hipSuccess) return from_hip(e, what); \
   } while (0)
 
+    char *fb = saved ? (char *)saved : wsb + ws.fwd;   // the forward activations
     hstu::AttnArgs a = attn_args(jag, desc);
     a.row_stride = HD; a.out_row_stride = HD;
     a.in_dtype = dt;
     a.out_dtype = hstu::kF32;
-    a.tau_stats = (int64_t *)(wsb + ws.stats);
+    a.tau_stats = (int64_t *)(fb + sv.stats);
     if (T == 0) {
       // no tokens: every gradient is 0 (the attention backward clears its two tables itself)
       HSTU_TRY(hstu::launch_fill_zero(grads->d_w_uvqk, 4 * HD * D, s), "zero fill");
@@ -633,38 +713,24 @@ hstu_status_t hstu_layer_bwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
       return ok();
     }
 
-    // ---- recompute the forward
     HSTU_TRY(hstu::launch_transpose(w->w_uvqk, f32w, wsb + ws.w1t, f32w, (int)(4 * HD), (int)D, (int)(4 * HD), s),
              "W1 transpose");
     HSTU_TRY(hstu::launch_transpose(w->w_out, f32w, wsb + ws.w2t, f32w, (int)D, (int)HD, (int)D, s), "W2 transpose");
-    hstu::GemmUvqkArgs g1{};
-    g1.x = x; g1.w = w->w_uvqk; g1.bias = w->b_uvqk;
-    g1.u = (float *)(wsb + ws.u); g1.v = wsb + ws.v; g1.q = wsb + ws.q; g1.k = wsb + ws.k; g1.z = wsb + ws.z;
-    g1.M = (int32_t)T; g1.K = (int32_t)D; g1.HD = (int32_t)HD;
-    g1.dtype = dt; g1.x_f32 = x_f32; g1.split = split;
-    HSTU_TRY(hstu::launch_gemm_uvqk(g1, s), "projection GEMM launch");
-    a.q = wsb + ws.q; a.k = wsb + ws.k; a.v = wsb + ws.v; a.out = wsb + ws.o;
-    a.row_stats = (float *)(wsb + ws.ostat);
-    HSTU_TRY(hstu::launch_attn_fwd(a, s), "attention launch");
+    if (!saved) {
+      // ---- recompute the forward (z, U, V, Q, K, O and, with the output LayerNorm, r)
+      hstu_status_t r = run_layer_forward(jag, desc, w, dtype, x_dtype, x, fb, sv, nullptr, HSTU_F32, s);
+      if (r != HSTU_OK) return r;
+    }
 
     // ---- dr
     const void *dr = dy;
     int dr_f32 = g_f32;
     if (ln_out) {
-      hstu::GemmOutArgs g2{};
-      g2.o = (const float *)(wsb + ws.o); g2.u = (const float *)(wsb + ws.u);
-      g2.row_stats = (const float *)(wsb + ws.ostat);
-      g2.heads = (int32_t)H; g2.head_dim = desc->head_dim; g2.eps = w->ln_eps;
-      g2.w = w->w_out; g2.bias = w->b_out; g2.x = x;
-      g2.y = nullptr; g2.y32 = (float *)(wsb + ws.r32);
-      g2.M = (int32_t)T; g2.N = (int32_t)D; g2.K = (int32_t)HD;
-      g2.dtype = dt; g2.split = split; g2.x_f32 = x_f32; g2.y_f32 = 1;
-      HSTU_TRY(hstu::launch_gemm_out(g2, s), "output GEMM launch");
       hstu::LnBwdArgs lb{};
-      lb.r = (float *)(wsb + ws.r32); lb.dy = dy; lb.M = (int32_t)T; lb.N = (int32_t)D; lb.dy_f32 = g_f32;
+      lb.r = (float *)(fb + sv.r32); lb.dy = dy; lb.M = (int32_t)T; lb.N = (int32_t)D; lb.dy_f32 = g_f32;
       lb.eps = w->ln_eps;
       HSTU_TRY(hstu::launch_ln_bwd_rows(lb, s), "LayerNorm backward launch");
-      dr = wsb + ws.r32;
+      dr = fb + sv.r32;
       dr_f32 = 1;
     }
 
@@ -674,12 +740,13 @@ hstu_status_t hstu_layer_bwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
     pg.M = (int32_t)T; pg.N = (int32_t)HD; pg.K = (int32_t)D; pg.dtype = dt; pg.splits = 1;
     HSTU_TRY(hstu::launch_gemm_plain(pg, s), "dg GEMM launch");
     hstu::NormGateBwdArgs nb{};
-    nb.o = (const float *)(wsb + ws.o); nb.u = (const float *)(wsb + ws.u); nb.dg = (const float *)(wsb + ws.dg);
-    nb.z = wsb + ws.z; nb.g = wsb + ws.g; nb.d_o = wsb + ws.d_o;
+    nb.o = (const float *)(fb + sv.o); nb.u = (const float *)(fb + sv.u); nb.dg = (const float *)(wsb + ws.dg);
+    nb.z = fb + sv.z; nb.g = wsb + ws.g; nb.d_o = wsb + ws.d_o;
     nb.M = (int32_t)T; nb.N = (int32_t)HD; nb.dtype = dt; nb.eps = w->ln_eps;
     HSTU_TRY(hstu::launch_norm_gate_bwd(nb, s), "norm-gate backward launch");
 
     // ---- attention backward, then dz for the V, Q, K slices
+    a.q = fb + sv.q; a.k = fb + sv.k; a.v = fb + sv.v;
     a.d_out = wsb + ws.d_o;
     a.out = wsb + ws.dq; a.dk = (float *)(wsb + ws.dk); a.dv = (float *)(wsb + ws.dv);
     a.d_pos_bias = grads->d_pos_bias; a.d_time_bias = grads->d_time_bias;
@@ -688,12 +755,12 @@ hstu_status_t hstu_layer_bwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
     HSTU_TRY(hstu::launch_attn_bwd_dq(a, s), "attention backward dq launch");
     HSTU_TRY(hstu::launch_attn_bwd_dkdv(a, s), "attention backward dk/dv launch");
     HSTU_TRY(hstu::launch_silu_grad_vqk((const float *)(wsb + ws.dv), (const float *)(wsb + ws.dq),
-                                        (const float *)(wsb + ws.dk), wsb + ws.z, (int)T, (int)HD, dt, s),
+                                        (const float *)(wsb + ws.dk), fb + sv.z, (int)T, (int)HD, dt, s),
              "SiLU gradient launch");
 
     // ---- dx = dr + dz W1
     hstu::GemmPlainArgs px{};
-    px.a = wsb + ws.z; px.a_f32 = f32w; px.b = wsb + ws.w1t; px.resid = dr; px.resid_f32 = dr_f32;
+    px.a = fb + sv.z; px.a_f32 = f32w; px.b = wsb + ws.w1t; px.resid = dr; px.resid_f32 = dr_f32;
     px.c = dx; px.c_f32 = g_f32;
     px.M = (int32_t)T; px.N = (int32_t)D; px.K = (int32_t)(4 * HD); px.dtype = dt; px.splits = 1;
     HSTU_TRY(hstu::launch_gemm_plain(px, s), "dx GEMM launch");
@@ -703,7 +770,7 @@ hstu_status_t hstu_layer_bwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
     HSTU_TRY(hstu::launch_transpose(x, x_f32, wsb + ws.xt, f32w, (int)T, (int)D, Tp, s), "x transpose");
     HSTU_TRY(hstu::launch_transpose(dr, dr_f32, wsb + ws.drt, f32w, (int)T, (int)D, Tp, s), "dr transpose");
     HSTU_TRY(hstu::launch_transpose(wsb + ws.g, f32w, wsb + ws.gt, f32w, (int)T, (int)HD, Tp, s), "g transpose");
-    HSTU_TRY(hstu::launch_transpose(wsb + ws.z, f32w, wsb + ws.dzt, f32w, (int)T, (int)(4 * HD), Tp, s),
+    HSTU_TRY(hstu::launch_transpose(fb + sv.z, f32w, wsb + ws.dzt, f32w, (int)T, (int)(4 * HD), Tp, s),
              "dz transpose");
     hstu::GemmPlainArgs pw{};
     pw.a = wsb + ws.dzt; pw.a_f32 = f32w; pw.b = wsb + ws.xt; pw.c = grads->d_w_uvqk; pw.c_f32 = 1;
@@ -720,7 +787,74 @@ hstu_status_t hstu_layer_bwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
 #undef HSTU_TRY
     return ok();
   } catch (...) {
-    return fail(HSTU_ERR_DEVICE, "unexpected C++ exception in hstu_layer_bwd");
+    return fail(HSTU_ERR_DEVICE, "unexpected C++ exception in the layer backward");
+  }
+}
+
+}  // namespace
+
+hstu_status_t hstu_layer_bwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, const hstu_layer_weights_t *w,
+                             hstu_dtype_t dtype, hstu_dtype_t x_dtype, const void *x, hstu_dtype_t grad_dtype,
+                             const void *dy, void *dx, const hstu_layer_grads_t *grads, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  return layer_bwd_impl(jag, desc, w, dtype, x_dtype, x, grad_dtype, dy, dx, grads, nullptr, 0, workspace,
+                        workspace_bytes, stream);
+}
+
+hstu_status_t hstu_layer_bwd_saved(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc,
+                                   const hstu_layer_weights_t *w, hstu_dtype_t dtype, hstu_dtype_t x_dtype,
+                                   const void *x, hstu_dtype_t grad_dtype, const void *dy, void *dx,
+                                   const hstu_layer_grads_t *grads, void *saved, size_t saved_bytes, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  if (!saved) return fail(HSTU_ERR_INVALID_ARGUMENT, "saved is NULL");
+  return layer_bwd_impl(jag, desc, w, dtype, x_dtype, x, grad_dtype, dy, dx, grads, saved, saved_bytes, workspace,
+                        workspace_bytes, stream);
+}
+
+size_t hstu_layer_saved_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, const hstu_layer_weights_t *w,
+                              hstu_dtype_t dtype) {
+  if (!jag || !desc || !w || jag->total_tokens < 0 || jag->num_seqs < 0 || desc->num_heads < 1 ||
+      desc->head_dim < 1 || w->d_model < 1 || !valid_dtype(dtype))
+    return 0;
+  return layer_saved(jag, desc, w->d_model, dtype, w->ln_output != 0).total;
+}
+
+hstu_status_t hstu_layer_fwd_save(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc,
+                                  const hstu_layer_weights_t *w, hstu_dtype_t dtype, hstu_dtype_t x_dtype,
+                                  const void *x, hstu_dtype_t y_dtype, void *y, void *saved, size_t saved_bytes,
+                                  void *stream) {
+  try {
+    hstu_status_t st = check_jagged_desc(jag, desc);
+    if (st != HSTU_OK) return st;
+    if (!w) return fail(HSTU_ERR_INVALID_ARGUMENT, "weights is NULL");
+    if (!valid_dtype(dtype)) return fail(HSTU_ERR_INVALID_ARGUMENT, "dtype = %d invalid", (int)dtype);
+    if (!valid_dtype(x_dtype) || (x_dtype != dtype && x_dtype != HSTU_F32))
+      return fail(HSTU_ERR_UNSUPPORTED, "x_dtype = %d must be HSTU_F32 or dtype", (int)x_dtype);
+    if (!valid_dtype(y_dtype) || (y_dtype != dtype && y_dtype != HSTU_F32))
+      return fail(HSTU_ERR_UNSUPPORTED, "y_dtype = %d must be HSTU_F32 or dtype", (int)y_dtype);
+    const int64_t T = jag->total_tokens, D = w->d_model;
+    if (D < 1 || D % 8 != 0 || D > 4096)
+      return fail(HSTU_ERR_UNSUPPORTED, "d_model = %lld must be a multiple of 8 in [8, 4096]", (long long)D);
+    if (!(w->ln_eps > 0.0f)) return fail(HSTU_ERR_INVALID_ARGUMENT, "ln_eps must be > 0");
+    if (!w->w_uvqk || !w->w_out) return fail(HSTU_ERR_INVALID_ARGUMENT, "w_uvqk/w_out is NULL");
+    if (!aligned16(w->w_uvqk) || !aligned16(w->w_out))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "weights must be 16-byte aligned");
+    const LayerSaved sv = layer_saved(jag, desc, D, dtype, w->ln_output != 0);
+    if (saved_bytes < sv.total)
+      return fail(HSTU_ERR_WORKSPACE_TOO_SMALL, "saved %zu < %zu bytes", saved_bytes, sv.total);
+    if (T == 0) return ok();
+    if (!x || !y || !saved) return fail(HSTU_ERR_INVALID_ARGUMENT, "x/y/saved is NULL");
+    if (!aligned16(x) || !aligned16(y) || !aligned16(saved))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "x/y/saved must be 16-byte aligned");
+    const size_t nx = (size_t)T * D * esize(x_dtype), ny = (size_t)T * D * esize(y_dtype);
+    if (overlaps(x, nx, y, ny)) return fail(HSTU_ERR_INVALID_ARGUMENT, "y overlaps x");
+    if (overlaps(saved, sv.total, x, nx) || overlaps(saved, sv.total, y, ny))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "saved overlaps x or y");
+    hstu_status_t r = run_layer_forward(jag, desc, w, dtype, x_dtype, x, (char *)saved, sv, y, y_dtype,
+                                        (hipStream_t)stream);
+    return r == HSTU_OK ? ok() : r;
+  } catch (...) {
+    return fail(HSTU_ERR_DEVICE, "unexpected C++ exception in hstu_layer_fwd_save");
   }
 }
 

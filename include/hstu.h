@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 5
+#define HSTU_ABI_VERSION 6
 
 typedef enum {
   HSTU_OK = 0,
@@ -288,6 +288,41 @@ hstu_status_t hstu_layer_bwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
                              const void *x, hstu_dtype_t grad_dtype, const void *dy, void *dx,
                              const hstu_layer_grads_t *grads, void *workspace, size_t workspace_bytes,
                              void *stream);
+
+/*
+ * Bytes of the saved activations that hstu_layer_fwd_save keeps for hstu_layer_bwd_saved (the
+ * projection's pre-activation z, U, V, Q, K, the attention output O with its row statistics, and with
+ * w->ln_output the pre-LayerNorm sum).  Depends only on host fields.
+ */
+size_t hstu_layer_saved_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc,
+                              const hstu_layer_weights_t *w, hstu_dtype_t dtype);
+
+/*
+ * hstu_layer_fwd that also keeps, in the caller's `saved` buffer (device, 16-byte aligned,
+ * hstu_layer_saved_bytes long, no overlap with x or y), the activations its backward needs, so that
+ * a training step's backward need not recompute the forward (the memory of one GPU holds them for a
+ * whole stack of layers at the shipped sizes).  y is bitwise the y of hstu_layer_fwd.  The layout of
+ * `saved` is private to the library.  Errors: as hstu_layer_fwd; a short `saved` is
+ * HSTU_ERR_WORKSPACE_TOO_SMALL.
+ */
+hstu_status_t hstu_layer_fwd_save(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc,
+                                  const hstu_layer_weights_t *w, hstu_dtype_t dtype, hstu_dtype_t x_dtype,
+                                  const void *x, hstu_dtype_t y_dtype, void *y, void *saved, size_t saved_bytes,
+                                  void *stream);
+
+/*
+ * hstu_layer_bwd reading the activations that hstu_layer_fwd_save kept in `saved` (from a call with
+ * the same jag, desc, w, dtype, x_dtype and x, not modified since) instead of recomputing them.  The
+ * backward works in place on them: `saved` is consumed, its contents are undefined afterwards.  The
+ * workspace needs hstu_layer_bwd_workspace_bytes - hstu_layer_saved_bytes bytes.  Results are bitwise
+ * those of hstu_layer_bwd.  Errors: as hstu_layer_bwd; a NULL or short `saved`, or one that overlaps
+ * an input, an output or the workspace, is an error.
+ */
+hstu_status_t hstu_layer_bwd_saved(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc,
+                                   const hstu_layer_weights_t *w, hstu_dtype_t dtype, hstu_dtype_t x_dtype,
+                                   const void *x, hstu_dtype_t grad_dtype, const void *dy, void *dx,
+                                   const hstu_layer_grads_t *grads, void *saved, size_t saved_bytes, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 /*
  * Embedding gather (input staging before the first layer):  out[t][:] = table[ids[t]][:].

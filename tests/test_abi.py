@@ -39,7 +39,7 @@ def _attn(jag, desc, in_dt=L.HSTU_BF16, out_dt=L.HSTU_BF16, q=P16 + 0x10000, k=P
 
 def test_exports_every_declared_symbol():
     names = L.exported_functions_in_header()
-    assert len(names) == 16
+    assert len(names) == 19
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib()
-    assert lib.hstu_abi_version() == 5
+    assert lib.hstu_abi_version() == 6
     assert lib.hstu_status_string(OK) == b"HSTU_OK"
     assert lib.hstu_status_string(WS_SMALL) == b"HSTU_ERR_WORKSPACE_TOO_SMALL"
     assert lib.hstu_status_string(99) == b"HSTU_STATUS_UNKNOWN"
@@ -349,3 +349,41 @@ def test_stack_argument_errors():
     assert st == WS_SMALL and str(need) in msg
     # zero tokens: nothing to do
     assert _stack(_jag(B=2, T=0, max_len=0), mkd(2), mkw(2), 2, table=None, y=None, wsp=None, nws=0)[0] == OK
+
+
+def test_layer_saved_sizes_and_errors():
+    lib = _lib()
+    jag, desc = _jag(B=2, T=100, max_len=60), _desc(H=2, Dh=64, P=32, Tb=32)
+    w = L.LayerWeightsT(256, P16 + 0x400000, None, P16 + 0x500000, None, 1e-6, 0, 0)
+    w_ln = L.LayerWeightsT(256, P16 + 0x400000, None, P16 + 0x500000, None, 1e-6, 1, 0)
+    sv = lib.hstu_layer_saved_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), L.HSTU_BF16)
+    sv_ln = lib.hstu_layer_saved_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w_ln), L.HSTU_BF16)
+    bw = lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), L.HSTU_BF16)
+    assert 0 < sv < bw and sv % 256 == 0
+    assert sv_ln >= sv + 100 * 256 * 4              # the pre-LayerNorm sum is kept only with the LayerNorm
+    assert sv >= 100 * 4 * 128 * 2                   # at least the projection's pre-activation z
+
+    def fwd(saved=P16 + 0x10000000, nsv=1 << 30, y=P16 + 0x200000):
+        st = lib.hstu_layer_fwd_save(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), L.HSTU_BF16, L.HSTU_BF16,
+                                     P16 + 0x100000, L.HSTU_BF16, y, saved, nsv, None)
+        return st, lib.hstu_last_error().decode()
+    st, msg = fwd(nsv=sv - 1)
+    assert st == WS_SMALL and str(sv) in msg
+    assert fwd(saved=None)[0] == INVALID
+    st, msg = fwd(saved=P16 + 0x100000 + 64)         # saved on top of x
+    assert st == INVALID and "overlaps" in msg
+
+    g = L.LayerGradsT(P16 + 0x600000, None, P16 + 0x700000, None, P16 + 0x800000, P16 + 0x810000)
+
+    def bwd(saved=P16 + 0x10000000, nsv=1 << 30, ws=P16 + 0x40000000, nws=1 << 30):
+        st = lib.hstu_layer_bwd_saved(ctypes.byref(jag), ctypes.byref(desc), ctypes.byref(w), L.HSTU_BF16,
+                                      L.HSTU_BF16, P16 + 0x100000, L.HSTU_BF16, P16 + 0x200000, P16 + 0x300000,
+                                      ctypes.byref(g), saved, nsv, ws, nws, None)
+        return st, lib.hstu_last_error().decode()
+    assert bwd(saved=None)[0] == INVALID
+    st, msg = bwd(nsv=sv - 1)
+    assert st == WS_SMALL and "saved" in msg
+    st, msg = bwd(nws=bw - sv - 1)
+    assert st == WS_SMALL
+    st, msg = bwd(saved=P16 + 0x40000000 + 256)      # saved on top of the workspace
+    assert st == INVALID and "overlap" in msg

@@ -162,3 +162,33 @@ def test_layer_bwd_is_bitwise_deterministic():
     b = _gpu(case, dy, True)
     for name in NAMES:
         assert np.array_equal(a[name], b[name]), name
+
+
+@pytest.mark.parametrize("dtype,ln_output", [("f32", True), ("bf16", False), ("bf16", True)])
+def test_layer_bwd_from_saved_activations_is_bitwise_the_recompute(dtype, ln_output):
+    """hstu_layer_fwd_save's y is hstu_layer_fwd's, and hstu_layer_bwd_saved's gradients are
+    hstu_layer_bwd's, bit for bit (the recompute path is the one held to the oracle above)."""
+    from hstu_sequential_transduction_attn_amd import _lib as ops
+    print(f"\n[case] layer bwd from saved activations {dtype} ln_output={ln_output}", flush=True)
+    rng = np.random.default_rng(1370)
+    lengths = [int(v) for v in rng.integers(1, 700, size=16)] + [0, 1]
+    D, H, Dh = (64, 2, 32) if dtype == "f32" else (256, 2, 128)
+    case = I.jagged_layer_case("lbwds", 1370, lengths, D=D, H=H, Dh=Dh, P=64, Tb=64, dtype=dtype, bias_std=0.2)
+    L = case.layers[0]
+    jd = jag_dev(case.jagged)
+    x = dev(case.x)
+    dy = dev(_dy(case, 1371, dtype))
+    args = (jd["seq_offsets"], jd["timestamps"], dev(L.w_uvqk), dev(L.w_out), dev(L.rab.pos_bias),
+            dev(L.rab.time_bias), case.num_heads, case.head_dim)
+    kw = dict(max_seq_len=jd["max_seq_len"], b_uvqk=dev(L.b_uvqk), b_out=dev(L.b_out), ln_eps=L.ln_eps,
+              ln_output=ln_output)
+    y_plain = ops.layer_fwd(x, *args, **kw)
+    nsv = ops.layer_saved_bytes(x, *args, max_seq_len=jd["max_seq_len"], ln_output=ln_output)
+    saved = torch.empty(nsv, dtype=torch.uint8, device="cuda")
+    y_saved = ops.layer_fwd(x, *args, saved=saved, **kw)
+    want = ops.layer_bwd(x, dy, *args, **kw)
+    got = ops.layer_bwd(x, dy, *args, saved=saved, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y_plain, y_saved), "forward with saved activations differs"
+    for name in NAMES:
+        assert torch.equal(got[name], want[name]), f"{name}: backward from saved activations differs"
