@@ -511,11 +511,11 @@ LayerSaved layer_saved(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, i
 }
 
 // Layer-backward workspace regions (256-byte aligned): without saved activations, first the
-// LayerSaved block; then W1^T, W2^T (dtype), dg (fp32), g and dO (dtype), dQ, dK, dV (fp32), the
-// attention backward's bias-gradient bins, the token-contiguous transposes x^T, dr^T, g^T, dz^T
+// LayerSaved block; then W1^T, W2^T (dtype), dg (fp32), g and dO (dtype), the attention backward's
+// bias-gradient bins, the token-contiguous transposes x^T, dr^T, g^T, dz^T
 // (dtype, T padded to Tp, a multiple of 32) and the split-K partial products of the weight gradients.
 struct LayerBwdWs {
-  size_t fwd, w1t, w2t, dg, g, d_o, dq, dk, dv, bins, xt, drt, gt, dzt, part, total;
+  size_t fwd, w1t, w2t, dg, g, d_o, bins, xt, drt, gt, dzt, part, total;
   int64_t Tp;
   int split_w1, split_w2;
 };
@@ -542,9 +542,6 @@ LayerBwdWs layer_bwd_ws(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, 
   w.dg = take((size_t)T * HD * 4);
   w.g = take((size_t)T * HD * es);
   w.d_o = take((size_t)T * HD * es);
-  w.dq = take((size_t)T * HD * 4);
-  w.dk = take((size_t)T * HD * 4);
-  w.dv = take((size_t)T * HD * 4);
   w.bins = take((size_t)hstu::attn_bwd_partial_floats(B, H, jag->max_seq_len, desc->num_pos_buckets) * 4);
   w.xt = take((size_t)D * w.Tp * es);
   w.drt = take((size_t)D * w.Tp * es);
@@ -745,18 +742,18 @@ hstu_status_t layer_bwd_impl(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
     nb.M = (int32_t)T; nb.N = (int32_t)HD; nb.dtype = dt; nb.eps = w->ln_eps;
     HSTU_TRY(hstu::launch_norm_gate_bwd(nb, s), "norm-gate backward launch");
 
-    // ---- attention backward, then dz for the V, Q, K slices
+    // ---- attention backward, whose epilogues turn dV, dQ, dK into the rest of dz in place over z
     a.q = fb + sv.q; a.k = fb + sv.k; a.v = fb + sv.v;
     a.d_out = wsb + ws.d_o;
-    a.out = wsb + ws.dq; a.dk = (float *)(wsb + ws.dk); a.dv = (float *)(wsb + ws.dv);
+    a.out = nullptr; a.dk = nullptr; a.dv = nullptr;
+    char *zb = fb + sv.z;
+    a.z_v = zb + (size_t)HD * es; a.z_q = zb + (size_t)2 * HD * es; a.z_k = zb + (size_t)3 * HD * es;
+    a.z_row_stride = 4 * HD;
     a.d_pos_bias = grads->d_pos_bias; a.d_time_bias = grads->d_time_bias;
     a.partial = (float *)(wsb + ws.bins);
     a.row_stats = nullptr;
     HSTU_TRY(hstu::launch_attn_bwd_dq(a, s), "attention backward dq launch");
     HSTU_TRY(hstu::launch_attn_bwd_dkdv(a, s), "attention backward dk/dv launch");
-    HSTU_TRY(hstu::launch_silu_grad_vqk((const float *)(wsb + ws.dv), (const float *)(wsb + ws.dq),
-                                        (const float *)(wsb + ws.dk), fb + sv.z, (int)T, (int)HD, dt, s),
-             "SiLU gradient launch");
 
     // ---- dx = dr + dz W1
     hstu::GemmPlainArgs px{};

@@ -286,7 +286,21 @@ attn_bwd_dkdv_kernel(const AttnArgs p, const int n_kblocks) {
   }
 
   // ---- epilogue: dK^T / dV^T element e of dh block db is dh = 32*db + 8*(e/4) + 4*half + e%4
-  if (my_valid) {
+  if (my_valid && p.z_q) {
+    T *kz = (T *)p.z_k + (int64_t)(o0 + my_k) * p.z_row_stride + h * DH;
+    T *vz = (T *)p.z_v + (int64_t)(o0 + my_k) * p.z_row_stride + h * DH;
+#pragma unroll
+    for (int db = 0; db < L::kDB; ++db)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const float gk[4] = {dk.d[db][4 * e4 + 0] * cb, dk.d[db][4 * e4 + 1] * cb, dk.d[db][4 * e4 + 2] * cb,
+                             dk.d[db][4 * e4 + 3] * cb};
+        const float gv[4] = {dv.d[db][4 * e4 + 0] * cb, dv.d[db][4 * e4 + 1] * cb, dv.d[db][4 * e4 + 2] * cb,
+                             dv.d[db][4 * e4 + 3] * cb};
+        silu_grad_store4(kz + 32 * db + 8 * e4 + 4 * half, gk);
+        silu_grad_store4(vz + 32 * db + 8 * e4 + 4 * half, gv);
+      }
+  } else if (my_valid) {
     float *krow = p.dk + (int64_t)(o0 + my_k) * p.out_row_stride + h * DH;
     float *vrow = p.dv + (int64_t)(o0 + my_k) * p.out_row_stride + h * DH;
 #pragma unroll

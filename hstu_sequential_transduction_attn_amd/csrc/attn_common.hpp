@@ -239,5 +239,17 @@ __device__ __forceinline__ void av_block(OAcc<Layout<T, DH>::kDB> &oacc, const f
   av_block_in<T, DH, false>(oacc, a, lV, kb, lane);
 }
 
+// dz = g * SiLU'(z) for four consecutive elements, in place over z (the layer backward's gradient of
+// the projection's pre-activation); SiLU'(z) = sigma (1 + z (1 - sigma)), sigma = 1 / (1 + 2^(-z log2 e)).
+template <typename T>
+__device__ __forceinline__ void silu_grad_store4(T *z, const float (&g)[4]) {
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const float zz = to_f32(z[x]);
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(zz * kNegLog2e));
+    z[x] = from_f32<T>(g[x] * sg * fmaf(zz, 1.0f - sg, 1.0f));
+  }
+}
+
 }  // namespace attn
 }  // namespace hstu

@@ -569,7 +569,17 @@ __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_
     // dQ = c_b * sum dS k (the accumulators hold true dS values); then the bias-gradient bins
     if (gb.cur_bt >= 0) flush_bin(gb.ht + gb.cur_bt, gb.run_t, lane);
     flush_bin(gb.hp + (P - 1), gb.run_p, lane);
-    if (my_valid) {
+    if (my_valid && p.z_q) {
+      T *zrow = (T *)p.z_q + (int64_t)(o0 + my_row) * p.z_row_stride + h * DH;
+#pragma unroll
+      for (int db = 0; db < L::kDB; ++db)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const float g[4] = {oacc.d[db][4 * e4 + 0] * cb, oacc.d[db][4 * e4 + 1] * cb,
+                              oacc.d[db][4 * e4 + 2] * cb, oacc.d[db][4 * e4 + 3] * cb};
+          silu_grad_store4(zrow + 32 * db + 8 * e4 + 4 * half, g);
+        }
+    } else if (my_valid) {
       float *drow = (float *)p.out + (int64_t)(o0 + my_row) * p.out_row_stride + h * DH;
 #pragma unroll
       for (int db = 0; db < L::kDB; ++db)

@@ -48,6 +48,11 @@ struct AttnArgs {
   const void *d_out;               // [T][row_stride] upstream gradient of out, in_dtype
   float *d_pos_bias, *d_time_bias; // [R][P], [R][Tb]
   float *dk, *dv;                  // [T][row_stride] fp32 (dQ goes to out, fp32)
+  // Layer path: when z_q is set, the gradients instead become those of the projection's pre-activation,
+  // dz = d{q,k,v} * SiLU'(z), written in place over z (in_dtype) at z_q, z_k, z_v (head h at column
+  // h*Dh of each row, z_row_stride elements between tokens); out, dk and dv are not written.
+  void *z_q, *z_k, *z_v;
+  int64_t z_row_stride;
 };
 
 // Key splits of cached scoring for a batch: enough workgroups to fill the chip, each split a whole
@@ -189,9 +194,6 @@ struct NormGateBwdArgs {
 };
 hipError_t launch_norm_gate_bwd(const NormGateBwdArgs &a, hipStream_t stream);
 
-// z[:, N:4N] <- [dv | dq | dk] * SiLU'(z[:, N:4N]) (dv, dq, dk fp32 [M][N]; z dtype [M][4N]; N % 4 == 0).
-hipError_t launch_silu_grad_vqk(const float *dv, const float *dq, const float *dk, void *z, int M, int N, int dtype,
-                                hipStream_t stream);
 // dst [C][Rp] = src[R][C]^T with rows R..Rp-1 zero (C % 4 == 0, Rp % 4 == 0, Rp >= R).
 hipError_t launch_transpose(const void *src, int src_f32, void *dst, int dst_f32, int R, int C, int Rp,
                             hipStream_t stream);

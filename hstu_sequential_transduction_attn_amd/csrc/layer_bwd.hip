@@ -8,7 +8,8 @@
 //   dg = dr W2                         -> plain GEMM
 //   dU = dg * LN(o),  do = LN'(o)(dg * U),  g recomputed for dW2      -> norm_gate_bwd_kernel
 //   dQ, dK, dV = attention backward(do)
-//   dz = [dU | dV | dQ | dK] * SiLU'(z)                               -> norm_gate_bwd / silu_grad_vqk
+//   dz = [dU | dV | dQ | dK] * SiLU'(z)                               -> norm_gate_bwd / the attention
+//                                                                        backward's epilogues
 //   dx = dr + dz W1;  dW1 = dz^T x;  dW2 = dr^T g                      -> GEMMs (the weight gradients on
 //                                                                        token-contiguous transposes)
 //   db1 = sum_t dz,  db2 = sum_t dr                                   -> row sums of the transposes
@@ -173,28 +174,6 @@ __global__ void __launch_bounds__(256) norm_gate_bwd_kernel(const float *__restr
   }
 }
 
-// ---- dz for the V, Q, K slices, in place: z[t][N + s*N + c] <- ds_s[t][c] * SiLU'(z[t][N + s*N + c]),
-// ds_0 = dV, ds_1 = dQ, ds_2 = dK (fp32 [M][N]).  One thread per 4 consecutive columns.
-template <typename TM>
-__global__ void __launch_bounds__(256) silu_grad_vqk_kernel(const float *__restrict__ dv, const float *__restrict__ dq,
-                                                            const float *__restrict__ dk, TM *__restrict__ z, int M,
-                                                            int N) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // index of a 4-column group
-  const int64_t groups_per_row = (int64_t)3 * N / 4;
-  if (i >= (int64_t)M * groups_per_row) return;
-  const int64_t t = i / groups_per_row;
-  const int c = (int)(i % groups_per_row) * 4;                  // column inside [0, 3N)
-  const int slot = c / N, cc = c % N;
-  const float *ds = slot == 0 ? dv : slot == 1 ? dq : dk;
-  const floatx4 d = load4(ds + t * N + cc);
-  TM *zp = z + t * 4 * N + N + c;
-  const floatx4 zz = load4(zp);
-  floatx4 out;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) out[e] = d[e] * silu_grad_f32(zz[e]);
-  store4(zp, out);
-}
-
 // ---- dst[c][r] = src[r][c] for r < R, 0 for R <= r < Rp (TI -> TO, rounded when TO is bf16).
 // 64 x 64 tiles through a padded LDS tile; C % 4 == 0, Rp % 4 == 0.
 template <typename TI, typename TO>
@@ -297,18 +276,6 @@ hipError_t launch_ln_bwd_rows(const LnBwdArgs &a, hipStream_t s) {
 hipError_t launch_norm_gate_bwd(const NormGateBwdArgs &a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   return a.dtype == kF32 ? launch_norm_gate_bwd_t<float>(a, s) : launch_norm_gate_bwd_t<__bf16>(a, s);
-}
-
-hipError_t launch_silu_grad_vqk(const float *dv, const float *dq, const float *dk, void *z, int M, int N, int dtype,
-                                hipStream_t s) {
-  if (M == 0) return hipSuccess;
-  const int64_t groups = (int64_t)M * 3 * N / 4;
-  const dim3 grid((unsigned)((groups + 255) / 256));
-  if (dtype == kF32)
-    hipLaunchKernelGGL((silu_grad_vqk_kernel<float>), grid, dim3(256), 0, s, dv, dq, dk, (float *)z, M, N);
-  else
-    hipLaunchKernelGGL((silu_grad_vqk_kernel<__bf16>), grid, dim3(256), 0, s, dv, dq, dk, (__bf16 *)z, M, N);
-  return hipGetLastError();
 }
 
 hipError_t launch_transpose(const void *src, int src_f32, void *dst, int dst_f32, int R, int C, int Rp, hipStream_t s) {
