@@ -148,3 +148,17 @@ def test_mfalcon_fused_full_size_sampled_user():
     _, idx = sub_jagged(case.jagged, seqs)
     r, m = assert_close(y[idx], _oracle(case, table, ids, seqs), "bf16", "mfalcon fused sampled")
     print(f"  user={seqs} n={int(lengths[seqs[0]])} rel_l2={r:.3e} max_abs={m:.3e}")
+
+
+def test_stack_fused_partial_statistics_tile():
+    """D = 352: each row's LayerNorm statistics merge a 256-column tile and a 96-column tile (unequal
+    counts), and the gathered residual rows span both column tiles."""
+    print("\n[case] stack fused D=352", flush=True)
+    rng = np.random.default_rng(1440)
+    lengths = [int(v) for v in rng.integers(1, 900, size=22)]
+    case, table, ids = _table_case("stk_p", 1440, lengths, D=352, H=2, Dh=128, P=64, Tb=64, num_layers=3,
+                                   table_rows=5_000, bias_std=0.1)
+    print(f"  T={sum(lengths)}", flush=True)
+    assert _fused(sum(lengths), 352, 256)
+    got = _gpu(case, table, ids, act_split=True, y_dtype=torch.float32)
+    assert_close(got, _oracle(case, table, ids), "bf16", "stack fused D=352", magnitude_aware=True)
