@@ -160,6 +160,29 @@ def run(args):
         extended(args, dev)
 
 
+def steady_ms(fn, warm_ms: float = 100.0, timed_ms: float = 60.0) -> float:
+    """Milliseconds per call of fn on the current stream at the chip's steady clock: untimed calls for
+    about warm_ms of sustained load first (at least 2), then at least 5 timed calls (about timed_ms)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    est = max((time.perf_counter() - t0) * 1e3, 1e-3)
+    for _ in range(max(2, min(400, int(warm_ms / est)))):
+        fn()
+    reps = max(5, min(200, int(timed_ms / est)))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def extended(args, dev, layers_only=False):
     """Layer workloads (stderr, informational): layer_bf16, stack8_bf16 and mfalcon_bf16 with every input
     and weight resident on the device; one forward = gather (when the workload stages its input from an
@@ -208,18 +231,7 @@ def extended(args, dev, layers_only=False):
                                   max_seq_len=j.max_seq_len, ln_eps=L["eps"], ln_output=li < len(layers) - 1,
                                   mask=j.mask, num_candidates=ncand, y_dtype=ydt, act_split=act_split, workspace=ws)
             return x
-        stream = torch.cuda.current_stream()
-        for _ in range(2):
-            forward()
-        torch.cuda.synchronize()
-        reps = 5
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            forward()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+        ms = steady_ms(forward)
         T, D, HD = j.total_tokens, case.d_model, H * Dh
         pairs = I.allowed_pairs(j)
         flop = len(layers) * (2 * T * D * 4 * HD + pairs * H * 4 * Dh + 2 * T * HD * D)
@@ -237,15 +249,7 @@ def extended(args, dev, layers_only=False):
             def stacked():
                 return ops.stack_fwd(table, ids, offs, tau, sl, H, Dh, max_seq_len=j.max_seq_len, mask=j.mask,
                                      num_candidates=ncand, act_split=act_split, y=y32, workspace=sws)
-            for _ in range(2):
-                stacked()
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(reps):
-                stacked()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ms2 = e0.elapsed_time(e1) / reps
+            ms2 = steady_ms(stacked)
             print(f"[extended] {name} (hstu_stack_fwd, gather and LayerNorms fused): {ms2:.3f} ms per forward; "
                   f"{flop / ms2 / 1e9:.1f} TFLOP/s", file=sys.stderr, flush=True)
             del sws, y32
@@ -301,17 +305,7 @@ def layer_backward(dev):
             ops.layer_bwd(x, dy, offs, tau, w1, w2, wp, wt, H, Dh, max_seq_len=j.max_seq_len, ln_eps=L.ln_eps,
                           ln_output=ln_output, mask=j.mask, act_split=stream32, workspace=ws, dx=dx, grads=grads)
 
-        stream = torch.cuda.current_stream()
-        for _ in range(2):
-            run()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(5):
-            run()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / 5
+        ms = steady_ms(run)
         HD = H * Dh
         pairs = I.allowed_pairs(j)
         attn = pairs * H * 4 * Dh
@@ -344,15 +338,7 @@ def layer_backward(dev):
 
         res = {}
         for label, fn in (("recompute", step_recompute), ("saved", step_saved)):
-            for _ in range(2):
-                fn()
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(5):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            res[label] = e0.elapsed_time(e1) / 5
+            res[label] = steady_ms(fn)
         print(f"[extended] layer_train_step {name}: forward + backward {res['recompute']:.3f} ms recomputing the "
               f"forward, {res['saved']:.3f} ms from saved activations ({nsv / 1e9:.2f} GB kept)",
               file=sys.stderr, flush=True)
@@ -385,17 +371,7 @@ def attn_backward(dev):
     def run():
         ops.attn_bwd(offs, tau, q, k, v, g, wp, wt, max_seq_len=j.max_seq_len, workspace=ws)
 
-    stream = torch.cuda.current_stream()
-    for _ in range(2):
-        run()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(5):
-        run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 5
+    ms = steady_ms(run)
     flop = 2.5 * case.flops()
     print(f"[extended] attn_bwd_L8192: {ms:.3f} ms per backward (dq, dk, dv, bias tables); {flop:.3e} algorithmic "
           f"FLOP -> {flop / ms / 1e9:.1f} TFLOP/s ({flop / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS * 100:.1f}% of dense bf16 peak)",
@@ -454,19 +430,7 @@ def cached_scoring(dev):
                                     max_candidates=mb, max_history=max(hist), attn_scale=scale, workspace=ws)
         return run
 
-    stream = torch.cuda.current_stream()
-
-    def timed(fn):
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(5):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / 5
+    timed = steady_ms
 
     per_pair = 4 * 4 * 128
     pairs_cached = sum(m * (h + 1) for h in hist)
