@@ -98,13 +98,19 @@ __device__ __forceinline__ void tile_body(OAcc<Layout<T, DH>::kDB> &oacc,
 // dP^T like K's feed S^T, and K is read transposed for dQ^T.
 
 // Bias-table gradient bins of one wave: all uniform and two-bucket tiles have position bucket P-1
-// (run_p); consecutive uniform tiles with the same time bucket share run_t; every other score goes
-// straight into the wave's own LDS bins.  Per-wave bins and single-lane flushes keep the sums in a
-// fixed order.
+// (run_p); consecutive uniform tiles with the same time bucket share run_t.  In the other tiles a
+// score of position bucket P-1 also goes to run_p, any other position bucket straight into the wave's
+// LDS bin (the lanes of one instruction hold distinct queries, so they rarely share a bin), and the
+// time buckets are run-length summed per lane (lane_t, lane_bt): along a query's keys the bucket
+// changes rarely, and a lane adds its run to the LDS bin only when it does.  Adding every score to its
+// time bin directly made most lanes of each instruction hit the same LDS address.  Per-wave bins,
+// program order and single-lane flushes keep the sums in a fixed order.
 struct GradBins {
   HSTU_LDS float *hp, *ht;   // this wave's position bins [P] and time bins [kTimeTab]
   float run_p, run_t;        // per-lane running sums
   int cur_bt;                // wave-uniform time bucket of run_t; -1 before the first uniform tile
+  float lane_t;              // per-lane run of time bucket lane_bt (general tiles)
+  int lane_bt;
 };
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -168,8 +174,15 @@ __device__ __forceinline__ void bwd_tile_body(OAcc<Layout<T, DH>::kDB> &dq,
     } else {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        __builtin_amdgcn_ds_faddf(gb.hp + (bins[e] & 0xffff), ds[e], 0, 0, false);
-        __builtin_amdgcn_ds_faddf(gb.ht + (bins[e] >> 16), ds[e], 0, 0, false);
+        const int bp = bins[e] & 0xffff, bt = bins[e] >> 16;
+        if (bp == c.P - 1) gb.run_p += ds[e];
+        else __builtin_amdgcn_ds_faddf(gb.hp + bp, ds[e], 0, 0, false);
+        if (bt != gb.lane_bt) {
+          __builtin_amdgcn_ds_faddf(gb.ht + gb.lane_bt, gb.lane_t, 0, 0, false);
+          gb.lane_bt = bt;
+          gb.lane_t = 0.0f;
+        }
+        gb.lane_t += ds[e];
       }
     }
     av_block_in<T, DH, true>(dq, ds, lK, kb, lane);
@@ -497,6 +510,7 @@ __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_
     gb.hp = wt_lds + kTimeTab + wave * nbins;
     gb.ht = gb.hp + P;
     gb.cur_bt = -1;
+    gb.lane_bt = 0;   // an empty run (lane_t = 0) of bucket 0
     for (int i = lane; i < nbins; i += kWave) gb.hp[i] = 0.0f;
   }
 
@@ -569,6 +583,7 @@ __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_
     // dQ = c_b * sum dS k (the accumulators hold true dS values); then the bias-gradient bins
     if (gb.cur_bt >= 0) flush_bin(gb.ht + gb.cur_bt, gb.run_t, lane);
     flush_bin(gb.hp + (P - 1), gb.run_p, lane);
+    __builtin_amdgcn_ds_faddf(gb.ht + gb.lane_bt, gb.lane_t, 0, 0, false);
     if (my_valid && p.z_q) {
       T *zrow = (T *)p.z_q + (int64_t)(o0 + my_row) * p.z_row_stride + h * DH;
 #pragma unroll
