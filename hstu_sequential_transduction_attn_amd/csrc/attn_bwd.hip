@@ -26,14 +26,17 @@ namespace {
 using namespace attn;
 
 // Per-wave constants of the per-score bias and mask of a general tile (roles of the forward's
-// TileCtx with queries and keys exchanged: the lane's key is fixed, the tile's queries vary).
+// TileCtx with queries and keys exchanged: the lane's key is fixed, the tile's queries vary).  The
+// lane's own key values (position, allowed queries, timestamp) are rebuilt from the lane index and
+// the wave's key timestamps in LDS where a general tile needs them: held in registers for the whole
+// loop, they pushed the two-waves-per-SIMD register budget into spills.
 struct KeyCtx {
   int q0;              // first query of the tile (sequence-local)
-  int my_pos;          // this lane's key position
+  int ka;              // first key of the wave
+  int n, nh;           // sequence length; history length (n without candidates)
   int pos_lim;         // position of query i is min(i, pos_lim)
-  int q_lo, q_hi;      // allowed queries of this lane's key: q_lo <= i <= q_hi
   int P, Tb;
-  int64_t my_tau;
+  const HSTU_LDS int64_t *ktau;    // the wave's 32 key timestamps
   const HSTU_LDS float *wp, *wt;
   const HSTU_LDS char *stage;
 };
@@ -41,8 +44,13 @@ struct KeyCtx {
 // Bias (and mask) of the 16 scores of 32-query block qb in place; element e holds query
 // q0 + 32*qb + 16*(e/8) + 8*half + e%8.
 template <typename T, int DH, bool MASKED>
-__device__ __forceinline__ void adjust_block_keys(floatx16 &s, const KeyCtx &c, int qb, int half) {
+__device__ __forceinline__ void adjust_block_keys(floatx16 &s, const KeyCtx &c, int qb, int lane) {
   using L = Layout<T, DH>;
+  const int half = lane >> 5;
+  const int my_k = c.ka + (lane & 31);
+  const int my_pos = imin(my_k, c.pos_lim);      // a candidate key sits at position nh
+  const int q_hi = my_k < c.nh ? c.n - 1 : my_k;  // allowed queries: my_k <= i <= q_hi
+  const int64_t my_tau = c.ktau[lane & 31];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const int il0 = 32 * qb + 16 * g + 8 * half;
@@ -58,12 +66,12 @@ __device__ __forceinline__ void adjust_block_keys(floatx16 &s, const KeyCtx &c, 
       const int e = 8 * g + e8;
       const int i = c.q0 + il0 + e8;
       const int pi = imin(i, c.pos_lim);
-      const uint32_t dp = __usad((uint32_t)pi, (uint32_t)c.my_pos, 0u);
+      const uint32_t dp = __usad((uint32_t)pi, (uint32_t)my_pos, 0u);
       const int bp = (int)(dp < (uint32_t)(c.P - 1) ? dp : (uint32_t)(c.P - 1));
-      const int bt = imin(bitlen_absdiff(ti[e8], c.my_tau), c.Tb - 1);
+      const int bt = imin(bitlen_absdiff(ti[e8], my_tau), c.Tb - 1);
       const float bias = c.wp[bp] + c.wt[bt];
       if constexpr (MASKED) {
-        const bool ok = (i >= c.q_lo) & (i <= c.q_hi);
+        const bool ok = (i >= my_k) & (i <= q_hi);
         s[e] = ok ? s[e] + bias : kMaskedScore;
       } else {
         s[e] = s[e] + bias;
@@ -84,22 +92,42 @@ __device__ __forceinline__ void dkdv_block(OAcc<Layout<T, DH>::kDB> &dk, OAcc<La
   const int l32 = lane & 31, half = lane >> 5;
   const HSTU_LDS char *lQ = c.stage + L::kOffK;
   const HSTU_LDS char *lG = c.stage + L::kOffV;
-  floatx16 s, dp;
+  floatx16 s;
   score_block<T, DH>(s, lQ, qb, l32, half, kf);
-  score_block<T, DH>(dp, lG, qb, l32, half, vf);
-  if (body == kGen64) adjust_block_keys<T, DH, false>(s, c, qb, half);
-  else if (body == kGen64M) adjust_block_keys<T, DH, true>(s, c, qb, half);
-  float a[16], ds[16];
+  if (body == kGen64) adjust_block_keys<T, DH, false>(s, c, qb, lane);
+  else if (body == kGen64M) adjust_block_keys<T, DH, true>(s, c, qb, lane);
+  // A = SiLU(x) and SiLU'(x) from S, then dV; dP only after that, so that S, A and dP are never all
+  // live at once (at two waves per SIMD the registers are the limit)
+  float a[16], gd[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const float u = fmaf(s[e], kNegLog2e, c1);             // -log2(e) x, x = s + bias
     const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u));
     const float x = u * kNegLn2;
     a[e] = x * sig;                                         // SiLU(x); 0 for a masked score
-    ds[e] = dp[e] * (sig * fmaf(x, 1.0f - sig, 1.0f));      // dP SiLU'(x)
+    gd[e] = sig * fmaf(x, 1.0f - sig, 1.0f);                // SiLU'(x)
   }
-  av_block_in<T, DH, true>(dv, a, lG, qb, lane);
-  av_block_in<T, DH, true>(dk, ds, lQ, qb, lane);
+  if constexpr (L::kBf16) {
+    bf16x8 pa[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pa[e / 8][e % 8] = f32_to_bf16(a[e]);
+    av_block_packed<DH, true>(dv, pa, lG, qb, lane);
+  } else {
+    av_block_in<T, DH, true>(dv, a, lG, qb, lane);
+  }
+  floatx16 dp;
+  score_block<T, DH>(dp, lG, qb, l32, half, vf);
+  float ds[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) ds[e] = dp[e] * gd[e];      // dP SiLU'(x)
+  if constexpr (L::kBf16) {
+    bf16x8 pd[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pd[e / 8][e % 8] = f32_to_bf16(ds[e]);
+    av_block_packed<DH, true>(dk, pd, lQ, qb, lane);
+  } else {
+    av_block_in<T, DH, true>(dk, ds, lQ, qb, lane);
+  }
 }
 
 template <typename T, int DH>
@@ -148,7 +176,8 @@ attn_bwd_dkdv_kernel(const AttnArgs p, const int n_kblocks) {
   const int lane = tid % kWave;
   const int l32 = lane & 31, half = lane >> 5;
 
-  HSTU_LDS float *wp_lds = (HSTU_LDS float *)(smem + L::kStages * L::kStageBytes);
+  HSTU_LDS int64_t *ktau_lds = (HSTU_LDS int64_t *)(smem + L::kStages * L::kStageBytes);
+  HSTU_LDS float *wp_lds = (HSTU_LDS float *)(ktau_lds + kBM);
   HSTU_LDS float *wt_lds = wp_lds + P;
   for (int i = tid; i < P; i += kThreads) wp_lds[i] = p.pos_bias[(int64_t)rr * P + i];
   const int nt_tab = imin(Tb, kTimeTab);
@@ -160,7 +189,7 @@ attn_bwd_dkdv_kernel(const AttnArgs p, const int n_kblocks) {
   const bool wave_active = ka < n;
   const int my_k = ka + l32;
   const bool my_valid = my_k < n;
-  const int64_t my_tau = my_valid ? p.timestamps[o0 + my_k] : 0;
+  ktau_lds[wave * kQW + l32] = my_valid ? p.timestamps[o0 + my_k] : 0;
   const int64_t kmin = wave_active ? stats[2 * (ka >> 5)] : 0;
   const int64_t kmax = wave_active ? stats[2 * (ka >> 5) + 1] : 0;
 
@@ -190,12 +219,12 @@ attn_bwd_dkdv_kernel(const AttnArgs p, const int n_kblocks) {
 
   // direct-to-LDS staging of Q and dO rows (both in the K layout) and the queries' timestamps
   const uint32_t rsb = (uint32_t)(p.row_stride * L::kES);
-  const int lr16 = 16 * wave + (lane >> 2);
-  const uint32_t x_add = (uint32_t)(h * L::kRB) + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-  const int tr16 = 16 * wave + ((lane & 31) >> 1);
-  const uint32_t t_add = 4u * (uint32_t)(lane & 1);
   const char *qbase = (const char *)p.q, *gbase = (const char *)p.d_out;
-  auto issue_tile = [&](int i, int stage) {
+  auto issue_tile = [&](int i, int stage, int ln) {
+    const int lr16 = 16 * wave + (ln >> 2);
+    const uint32_t x_add = (uint32_t)(h * L::kRB) + 16u * (uint32_t)((ln & 3) ^ ((ln >> 4) & 3));
+    const int tr16 = 16 * wave + ((ln & 31) >> 1);
+    const uint32_t t_add = 4u * (uint32_t)(ln & 1);
     const int q0 = (t0 + i) * kBN;
     const int lim = n - 1 - q0;
     const uint32_t r = (uint32_t)imin(lr16, lim);
@@ -216,13 +245,13 @@ attn_bwd_dkdv_kernel(const AttnArgs p, const int n_kblocks) {
   }
 
   KeyCtx c;
-  c.my_pos = cand ? imin(my_k, nh) : my_k;
+  c.ka = ka;
+  c.n = n;
+  c.nh = nh;
   c.pos_lim = cand ? nh : n;
-  c.q_lo = my_k;
-  c.q_hi = my_k < nh ? n - 1 : my_k;
   c.P = P;
   c.Tb = Tb;
-  c.my_tau = my_tau;
+  c.ktau = ktau_lds + wave * kQW;
   c.wp = wp_lds;
   c.wt = wt_lds;
   const int kpl = imin(kl, nh);                    // position of the wave's last key
@@ -230,7 +259,7 @@ attn_bwd_dkdv_kernel(const AttnArgs p, const int n_kblocks) {
   constexpr int kAhead = L::kStages - 1;
 #pragma unroll
   for (int i = 0; i < kAhead; ++i)
-    if (i < ntiles) issue_tile(i, i);
+    if (i < ntiles) issue_tile(i, i, lane);
   __syncthreads();
 
   for (int i = 0; i < ntiles; ++i) {
@@ -239,7 +268,8 @@ attn_bwd_dkdv_kernel(const AttnArgs p, const int n_kblocks) {
     else if (after == 1) wait_vmcnt<L::kLoadsPerTile>();
     else wait_vmcnt<0>();
     __syncthreads();
-    if (i + kAhead < ntiles) issue_tile(i + kAhead, (i + kAhead) % L::kStages);
+    const int ln = lane_now();
+    if (i + kAhead < ntiles) issue_tile(i + kAhead, (i + kAhead) % L::kStages, ln);
 
     // class of (this wave's keys, tile i), in scalar code
     const int q0 = (t0 + i) * kBN;
@@ -281,11 +311,15 @@ attn_bwd_dkdv_kernel(const AttnArgs p, const int n_kblocks) {
     if (body != kNone) {
       c.q0 = q0;
       c.stage = smem + (i % L::kStages) * L::kStageBytes;
-      dkdv_tile<T, DH>(dk, dv, kf, vf, c, body, c1, lane);
+      dkdv_tile<T, DH>(dk, dv, kf, vf, c, body, c1, ln);
     }
   }
 
   // ---- epilogue: dK^T / dV^T element e of dh block db is dh = 32*db + 8*(e/4) + 4*half + e%4
+  {
+  const int le = lane_now();
+  const int my_k = ka + (le & 31), half = le >> 5;
+  const bool my_valid = my_k < n;
   if (my_valid && p.z_q) {
     T *kz = (T *)p.z_k + (int64_t)(o0 + my_k) * p.z_row_stride + h * DH;
     T *vz = (T *)p.z_v + (int64_t)(o0 + my_k) * p.z_row_stride + h * DH;
@@ -317,12 +351,14 @@ attn_bwd_dkdv_kernel(const AttnArgs p, const int n_kblocks) {
         *(floatx4 *)(vrow + 32 * db + 8 * e4 + 4 * half) = wv;
       }
   }
+  }
 }
 
 template <typename T, int DH>
 size_t dkdv_lds_bytes(int num_pos_buckets) {
   using L = Layout<T, DH>;
-  return (size_t)L::kStages * L::kStageBytes + (size_t)(num_pos_buckets + kTimeTab) * sizeof(float);
+  return (size_t)L::kStages * L::kStageBytes + (size_t)kBM * sizeof(int64_t) +
+         (size_t)(num_pos_buckets + kTimeTab) * sizeof(float);
 }
 
 template <typename T, int DH>

@@ -59,6 +59,17 @@ struct Layout {
   __device__ static int tau_at(int j) { return kOffTau + 256 * (j >> 4) + 8 * (j & 15); }
 };
 
+// The lane's index in its wave, recomputed at each use.  The volatile read is never hoisted or
+// merged, so addresses derived from it are rebuilt in the loop body (a few VALU instructions) rather
+// than held across the loop; near the register limit the compiler would spill them, and a reload from
+// scratch waits on the vector-memory counter that also tracks the direct-to-LDS prefetch of the next
+// tile, so every reload would wait for that prefetch.
+__device__ __forceinline__ int lane_now() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // The O^T accumulators of one wave: N blocks of 32 dh rows x 32 queries.
 template <int N>
 struct OAcc {
@@ -174,6 +185,19 @@ __device__ __forceinline__ void silu_block(const floatx16 &s, float (&a)[16], fl
   }
 }
 
+// LDS offsets of the A operand of k step st of score_block in a K-layout tile (bf16): row
+// r = 32*kb + kperm(l32), byte 32*st + 16*half.  The XOR of the layout sees bits 2-3 of the row (kb
+// never changes them) and the piece index 2*(st&1) + half, so every step is one of two lane parts
+// plus 2048*kb + 4096*(st/2).
+struct ScoreAddr {
+  int even, odd;
+};
+template <int DH>
+__device__ __forceinline__ ScoreAddr score_addr(int l32, int half) {
+  using L = Layout<__bf16, DH>;
+  return {L::k_at(kperm(l32), 16 * half), L::k_at(kperm(l32), 32 + 16 * half)};
+}
+
 template <typename T, int DH>
 __device__ __forceinline__ void score_block(floatx16 &s, const HSTU_LDS char *lK, int kb, int l32, int half,
                                             const typename QFrag<T>::type (&qf)[Layout<T, DH>::kQSteps]) {
@@ -183,7 +207,9 @@ __device__ __forceinline__ void score_block(floatx16 &s, const HSTU_LDS char *lK
 #pragma unroll
   for (int st = 0; st < L::kQSteps; ++st) {
     if constexpr (L::kBf16) {
-      const bf16x8 kf = *(const HSTU_LDS bf16x8 *)(lK + L::k_at(r, (16 * st + 8 * half) * 2));
+      const ScoreAddr sa = score_addr<DH>(l32, half);
+      const int off = ((st & 1) ? sa.odd : sa.even) + 2048 * kb + 4096 * (st >> 1);
+      const bf16x8 kf = *(const HSTU_LDS bf16x8 *)(lK + off);
       s = mfma32(kf, qf[st], s);
     } else {
       const float kf = *(const HSTU_LDS float *)(lK + L::k_at(r, (2 * st + half) * 4));
@@ -194,13 +220,22 @@ __device__ __forceinline__ void score_block(floatx16 &s, const HSTU_LDS char *lK
 
 // O^T += X^T a^T for one 32-key block: X^T read transposed from a tile in the V layout, or (XL) in the
 // K layout (the backward's dQ^T += K^T dS^T reads the K tile this way).
+template <int DH, bool XL>
+__device__ __forceinline__ void av_block_packed(OAcc<Layout<__bf16, DH>::kDB> &oacc, const bf16x8 (&pf)[2],
+                                                const HSTU_LDS char *lV, int kb, int lane);
+
 template <typename T, int DH, bool XL>
 __device__ __forceinline__ void av_block_in(OAcc<Layout<T, DH>::kDB> &oacc, const float (&a)[16],
                                             const HSTU_LDS char *lV, int kb, int lane) {
   using L = Layout<T, DH>;
   const auto at = [](int r, int b) { return XL ? L::k_at(r, b) : L::v_at(r, b); };
   const int l32 = lane & 31, half = lane >> 5;
-  if constexpr (L::kBf16) {
+  if constexpr (L::kBf16 && XL) {
+    bf16x8 pf[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pf[e / 8][e % 8] = f32_to_bf16(a[e]);
+    av_block_packed<DH, XL>(oacc, pf, lV, kb, lane);
+  } else if constexpr (L::kBf16) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       bf16x8 pf;
@@ -229,6 +264,35 @@ __device__ __forceinline__ void av_block_in(OAcc<Layout<T, DH>::kDB> &oacc, cons
         const float vf = *(const HSTU_LDS float *)(lV + at(r, (32 * db + l32) * 4));
         oacc.d[db] = mfma32(vf, a[e], oacc.d[db]);
       }
+    }
+  }
+}
+
+// av_block_in with the bf16 operand already packed (pf[s2] holds a[8*s2 .. 8*s2+7], rounded).
+template <int DH, bool XL>
+__device__ __forceinline__ void av_block_packed(OAcc<Layout<__bf16, DH>::kDB> &oacc, const bf16x8 (&pf)[2],
+                                                const HSTU_LDS char *lV, int kb, int lane) {
+  using L = Layout<__bf16, DH>;
+  const auto at = [](int r, int b) { return XL ? L::k_at(r, b) : L::v_at(r, b); };
+  // Row r0 + 16*s2 + 32*kb and byte b0 + 64*db of either layout lie at a lane part plus
+  // 64*(16*s2 + 32*kb) + 4096*db: the XOR of the K layout reads only bits 2-3 of the row and bits 4-5
+  // of the byte, which those steps never change.  Two lane parts serve every read of the block.
+  const int half = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
+  const int r0 = 8 * half + (i16 >> 2), b0 = (16 * (g16 & 1) + 4 * (i16 & 3)) * 2;
+  const HSTU_LDS char *p0 = lV + at(r0, b0) + 2048 * kb;
+  const HSTU_LDS char *p1 = lV + at(r0 + 4, b0) + 2048 * kb;
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+    for (int db = 0; db < L::kDB; ++db) {
+      const int step = 1024 * s2 + 4096 * db;
+      const shortx4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HSTU_LDS shortx4 *)(p0 + step));
+      const shortx4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HSTU_LDS shortx4 *)(p1 + step));
+      const bf16x4 w0 = __builtin_bit_cast(bf16x4, v0), w1 = __builtin_bit_cast(bf16x4, v1);
+      bf16x8 vf;
+      vf[0] = w0[0]; vf[1] = w0[1]; vf[2] = w0[2]; vf[3] = w0[3];
+      vf[4] = w1[0]; vf[5] = w1[1]; vf[6] = w1[2]; vf[7] = w1[3];
+      oacc.d[db] = mfma32(vf, pf[s2], oacc.d[db]);
     }
   }
 }

@@ -409,13 +409,14 @@ __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_
   // lanes 0..31 into an unused half of the wave's 256-byte slot).  Rows past the end of the sequence
   // load its last row instead (finite data that the mask discards).
   const uint32_t rsb = (uint32_t)(p.row_stride * L::kES);        // bytes between tokens (<= 16 KB)
-  const int lr16 = 16 * wave + (lane >> 2);                      // tile-local row this lane loads
-  const uint32_t k_add = (uint32_t)(h * L::kRB) + 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-  const uint32_t v_add = BWD ? k_add : (uint32_t)(h * L::kRB) + 16u * (uint32_t)(lane & 3);
-  const int tr16 = 16 * wave + ((lane & 31) >> 1);               // tile-local key of this lane's tau word
-  const uint32_t t_add = 4u * (uint32_t)(lane & 1);
+  // (the backward, near the register limit, rebuilds the lane's offsets at each tile from lane_now())
   const char *kbase = (const char *)(CACHED ? p.k_hist : p.k), *vbase = (const char *)(CACHED ? p.v_hist : p.v);
-  auto issue_tile = [&](int i, int stage) {
+  auto issue_tile = [&](int i, int stage, int ln) {
+    const int lr16 = 16 * wave + (ln >> 2);                      // tile-local row this lane loads
+    const uint32_t k_add = (uint32_t)(h * L::kRB) + 16u * (uint32_t)((ln & 3) ^ ((ln >> 4) & 3));
+    const uint32_t v_add = BWD ? k_add : (uint32_t)(h * L::kRB) + 16u * (uint32_t)(ln & 3);
+    const int tr16 = 16 * wave + ((ln & 31) >> 1);               // tile-local key of this lane's tau word
+    const uint32_t t_add = 4u * (uint32_t)(ln & 1);
     const int k0 = tile_of(i) * kBN;
     const int lim = nkeys - 1 - k0;                              // >= 0: every tile starts inside the keys
     const uint32_t r = (uint32_t)imin(lr16, lim);
@@ -517,7 +518,7 @@ __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_
   constexpr int kAhead = L::kStages - 1;      // tiles in flight beyond the one being computed
 #pragma unroll
   for (int i = 0; i < kAhead; ++i)
-    if (i < ntiles) issue_tile(i, i);
+    if (i < ntiles) issue_tile(i, i, lane);
   __syncthreads();                            // bias tables visible to the classification
 
   for (int i = 0; i < ntiles; ++i) {
@@ -528,7 +529,8 @@ __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_
     else if (after == 1) wait_vmcnt<L::kLoadsPerTile>();
     else wait_vmcnt<0>();
     __syncthreads();  // tile i visible to all waves; every wave is done with tile i - 1
-    if (i + kAhead < ntiles) issue_tile(i + kAhead, (i + kAhead) % L::kStages);
+    const int ln = BWD ? lane_now() : lane;
+    if (i + kAhead < ntiles) issue_tile(i + kAhead, (i + kAhead) % L::kStages, ln);
 
     const int li = i & 63;
     const int code = readlane_i(cls_code, li);
@@ -544,7 +546,7 @@ __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_
       c.blo = (code >> 8) & 255;
       c.base_lo = (uint32_t)readlane_i((int)cls_base, li);
       c.qoff = (uint32_t)(uint64_t)my_tau - c.base_lo;
-      if constexpr (BWD) bwd_tile_body<T, DH>(oacc, qf, gf, c, body, code, lane, gb);
+      if constexpr (BWD) bwd_tile_body<T, DH>(oacc, qf, gf, c, body, code, ln, gb);
       else tile_body<T, DH>(oacc, qf, c, body, lane);
     }
   }
