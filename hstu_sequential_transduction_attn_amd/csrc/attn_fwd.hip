@@ -111,7 +111,41 @@ struct GradBins {
   int cur_bt;                // wave-uniform time bucket of run_t; -1 before the first uniform tile
   float lane_t;              // per-lane run of time bucket lane_bt (general tiles)
   int lane_bt;
+  bool diag;                 // wave-uniform: every query of the wave is a history query
 };
+
+// Lane i takes lane i + 1 (lane 63 takes 0), and lane i takes lane (i + 1) mod 64.
+__device__ __forceinline__ float wave_shl1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x130, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float wave_rol1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x134, 0xf, 0xf, true));
+}
+
+// Position bins of one 32-key block when every unclamped pair's bucket is i - j (history queries).
+// w holds the block's dS with clamped pairs already zeroed.  For element e = 8g + m of lane L (query
+// i = qa + L%32, key j = kb0 + 16g + 8(L/32) + m), i - j = qk - 16g - 8(L/32) + L%32 - m: along each
+// anti-diagonal (lane + 1, element + 1) the bucket is the same.  Chain A shifts by one lane per element
+// and sums the anti-diagonals that stay inside their lane half (L%32 >= m) into the lane where they
+// start; chain B rotates the others (L%32 < m, whose bucket belongs to the other half's numbering) into
+// lanes 25..31 and 57..63.  Two LDS adds per 8 elements replace eight; the order of the sums is fixed.
+__device__ __forceinline__ void diag_pos_bins(GradBins &gb, const float (&w)[16], int qk, int lane, int P) {
+  const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    float a = l32 >= 7 ? w[8 * g + 7] : 0.0f;
+    float b = l32 < 7 ? w[8 * g + 7] : 0.0f;
+#pragma unroll
+    for (int m = 6; m >= 0; --m) {
+      a = wave_shl1(a) + (l32 >= m ? w[8 * g + m] : 0.0f);
+      b = wave_rol1(b) + (l32 < m ? w[8 * g + m] : 0.0f);
+    }
+    const int bin_a = qk + l32 - 16 * g - 8 * h;   // bucket of lane L's chain-A sum
+    const int bin_b = bin_a + 16 * h - 40;          // bucket of its chain-B sum (lanes 25..31, 57..63)
+    if (bin_a >= 0 && bin_a < P - 1) __builtin_amdgcn_ds_faddf(gb.hp + bin_a, a, 0, 0, false);
+    if (l32 >= 25 && bin_b >= 0 && bin_b < P - 1) __builtin_amdgcn_ds_faddf(gb.hp + bin_b, b, 0, 0, false);
+  }
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -172,11 +206,26 @@ __device__ __forceinline__ void bwd_tile_body(OAcc<Layout<T, DH>::kDB> &dq,
         else sb += ds[e];
       }
     } else {
+      if (gb.diag) {
+        float w[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const bool clamp = (bins[e] & 0xffff) == c.P - 1;
+          gb.run_p += clamp ? ds[e] : 0.0f;
+          w[e] = clamp ? 0.0f : ds[e];
+        }
+        diag_pos_bins(gb, w, c.my_q - l32 - c.k0 - 32 * kb, lane, c.P);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int bp = bins[e] & 0xffff;
+          if (bp == c.P - 1) gb.run_p += ds[e];
+          else __builtin_amdgcn_ds_faddf(gb.hp + bp, ds[e], 0, 0, false);
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int bp = bins[e] & 0xffff, bt = bins[e] >> 16;
-        if (bp == c.P - 1) gb.run_p += ds[e];
-        else __builtin_amdgcn_ds_faddf(gb.hp + bp, ds[e], 0, 0, false);
+        const int bt = bins[e] >> 16;
         if (bt != gb.lane_bt) {
           __builtin_amdgcn_ds_faddf(gb.ht + gb.lane_bt, gb.lane_t, 0, 0, false);
           gb.lane_bt = bt;
@@ -512,6 +561,7 @@ __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_
     gb.ht = gb.hp + P;
     gb.cur_bt = -1;
     gb.lane_bt = 0;   // an empty run (lane_t = 0) of bucket 0
+    gb.diag = !cand || qa + kQW - 1 < nh;
     for (int i = lane; i < nbins; i += kWave) gb.hp[i] = 0.0f;
   }
 
