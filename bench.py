@@ -1,7 +1,7 @@
 """Benchmark of the HSTU attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--extended]
-    python bench.py --only {layers,cached,attn_bwd,layer_bwd}
+    python bench.py --only {layers,cached,attn_bwd,layer_bwd,layer_bwd_call}
 
 A step is one hstu_attn_fwd call (QK^T, bias, SiLU, mask and AV of every allowed pair) over the
 L = 8192 workload: 8 sequences of 8192 events, 4 heads x 128, P = Tb = 256 bias buckets, causal,
@@ -261,13 +261,14 @@ def extended(args, dev, layers_only=False):
     layer_backward(dev)
 
 
-def layer_backward(dev):
+def layer_backward(dev, train_step: bool = True):
     """Layer backward (stderr, informational): hstu_layer_bwd on one layer of layer_bf16 (bf16 stream,
     no output LayerNorm) and of stack8_bf16 (its first layer: fp32 activations and gradients, output
     LayerNorm, split activations), for a random upstream gradient.  One call recomputes the forward
     (nothing is saved) and forms dx and every parameter gradient.  Algorithmic FLOP: the forward's
     GEMMs and attention, plus dg, dW2, dx, dW1 (2 T D HD each for the H*Dh-wide ones, 2 T D 4HD for the
-    projection's) and 2.5x the attention's pair products."""
+    projection's) and 2.5x the attention's pair products.  With train_step, also one layer's forward +
+    backward, recomputing the forward and from saved activations."""
     import torch
     from hstu_sequential_transduction_attn_amd import configs as C
     from hstu_sequential_transduction_attn_amd import inputs as I
@@ -316,6 +317,9 @@ def layer_backward(dev):
               f"recomputed); {flop:.3e} algorithmic FLOP ({bwd:.3e} backward + {fwd:.3e} recompute) -> "
               f"{flop / ms / 1e9:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
+        if not train_step:
+            del ws, x, dy, dx, grads
+            continue
         # one layer's training step both ways: forward + backward that recomputes the forward, and
         # forward that keeps its activations + backward that reads them
         fkw = dict(max_seq_len=j.max_seq_len, ln_eps=L.ln_eps, ln_output=ln_output, mask=j.mask, act_split=stream32)
@@ -453,7 +457,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extended", action="store_true")
-    ap.add_argument("--only", choices=["layers", "cached", "attn_bwd", "layer_bwd"],
+    ap.add_argument("--only", choices=["layers", "cached", "attn_bwd", "layer_bwd", "layer_bwd_call"],
                     help="run only this informational leg of --extended (stderr), without the metric line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (torch copy_) five times, to scale "
@@ -472,7 +476,8 @@ def main():
         ops.load_library()
         dev = torch.device("cuda:0")
         {"layers": lambda: extended(args, dev, layers_only=True), "cached": lambda: cached_scoring(dev),
-         "attn_bwd": lambda: attn_backward(dev), "layer_bwd": lambda: layer_backward(dev)}[args.only]()
+         "attn_bwd": lambda: attn_backward(dev), "layer_bwd": lambda: layer_backward(dev),
+         "layer_bwd_call": lambda: layer_backward(dev, train_step=False)}[args.only]()
         return
     run(args)
 
