@@ -166,3 +166,15 @@ def test_empty_batch_and_empty_sequences():
     assert_close(host(gpu_attn(case)), _oracle(case), "bf16", "empty seqs", magnitude_aware=True)
     case0 = I.attn_case("empty0", 951, [0, 0], H=1, Dh=32, P=8, Tb=8, dtype="bf16")
     assert host(gpu_attn(case0)).size == 0
+
+
+@pytest.mark.parametrize("P,Tb", [(1, 1), (2, 3), (33, 1)])
+def test_tiny_bias_tables(P, Tb):
+    """Degenerate tables (P = 1: every position bucket is the clamped one; Tb = 1: one time bucket), with
+    and without the candidate mask."""
+    print(f"\n[case] tiny tables P={P} Tb={Tb}", flush=True)
+    case = I.attn_case("tiny", 1500 + P + Tb, [700, 1, 130, 64], H=2, Dh=64, P=P, Tb=Tb, dtype="bf16")
+    assert_close(host(gpu_attn(case)), _oracle(case), "bf16", f"P={P} Tb={Tb}", magnitude_aware=True)
+    cc = I.attn_case("tinyc", 1510 + P + Tb, [400, 90], H=2, Dh=64, P=P, Tb=Tb, dtype="bf16",
+                     num_candidates=[70, 30])
+    assert_close(host(gpu_attn(cc)), _oracle(cc), "bf16", f"candidates P={P} Tb={Tb}", magnitude_aware=True)

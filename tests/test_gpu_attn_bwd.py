@@ -91,6 +91,23 @@ def test_bwd_long_sequences_uniform_tiles():
     _check(_gpu(case, g), _oracle(case, g), "bf16", "long")
 
 
+@pytest.mark.parametrize("P,Tb", [(1, 1), (2, 3), (33, 1)])
+def test_bwd_tiny_bias_tables(P, Tb):
+    """Degenerate tables: with P = 1 every pair's position bucket is the clamped one, with P = 2 only the
+    diagonal is unclamped, and Tb = 1 gives one time bucket.  Sequences long enough for near-diagonal
+    tiles both with and without clamped pairs; also the candidate mask (its candidate waves sum the
+    position buckets score by score)."""
+    print(f"\n[case] bwd tiny tables P={P} Tb={Tb}", flush=True)
+    case = I.attn_case("bwdt", 1150 + P + Tb, [700, 1, 130, 64], H=2, Dh=64, P=P, Tb=Tb, dtype="bf16",
+                       with_u=False)
+    g = _grad_out(case, 1150)
+    _check(_gpu(case, g), _oracle(case, g), "bf16", f"P={P} Tb={Tb}")
+    cc = I.attn_case("bwdtc", 1160 + P + Tb, [400, 90], H=2, Dh=64, P=P, Tb=Tb, dtype="bf16",
+                     num_candidates=[70, 30], with_u=False)
+    gc = _grad_out(cc, 1160)
+    _check(_gpu(cc, gc), _oracle(cc, gc), "bf16", f"candidates P={P} Tb={Tb}")
+
+
 def test_bwd_deterministic_and_bins_consistent():
     print("\n[case] bwd determinism", flush=True)
     case = I.attn_case("bwdd", 1140, [1500, 900, 3], H=2, Dh=64, P=300, Tb=40, dtype="bf16", with_u=False)
