@@ -316,13 +316,13 @@ attn_bwd_dkdv_kernel(const AttnArgs p, const int n_kblocks) {
   }
 
   // ---- epilogue: dK^T / dV^T element e of dh block db is dh = 32*db + 8*(e/4) + 4*half + e%4
-  {
+  // (the lane's key rebuilt from lane_now(), not held across the loop)
   const int le = lane_now();
-  const int my_k = ka + (le & 31), half = le >> 5;
-  const bool my_valid = my_k < n;
-  if (my_valid && p.z_q) {
-    T *kz = (T *)p.z_k + (int64_t)(o0 + my_k) * p.z_row_stride + h * DH;
-    T *vz = (T *)p.z_v + (int64_t)(o0 + my_k) * p.z_row_stride + h * DH;
+  const int e_key = ka + (le & 31), e_half = le >> 5;
+  const bool e_valid = e_key < n;
+  if (e_valid && p.z_q) {
+    T *kz = (T *)p.z_k + (int64_t)(o0 + e_key) * p.z_row_stride + h * DH;
+    T *vz = (T *)p.z_v + (int64_t)(o0 + e_key) * p.z_row_stride + h * DH;
 #pragma unroll
     for (int db = 0; db < L::kDB; ++db)
 #pragma unroll
@@ -331,12 +331,12 @@ attn_bwd_dkdv_kernel(const AttnArgs p, const int n_kblocks) {
                              dk.d[db][4 * e4 + 3] * cb};
         const float gv[4] = {dv.d[db][4 * e4 + 0] * cb, dv.d[db][4 * e4 + 1] * cb, dv.d[db][4 * e4 + 2] * cb,
                              dv.d[db][4 * e4 + 3] * cb};
-        silu_grad_store4(kz + 32 * db + 8 * e4 + 4 * half, gk);
-        silu_grad_store4(vz + 32 * db + 8 * e4 + 4 * half, gv);
+        silu_grad_store4(kz + 32 * db + 8 * e4 + 4 * e_half, gk);
+        silu_grad_store4(vz + 32 * db + 8 * e4 + 4 * e_half, gv);
       }
-  } else if (my_valid) {
-    float *krow = p.dk + (int64_t)(o0 + my_k) * p.out_row_stride + h * DH;
-    float *vrow = p.dv + (int64_t)(o0 + my_k) * p.out_row_stride + h * DH;
+  } else if (e_valid) {
+    float *krow = p.dk + (int64_t)(o0 + e_key) * p.out_row_stride + h * DH;
+    float *vrow = p.dv + (int64_t)(o0 + e_key) * p.out_row_stride + h * DH;
 #pragma unroll
     for (int db = 0; db < L::kDB; ++db)
 #pragma unroll
@@ -347,10 +347,9 @@ attn_bwd_dkdv_kernel(const AttnArgs p, const int n_kblocks) {
           wk[x] = dk.d[db][4 * e4 + x] * cb;
           wv[x] = dv.d[db][4 * e4 + x] * cb;
         }
-        *(floatx4 *)(krow + 32 * db + 8 * e4 + 4 * half) = wk;
-        *(floatx4 *)(vrow + 32 * db + 8 * e4 + 4 * half) = wv;
+        *(floatx4 *)(krow + 32 * db + 8 * e4 + 4 * e_half) = wk;
+        *(floatx4 *)(vrow + 32 * db + 8 * e4 + 4 * e_half) = wv;
       }
-  }
   }
 }
 
