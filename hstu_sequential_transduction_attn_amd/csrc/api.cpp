@@ -515,7 +515,7 @@ LayerSaved layer_saved(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, i
 // bias-gradient bins, the token-contiguous transposes x^T, dr^T, g^T, dz^T
 // (dtype, T padded to Tp, a multiple of 32) and the split-K partial products of the weight gradients.
 struct LayerBwdWs {
-  size_t fwd, w1t, w2t, dg, g, d_o, bins, xt, drt, gt, dzt, part, total;
+  size_t fwd, w1t, w2t, dg, g, d_o, bins, xt, drt, gt, dzt, part, bsum, total;
   int64_t Tp;
   int split_w1, split_w2;
 };
@@ -550,6 +550,7 @@ LayerBwdWs layer_bwd_ws(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, 
   const size_t p1 = w.split_w1 > 1 ? (size_t)w.split_w1 * 4 * HD * D : 0;
   const size_t p2 = w.split_w2 > 1 ? (size_t)w.split_w2 * D * HD : 0;
   w.part = take((p1 > p2 ? p1 : p2) * 4);
+  w.bsum = take((size_t)(4 * HD + D) * hstu::transpose_colsum_ld((int)w.Tp) * 4);   // bias-sum tile partials
   w.total = off;
   return w;
 }
@@ -765,10 +766,15 @@ hstu_status_t layer_bwd_impl(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
     // ---- weight and bias gradients from token-contiguous transposes
     const int Tp = (int)ws.Tp;
     HSTU_TRY(hstu::launch_transpose(x, x_f32, wsb + ws.xt, f32w, (int)T, (int)D, Tp, s), "x transpose");
-    HSTU_TRY(hstu::launch_transpose(dr, dr_f32, wsb + ws.drt, f32w, (int)T, (int)D, Tp, s), "dr transpose");
+    // the bias gradients (column sums of dz and dr over the tokens) come from the same tiles
+    const int ldp = hstu::transpose_colsum_ld(Tp);
+    float *bsum = (float *)(wsb + ws.bsum);
+    float *bsum_out = bsum + (size_t)4 * HD * ldp;
+    HSTU_TRY(hstu::launch_transpose(dr, dr_f32, wsb + ws.drt, f32w, (int)T, (int)D, Tp, s,
+                                    grads->d_b_out ? bsum_out : nullptr), "dr transpose");
     HSTU_TRY(hstu::launch_transpose(wsb + ws.g, f32w, wsb + ws.gt, f32w, (int)T, (int)HD, Tp, s), "g transpose");
-    HSTU_TRY(hstu::launch_transpose(fb + sv.z, f32w, wsb + ws.dzt, f32w, (int)T, (int)(4 * HD), Tp, s),
-             "dz transpose");
+    HSTU_TRY(hstu::launch_transpose(fb + sv.z, f32w, wsb + ws.dzt, f32w, (int)T, (int)(4 * HD), Tp, s,
+                                    grads->d_b_uvqk ? bsum : nullptr), "dz transpose");
     hstu::GemmPlainArgs pw{};
     pw.a = wsb + ws.dzt; pw.a_f32 = f32w; pw.b = wsb + ws.xt; pw.c = grads->d_w_uvqk; pw.c_f32 = 1;
     pw.M = (int32_t)(4 * HD); pw.N = (int32_t)D; pw.K = Tp; pw.dtype = dt;
@@ -778,9 +784,9 @@ hstu_status_t layer_bwd_impl(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
     pw.M = (int32_t)D; pw.N = (int32_t)HD; pw.splits = ws.split_w2;
     HSTU_TRY(hstu::launch_gemm_plain(pw, s), "d_w_out GEMM launch");
     if (grads->d_b_uvqk)
-      HSTU_TRY(hstu::launch_row_sum(wsb + ws.dzt, f32w, grads->d_b_uvqk, (int)(4 * HD), Tp, s), "d_b_uvqk launch");
+      HSTU_TRY(hstu::launch_row_sum(bsum, 1, grads->d_b_uvqk, (int)(4 * HD), ldp, s), "d_b_uvqk launch");
     if (grads->d_b_out)
-      HSTU_TRY(hstu::launch_row_sum(wsb + ws.drt, f32w, grads->d_b_out, (int)D, Tp, s), "d_b_out launch");
+      HSTU_TRY(hstu::launch_row_sum(bsum_out, 1, grads->d_b_out, (int)D, ldp, s), "d_b_out launch");
 #undef HSTU_TRY
     return ok();
   } catch (...) {

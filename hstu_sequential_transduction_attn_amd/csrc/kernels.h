@@ -194,9 +194,12 @@ struct NormGateBwdArgs {
 };
 hipError_t launch_norm_gate_bwd(const NormGateBwdArgs &a, hipStream_t stream);
 
-// dst [C][Rp] = src[R][C]^T with rows R..Rp-1 zero (C % 4 == 0, Rp % 4 == 0, Rp >= R).
+// dst [C][Rp] = src[R][C]^T with rows R..Rp-1 zero (C % 4 == 0, Rp % 4 == 0, Rp >= R).  With colsum,
+// also colsum[c * transpose_colsum_ld(Rp) + t] = the sum of column c over the 64 source rows of tile t
+// (0 past the rows), for launch_row_sum to add in a fixed order.
 hipError_t launch_transpose(const void *src, int src_f32, void *dst, int dst_f32, int R, int C, int Rp,
-                            hipStream_t stream);
+                            hipStream_t stream, float *colsum = nullptr);
+int transpose_colsum_ld(int Rp);   // 64-row tiles of Rp rows, rounded up to a multiple of 4
 // out[c] = sum of row c of src [rows][Rp] (Rp % 4 == 0), fixed summation order.
 hipError_t launch_row_sum(const void *src, int src_f32, float *out, int rows, int Rp, hipStream_t stream);
 // p[0..n) = 0 (a kernel, not a memset, so that a captured graph replays it faithfully).

@@ -175,10 +175,12 @@ __global__ void __launch_bounds__(256) norm_gate_bwd_kernel(const float *__restr
 }
 
 // ---- dst[c][r] = src[r][c] for r < R, 0 for R <= r < Rp (TI -> TO, rounded when TO is bf16).
-// 64 x 64 tiles through a padded LDS tile; C % 4 == 0, Rp % 4 == 0.
+// 64 x 64 tiles through a padded LDS tile; C % 4 == 0, Rp % 4 == 0.  With colsum, each tile also writes
+// its 64 column sums (of the source values) to colsum[c * ldp + blockIdx.y]: four lanes per column add
+// 16 rows each, then a fixed butterfly over the four.  Tiles past the rows write zeros.
 template <typename TI, typename TO>
 __global__ void __launch_bounds__(256) transpose_kernel(const TI *__restrict__ src, TO *__restrict__ dst, int R, int C,
-                                                        int Rp) {
+                                                        int Rp, float *__restrict__ colsum, int ldp) {
   __shared__ float tile[64][65];
   const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
   const int tid = threadIdx.x;
@@ -194,6 +196,15 @@ __global__ void __launch_bounds__(256) transpose_kernel(const TI *__restrict__ s
     }
   }
   __syncthreads();
+  if (colsum) {
+    const int cc = tid / 4, q = tid % 4;
+    float sum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += tile[16 * q + r][cc];
+    sum += __shfl_xor(sum, 1, 4);
+    sum += __shfl_xor(sum, 2, 4);
+    if (q == 0 && c0 + cc < C) colsum[(int64_t)(c0 + cc) * ldp + blockIdx.y] = sum;
+  }
   {
     const int rr = 4 * (tid % 16), cc = tid / 16;
 #pragma unroll
@@ -260,9 +271,11 @@ hipError_t launch_norm_gate_bwd_t(const NormGateBwdArgs &a, hipStream_t s) {
 }
 
 template <typename TI, typename TO>
-hipError_t launch_transpose_t(const void *src, void *dst, int R, int C, int Rp, hipStream_t s) {
-  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((Rp + 63) / 64));
-  hipLaunchKernelGGL((transpose_kernel<TI, TO>), grid, dim3(256), 0, s, (const TI *)src, (TO *)dst, R, C, Rp);
+hipError_t launch_transpose_t(const void *src, void *dst, int R, int C, int Rp, float *colsum, hipStream_t s) {
+  const int ldp = transpose_colsum_ld(Rp);
+  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)(colsum ? ldp : (Rp + 63) / 64));
+  hipLaunchKernelGGL((transpose_kernel<TI, TO>), grid, dim3(256), 0, s, (const TI *)src, (TO *)dst, R, C, Rp, colsum,
+                     ldp);
   return hipGetLastError();
 }
 
@@ -278,12 +291,15 @@ hipError_t launch_norm_gate_bwd(const NormGateBwdArgs &a, hipStream_t s) {
   return a.dtype == kF32 ? launch_norm_gate_bwd_t<float>(a, s) : launch_norm_gate_bwd_t<__bf16>(a, s);
 }
 
-hipError_t launch_transpose(const void *src, int src_f32, void *dst, int dst_f32, int R, int C, int Rp, hipStream_t s) {
+int transpose_colsum_ld(int Rp) { return ((Rp + 63) / 64 + 3) / 4 * 4; }
+
+hipError_t launch_transpose(const void *src, int src_f32, void *dst, int dst_f32, int R, int C, int Rp, hipStream_t s,
+                            float *colsum) {
   if (C == 0 || Rp == 0) return hipSuccess;
-  if (src_f32 && dst_f32) return launch_transpose_t<float, float>(src, dst, R, C, Rp, s);
-  if (src_f32) return launch_transpose_t<float, __bf16>(src, dst, R, C, Rp, s);
-  if (dst_f32) return launch_transpose_t<__bf16, float>(src, dst, R, C, Rp, s);
-  return launch_transpose_t<__bf16, __bf16>(src, dst, R, C, Rp, s);
+  if (src_f32 && dst_f32) return launch_transpose_t<float, float>(src, dst, R, C, Rp, colsum, s);
+  if (src_f32) return launch_transpose_t<float, __bf16>(src, dst, R, C, Rp, colsum, s);
+  if (dst_f32) return launch_transpose_t<__bf16, float>(src, dst, R, C, Rp, colsum, s);
+  return launch_transpose_t<__bf16, __bf16>(src, dst, R, C, Rp, colsum, s);
 }
 
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s) {
