@@ -241,6 +241,35 @@ def attn_bwd(jag: dict, q, k, v, pos_bias, time_bias, d_out, return_sq=False):
     return dq, dk, dv, dwp, dwt
 
 
+def attn_bwd_sampled(jag: dict, q, k, v, pos_bias, time_bias, d_out, b, h, rows, cols):
+    """dq for the query rows `rows` and dk, dv for the key rows `cols` of sequence b, head h, in float64:
+    attn_bwd's definitions restricted to one row of S and dP per sampled query and one column per
+    sampled key, so that single rows of a long sequence can be checked without the n x n products."""
+    q, k, v, g = (np.asarray(a, np.float64) for a in (q, k, v, d_out))
+    wp = np.asarray(pos_bias, np.float64)
+    wt = np.asarray(time_bias, np.float64)
+    tau = np.asarray(jag["timestamps"], np.int64)
+    R, P, Tb = wp.shape[0], wp.shape[1], wt.shape[1]
+    r = 0 if R == 1 else h
+    o0, o1, n, n_hist, mask, scale = _seq_params(jag, b)
+    pos = positions(n, n_hist, mask)
+    tb = tau[o0:o1]
+    qh, kh, vh, gh = q[o0:o1, h], k[o0:o1, h], v[o0:o1, h], g[o0:o1, h]
+    ri = np.asarray(rows, dtype=np.int64)
+    s = (qh[ri] @ kh.T + wp[r][position_bucket(pos[ri][:, None], pos[None, :], P)]
+         + wt[r][time_bucket(tb[ri][:, None], tb[None, :], Tb)])
+    ds = np.where(allowed(ri, n, n_hist, mask), scale * (gh[ri] @ vh.T) * silu_grad(s), 0.0)
+    dq = ds @ kh
+    cj = np.asarray(cols, dtype=np.int64)
+    s2 = (qh @ kh[cj].T + wp[r][position_bucket(pos[:, None], pos[cj][None, :], P)]
+          + wt[r][time_bucket(tb[:, None], tb[cj][None, :], Tb)])
+    ok2 = allowed(np.arange(n), n, n_hist, mask)[:, cj]
+    dv = scale * (np.where(ok2, silu(s2), 0.0).T @ gh)
+    ds2 = np.where(ok2, scale * (gh @ vh[cj].T) * silu_grad(s2), 0.0)
+    dk = ds2.T @ qh
+    return dq, dk, dv
+
+
 # --------------------------------------------------------------------------- cached-history scoring
 def attn_cached(hist: dict, cand: dict, k_hist, v_hist, q, k, v, pos_bias, time_bias, attn_scale=None):
     """Candidates scored against a cached user history: O [T_c, H, Dh] in float64.

@@ -130,3 +130,28 @@ def test_bwd_empty_batch_zeroes_the_bias_gradients():
     dq, dk, dv, d_pos, d_time = ops.attn_bwd(offs, tau, q, q, q, q, wp, wt, max_seq_len=0)
     assert dq.shape[0] == 0
     assert not torch.any(d_pos).item() and not torch.any(d_time).item()
+
+
+def test_bwd_L8192_sampled_rows_against_oracle():
+    """The attention backward at its benchmark shape (8 x 8192, H = 4 x 128, P = Tb = 256), launched as
+    for the full batch: dq of sampled query rows and dk, dv of sampled key rows of two (sequence, head)
+    pairs against the oracle's row- and column-restricted backward (tile edges, the first and last rows,
+    and random rows)."""
+    from hstu_sequential_transduction_attn_amd import configs as C
+    print("\n[case] attn_L8192 backward, sampled rows", flush=True)
+    case = C.attn_L8192()
+    g = _grad_out(case, 1170)
+    got = _gpu(case, g)
+    rng = np.random.default_rng(1171)
+    picks = [0, 1, 31, 32, 63, 64, 127, 128, 4095, 4096, 8190, 8191] + [int(x) for x in rng.integers(0, 8192, 4)]
+    jag = oracle_jag(case.jagged)
+    offs = case.jagged.seq_offsets
+    for b, h in [(0, 0), (7, 3)]:
+        want = O.attn_bwd_sampled(jag, case.q.values, case.k.values, case.v.values, case.rab.pos_bias,
+                                  case.rab.time_bias, g.values, b, h, picks, picks)
+        idx = int(offs[b]) + np.asarray(picks)
+        for x, y, name in zip((got[0][idx, h], got[1][idx, h], got[2][idx, h]), want, NAMES):
+            r, m = rel_l2(x, y), max_abs(x, y)
+            print(f"  b={b} h={h} {name}: rel_l2={r:.3e} max_abs={m:.3e}")
+            bound = 2e-2 + 2.0 ** -7 * float(np.abs(y).max())
+            assert r <= 5e-3 and m <= bound, f"b={b} h={h} {name}: rel_l2={r:.3e} max_abs={m:.3e}"

@@ -106,3 +106,22 @@ def test_bin_sums_of_squares():
     ds = (g1[0, 0] @ v1[0, 0]) * O.silu_grad(s)
     np.testing.assert_allclose(sqp1[0, 0], ds ** 2, rtol=1e-12)
     np.testing.assert_allclose(sqt1[0, 0], ds ** 2, rtol=1e-12)
+
+
+@pytest.mark.parametrize("mask", [O.CAUSAL, O.CAUSAL_CANDIDATES])
+def test_sampled_rows_and_columns_match_the_full_backward(mask):
+    """attn_bwd_sampled restricts attn_bwd (pinned above to finite differences) to single query rows and
+    key rows: equal to it on every sampled row, per-head tables, both masks."""
+    lengths = [11, 1, 17]
+    q, k, v, g, wp, wt, tau = _inputs(12, lengths, H=3, P=6, Tb=5, R=3)
+    cands = [4, 1, 6] if mask == O.CAUSAL_CANDIDATES else None
+    jag = _jag(lengths, tau, mask=mask, num_candidates=cands, attn_scale=[0.3, 1.0, -0.7])
+    dq, dk, dv, _, _ = O.attn_bwd(jag, q, k, v, wp, wt, g)
+    offs = jag["seq_offsets"]
+    for b, rows, cols in [(0, [0, 3, 10], [0, 5, 10]), (1, [0], [0]), (2, [16, 2, 11, 12], [1, 12, 16])]:
+        for h in range(3):
+            sq, sk, sv = O.attn_bwd_sampled(jag, q, k, v, wp, wt, g, b, h, rows, cols)
+            o0 = int(offs[b])
+            np.testing.assert_allclose(sq, dq[o0 + np.asarray(rows), h], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(sk, dk[o0 + np.asarray(cols), h], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(sv, dv[o0 + np.asarray(cols), h], rtol=1e-12, atol=1e-13)
