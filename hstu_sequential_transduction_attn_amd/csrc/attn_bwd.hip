@@ -17,7 +17,9 @@
 // A key sees the queries i >= j (a history key also every candidate; a candidate key only itself), so
 // the tiles run from the key block's first row to the end of the sequence.  Each wave classifies each
 // tile in scalar code: none, uniform (one bias for every pair), or general (per-score bias and mask).
-// The registers (keys' K and V, dK^T and dV^T accumulators) take one wave per SIMD.
+// bf16 runs two waves per SIMD: the keys' K and V and the dK^T and dV^T accumulators fill most of the
+// 256 registers, and the loop keeps nothing else across tiles that can be rebuilt (see KeyCtx), so
+// nothing spills (a reload from scratch would also wait for the next tile's direct-to-LDS prefetch).
 #include "attn_common.hpp"
 
 namespace hstu {
@@ -142,7 +144,7 @@ __device__ __forceinline__ void dkdv_tile(OAcc<Layout<T, DH>::kDB> &dk, OAcc<Lay
 __device__ __forceinline__ int64_t smin64(int64_t a, int64_t b) { return a < b ? a : b; }
 __device__ __forceinline__ int64_t smax64(int64_t a, int64_t b) { return a > b ? a : b; }
 
-// bf16: two waves per SIMD (<= 256 registers; at Dh = 128 a few spill); fp32 operands take twice the
+// bf16: two waves per SIMD (<= 256 registers, none spilled at Dh = 128); fp32 operands take twice the
 // fragment registers and run one wave per SIMD.
 template <typename T, int DH>
 __global__ void __launch_bounds__(kThreads)

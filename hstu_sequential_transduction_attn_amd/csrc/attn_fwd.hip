@@ -749,8 +749,8 @@ attn_fwd_kernel(const AttnArgs p, const int n_qblocks) {
 }
 
 // The backward's dQ pass carries dO fragments and bucket indices as well.  It too runs two waves per
-// SIMD: at Dh = 128 a few registers spill, and that is still faster than one wave per SIMD without
-// spills (the waves' MFMA and VALU phases overlap).
+// SIMD; at Dh = 128 (bf16) it fits the 256 registers without spilling because its lane offsets are
+// rebuilt at each tile from lane_now() rather than held across the loop.
 template <typename T, int DH>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq_kernel(const AttnArgs p, const int n_qblocks) {
