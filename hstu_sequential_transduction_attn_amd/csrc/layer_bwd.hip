@@ -12,7 +12,8 @@
 //                                                                        backward's epilogues
 //   dx = dr + dz W1;  dW1 = dz^T x;  dW2 = dr^T g                      -> GEMMs (the weight gradients on
 //                                                                        token-contiguous transposes)
-//   db1 = sum_t dz,  db2 = sum_t dr                                   -> row sums of the transposes
+//   db1 = sum_t dz,  db2 = sum_t dr                                   -> column sums per 64-row tile in
+//                                                                        the transposes, then added
 // where LN'(a) b = rstd (b - mean(b) - a_hat mean(b a_hat)) is the LayerNorm Jacobian applied to b.
 //
 // Row kernels use one wave per row with the row in registers (two passes over registers for the
