@@ -99,19 +99,21 @@ __device__ __forceinline__ void tile_body(OAcc<Layout<T, DH>::kDB> &oacc,
 
 // Bias-table gradient bins of one wave: all uniform and two-bucket tiles have position bucket P-1
 // (run_p); consecutive uniform tiles with the same time bucket share run_t.  In the other tiles a
-// score of position bucket P-1 also goes to run_p, any other position bucket straight into the wave's
-// LDS bin (the lanes of one instruction hold distinct queries, so they rarely share a bin), and the
-// time buckets are run-length summed per lane (lane_t, lane_bt): along a query's keys the bucket
-// changes rarely, and a lane adds its run to the LDS bin only when it does.  Adding every score to its
-// time bin directly made most lanes of each instruction hit the same LDS address.  Per-wave bins,
-// program order and single-lane flushes keep the sums in a fixed order.
+// score of position bucket P-1 also goes to run_p; the other position buckets are summed along
+// anti-diagonals first (diag_pos_bins) in waves of history queries, and go score by score into the
+// wave's LDS bins in waves of candidates.  The time buckets are run-length summed per lane (lane_t,
+// lane_bt): along a query's keys the bucket changes rarely, and a lane adds its run to the LDS bin only
+// when it does.  Adding every score to its time bin directly made most lanes of each instruction hit
+// the same LDS address.  Per-wave bins, program order and single-lane flushes keep the sums in a fixed
+// order.
 struct GradBins {
   HSTU_LDS float *hp, *ht;   // this wave's position bins [P] and time bins [kTimeTab]
   float run_p, run_t;        // per-lane running sums
   int cur_bt;                // wave-uniform time bucket of run_t; -1 before the first uniform tile
   float lane_t;              // per-lane run of time bucket lane_bt (general tiles)
   int lane_bt;
-  bool diag;                 // wave-uniform: every query of the wave is a history query
+  bool diag;                 // wave-uniform: every query of the wave is a history query, so the
+                             // position bucket of every unclamped pair is i - j
 };
 
 // Lane i takes lane i + 1 (lane 63 takes 0), and lane i takes lane (i + 1) mod 64.
