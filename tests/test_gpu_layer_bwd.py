@@ -192,3 +192,28 @@ def test_layer_bwd_from_saved_activations_is_bitwise_the_recompute(dtype, ln_out
     assert torch.equal(y_plain, y_saved), "forward with saved activations differs"
     for name in NAMES:
         assert torch.equal(got[name], want[name]), f"{name}: backward from saved activations differs"
+
+
+@pytest.mark.parametrize("seed", [7021, 7052, 7003, 7037])
+def test_layer_bwd_f32_random_shapes(seed):
+    """fp32 layers on seeded random shapes (widths that are not multiples of the tiles, tiny and odd
+    bias tables, candidates, biases, the output LayerNorm), checked to 1e-5 relative: the arithmetic of
+    every step with no bf16 rounding to hide behind."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 6))
+    lengths = [int(x) for x in rng.integers(0, 300, B)]
+    if rng.random() < 0.3:
+        lengths[0] = int(rng.integers(300, 1100))
+    D = int(rng.choice([32, 64, 72, 96, 128, 200, 256]))
+    H, Dh = int(rng.integers(1, 4)), int(rng.choice([32, 64, 128]))
+    P, Tb = int(rng.integers(1, 200)), int(rng.integers(1, 70))
+    ln_output = bool(rng.random() < 0.5)
+    case = I.jagged_layer_case("lrnd", seed, lengths, D=D, H=H, Dh=Dh, P=P, Tb=Tb, dtype="f32",
+                               bias_std=float(rng.choice([0.0, 0.2])))
+    if rng.random() < 0.4:
+        case.jagged.mask = I.CAUSAL_CANDIDATES
+        case.jagged.num_candidates = np.array([int(rng.integers(0, n + 1)) for n in lengths], np.int32)
+    print(f"\n[case] layer bwd f32 random seed={seed} lengths={lengths} D={D} H={H} Dh={Dh} P={P} Tb={Tb} "
+          f"ln_output={ln_output} candidates={case.jagged.num_candidates is not None}", flush=True)
+    dy = _dy(case, seed + 1, "f32")
+    _check(_gpu(case, dy, ln_output), _oracle(case, dy, ln_output), "f32", f"random {seed}")
