@@ -41,11 +41,14 @@ struct KeyCtx {
   const HSTU_LDS int64_t *ktau;    // the wave's 32 key timestamps
   const HSTU_LDS float *wp, *wt;
   const HSTU_LDS char *stage;
+  uint32_t base_lo;    // 32-bit mode: low word of the tile's smallest timestamp (all within 2^32 of it)
 };
 
 // Bias (and mask) of the 16 scores of 32-query block qb in place; element e holds query
 // q0 + 32*qb + 16*(e/8) + 8*half + e%8.
-template <typename T, int DH, bool MASKED>
+// K32: every timestamp of the tile lies within 2^32 of c.base_lo's full value, so each |dt| is the
+// distance of two 32-bit offsets from it (one v_sad_u32) instead of a 64-bit difference.
+template <typename T, int DH, bool MASKED, bool K32>
 __device__ __forceinline__ void adjust_block_keys(floatx16 &s, const KeyCtx &c, int qb, int lane) {
   using L = Layout<T, DH>;
   const int half = lane >> 5;
@@ -53,6 +56,7 @@ __device__ __forceinline__ void adjust_block_keys(floatx16 &s, const KeyCtx &c, 
   const int my_pos = imin(my_k, c.pos_lim);      // a candidate key sits at position nh
   const int q_hi = my_k < c.nh ? c.n - 1 : my_k;  // allowed queries: my_k <= i <= q_hi
   const int64_t my_tau = c.ktau[lane & 31];
+  const uint32_t koff = (uint32_t)(uint64_t)my_tau - c.base_lo;
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const int il0 = 32 * qb + 16 * g + 8 * half;
@@ -70,7 +74,8 @@ __device__ __forceinline__ void adjust_block_keys(floatx16 &s, const KeyCtx &c, 
       const int pi = imin(i, c.pos_lim);
       const uint32_t dp = __usad((uint32_t)pi, (uint32_t)my_pos, 0u);
       const int bp = (int)(dp < (uint32_t)(c.P - 1) ? dp : (uint32_t)(c.P - 1));
-      const int bt = imin(bitlen_absdiff(ti[e8], my_tau), c.Tb - 1);
+      const int bt = imin(K32 ? bitlen_u32(__usad(koff, (uint32_t)(uint64_t)ti[e8] - c.base_lo, 0u))
+                              : bitlen_absdiff(ti[e8], my_tau), c.Tb - 1);
       const float bias = c.wp[bp] + c.wt[bt];
       if constexpr (MASKED) {
         const bool ok = (i >= my_k) & (i <= q_hi);
@@ -96,8 +101,10 @@ __device__ __forceinline__ void dkdv_block(OAcc<Layout<T, DH>::kDB> &dk, OAcc<La
   const HSTU_LDS char *lG = c.stage + L::kOffV;
   floatx16 s;
   score_block<T, DH>(s, lQ, qb, l32, half, kf);
-  if (body == kGen64) adjust_block_keys<T, DH, false>(s, c, qb, lane);
-  else if (body == kGen64M) adjust_block_keys<T, DH, true>(s, c, qb, lane);
+  if (body == kGen32) adjust_block_keys<T, DH, false, true>(s, c, qb, lane);
+  else if (body == kGen32M) adjust_block_keys<T, DH, true, true>(s, c, qb, lane);
+  else if (body == kGen64) adjust_block_keys<T, DH, false, false>(s, c, qb, lane);
+  else if (body == kGen64M) adjust_block_keys<T, DH, true, false>(s, c, qb, lane);
   // A = SiLU(x) and SiLU'(x) from S, then dV; dP only after that, so that S, A and dP are never all
   // live at once (at two waves per SIMD the registers are the limit)
   float a[16], gd[16];
@@ -282,13 +289,17 @@ attn_bwd_dkdv_kernel(const AttnArgs p, const int n_kblocks) {
       const bool any = ka < nh ? ql >= ka : (ql >= ka && q0 <= kl);
       if (any) {
         const bool all = kl < nh && q0 >= kl && q0 + kBN - 1 < n;   // a full tile: no repeated rows
-        body = all ? kGen64 : kGen64M;
+        // the tile's timestamp range (rows past the end repeat the last row, inside the last chunk)
+        int64_t qmin = stats[2 * (q0 >> 5)], qmax = stats[2 * (q0 >> 5) + 1];
+        if (q0 + kChunk < n) {
+          qmin = smin64(qmin, stats[2 * (q0 >> 5) + 2]);
+          qmax = smax64(qmax, stats[2 * (q0 >> 5) + 3]);
+        }
+        const int64_t tmin = smin64(qmin, kmin);
+        const bool k32 = (uint64_t)smax64(qmax, kmax) - (uint64_t)tmin < (1ull << 32);
+        body = k32 ? (all ? kGen32 : kGen32M) : (all ? kGen64 : kGen64M);
+        c.base_lo = (uint32_t)(uint64_t)tmin;
         if (all && imin(q0, nh) - kpl >= P - 1) {
-          int64_t qmin = stats[2 * (q0 >> 5)], qmax = stats[2 * (q0 >> 5) + 1];
-          if (q0 + kChunk < n) {
-            qmin = smin64(qmin, stats[2 * (q0 >> 5) + 2]);
-            qmax = smax64(qmax, stats[2 * (q0 >> 5) + 3]);
-          }
           uint64_t lo, hi;
           if (qmin >= kmax) {
             lo = (uint64_t)qmin - (uint64_t)kmax;
