@@ -686,7 +686,6 @@ hstu_status_t layer_bwd_impl(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
     char *wsb = (char *)workspace;
     const int dt = ityp, f32w = dtype == HSTU_F32;
     const int x_f32 = x_dtype == HSTU_F32, g_f32 = grad_dtype == HSTU_F32;
-    const bool split = dtype == HSTU_BF16 && w->act_split != 0;
     hipError_t e;
 #define HSTU_TRY(call, what)                 \
   do {                                       \

@@ -120,7 +120,13 @@ size_t hstu_attn_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_
                                  hstu_dtype_t in_dtype);
 
 /*
- * Pointwise attention forward (steps 2-3 of the layer; the causal-jagged kernel):
+ * Pointwise attention forward (steps 2-3 of the layer; the causal-jagged kernel).  Passage: "DLRMv4"
+ * page, section "モデルアーキテクチャ：HSTUが従来の特徴インタラクションスタックに取って代わる" --
+ * pointwise attention aggregates the sequence, with a bias from the positional and the temporal
+ * distance of two events; section "1つの訓練サンプルがHSTUでどのように処理されるか" -- each user's
+ * time-ordered events form one causal block, candidates appended at its end (the mask
+ * HSTU_MASK_CAUSAL_CANDIDATES); "Actions Speak Louder than Words ...", abstract -- the attention
+ * variant run at sequence length 8192.  What it computes:
  *   out[t][h][:] = c_b * sum_{allowed j} SiLU(q_t . k_j + rab) v_j   for every token t of every sequence.
  * q, k, v: [T][H][Dh] row-major (device), dtype in_dtype (HSTU_BF16 or HSTU_F32).
  * out:     [T][H][Dh] row-major (device), out_dtype = HSTU_F32 or in_dtype; may not alias q, k, v.
@@ -205,7 +211,13 @@ size_t hstu_layer_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc
                                   const hstu_layer_weights_t *w, hstu_dtype_t dtype);
 
 /*
- * One HSTU layer forward (steps 1-4):  y = [LN](x + W2 (LN(O) * U) + b2).
+ * One HSTU layer forward (steps 1-4):  y = [LN](x + W2 (LN(O) * U) + b2).  Passage: "DLRMv4" page,
+ * section "モデルアーキテクチャ：HSTUが従来の特徴インタラクションスタックに取って代わる" -- inside a
+ * layer a single projection produces every internal representation, pointwise attention with a
+ * position/time bias aggregates the sequence, and a gated transformation lets the aggregated features
+ * interact in place of the cross network and feed-forward block.  The residual and the optional output
+ * LayerNorm are the stack's ("residual plus LayerNorm between layers" is the reading taken for the
+ * stacked workloads).
  * dtype:   element type of the weights and of the MFMA operands (HSTU_BF16: bf16 MFMA with fp32
  *          accumulation; HSTU_F32: fp32 throughout).
  * x:       [T][D] (device), element type x_dtype in {HSTU_F32, dtype}.
@@ -325,7 +337,10 @@ hstu_status_t hstu_layer_bwd_saved(const hstu_jagged_t *jag, const hstu_attn_des
                                    size_t workspace_bytes, void *stream);
 
 /*
- * Embedding gather (input staging before the first layer):  out[t][:] = table[ids[t]][:].
+ * Embedding gather (input staging before the first layer):  out[t][:] = table[ids[t]][:].  Passage:
+ * "DLRMv4" page, section "モデルアーキテクチャ：HSTUが従来の特徴インタラクションスタックに取って代わる"
+ * -- categorical ids become vectors by an embedding lookup; section "特徴拡張：Embedding Tableが
+ * 約560GBへ拡大" -- the tables those ids index (512-wide rows in the benchmark).
  * table: [table_rows][d] (device); ids: [T] int64 (device), each in [0, table_rows);
  * out: [T][d] (device).  Element type `dtype`; d * element size must be a multiple of 16 bytes.
  */
