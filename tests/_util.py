@@ -24,15 +24,17 @@ def max_abs(got: np.ndarray, want: np.ndarray) -> float:
     return float(d.max()) if d.size else 0.0
 
 
-# Ad-hoc (non-workload) cases can have outputs of magnitude ~10 (a length-1 sequence has c_b = 1),
-# where one bf16 ulp is 0.0625.  For them the absolute bar grows with the value: half an ulp of the
-# bf16 output (2^-9 relative) plus the bf16 rounding of SiLU(s) as the AV operand, i.e. 2^-8 |want|.
-BF16_REL_ELEM = 2.0 ** -8
+# Ad-hoc (non-workload) cases can have outputs of magnitude ~100 (a length-1 sequence has c_b = 1 and
+# O = SiLU(s) v with |s| up to ~35), where one bf16 ulp is 0.5.  For them the absolute bar grows with the
+# value.  bf16 keeps 8 significant bits, so one round-to-nearest moves a value by up to half an ulp,
+# 2^-8 of it; such an output is rounded twice (SiLU(s) as the bf16 AV operand, then the bf16 output),
+# which moves it by up to 2^-7 |want|.
+BF16_REL_ELEM = 2.0 ** -7
 
 
 def assert_close(got, want, dtype: str, what: str = "", magnitude_aware: bool = False):
     """The workloads' bar: bf16 max_abs <= 2e-2 and rel_l2 <= 5e-3; f32 rel_l2 <= 1e-5.
-    magnitude_aware (ad-hoc bf16 cases only): |got - want| <= 2e-2 + 2^-8 |want| elementwise."""
+    magnitude_aware (ad-hoc bf16 cases only): |got - want| <= 2e-2 + 2^-7 |want| elementwise."""
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     r, m = rel_l2(got, want), max_abs(got, want)
@@ -137,3 +139,4 @@ def gather_input(case: I.LayerCase):
     rows = dev(case.table_values)
     table.index_copy_(0, dev(case.table_touched.astype(np.int64)), rows)
     return ops.gather_rows(table, dev(case.ids.astype(np.int64)))
+
