@@ -170,7 +170,8 @@ def make_desc(num_heads: int, head_dim: int, pos_bias: torch.Tensor, time_bias: 
 
 
 def attn_fwd(seq_offsets, timestamps, q, k, v, pos_bias, time_bias, *, max_seq_len: int, mask: int = MASK_CAUSAL,
-             num_candidates=None, attn_scale=None, out_dtype: Optional[torch.dtype] = None, out=None, stream=None):
+             num_candidates=None, attn_scale=None, out_dtype: Optional[torch.dtype] = None, out=None, workspace=None,
+             stream=None):
     """O = hstu_attn_fwd(...): q, k, v [T, H, Dh] (bf16 or f32, contiguous); returns out [T, H, Dh]."""
     lib = load_library()
     T, H, Dh = q.shape
@@ -179,22 +180,27 @@ def attn_fwd(seq_offsets, timestamps, q, k, v, pos_bias, time_bias, *, max_seq_l
     jag = make_jagged(seq_offsets, timestamps, max_seq_len, num_candidates, attn_scale)
     desc = make_desc(H, Dh, pos_bias, time_bias, mask)
     dt = _dtype_code(q)
-    nws = lib.hstu_attn_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), dt)
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device) if nws else None
+    nws = int(lib.hstu_attn_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), dt))
+    if nws and (workspace is None or workspace.numel() < nws):
+        workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
     _check(lib.hstu_attn_fwd(ctypes.byref(jag), ctypes.byref(desc), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                             _dtype_code(out), _ptr(ws), nws, _stream(stream)))
+                             _dtype_code(out), _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                             _stream(stream)))
     return out
 
 
 def attn_bwd(seq_offsets, timestamps, q, k, v, d_out, pos_bias, time_bias, *, max_seq_len: int,
-             mask: int = MASK_CAUSAL, num_candidates=None, attn_scale=None, workspace=None, stream=None):
+             mask: int = MASK_CAUSAL, num_candidates=None, attn_scale=None, workspace=None, outs=None, stream=None):
     """(dq, dk, dv, d_pos_bias, d_time_bias) = hstu_attn_bwd(...): gradients of attn_fwd's output for
-    the upstream gradient d_out [T, H, Dh] (q's dtype); all returned in fp32."""
+    the upstream gradient d_out [T, H, Dh] (q's dtype); all returned in fp32 (into `outs` when given)."""
     lib = load_library()
     T, H, Dh = q.shape
     f32 = dict(dtype=torch.float32, device=q.device)
-    dq, dk, dv = (torch.empty((T, H, Dh), **f32) for _ in range(3))
-    d_pos, d_time = torch.empty(pos_bias.shape, **f32), torch.empty(time_bias.shape, **f32)
+    if outs is None:
+        dq, dk, dv = (torch.empty((T, H, Dh), **f32) for _ in range(3))
+        d_pos, d_time = torch.empty(pos_bias.shape, **f32), torch.empty(time_bias.shape, **f32)
+    else:
+        dq, dk, dv, d_pos, d_time = outs
     jag = make_jagged(seq_offsets, timestamps, max_seq_len, num_candidates, attn_scale)
     desc = make_desc(H, Dh, pos_bias, time_bias, mask)
     dt = _dtype_code(q)

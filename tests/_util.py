@@ -140,3 +140,36 @@ def gather_input(case: I.LayerCase):
     table.index_copy_(0, dev(case.table_touched.astype(np.int64)), rows)
     return ops.gather_rows(table, dev(case.ids.astype(np.int64)))
 
+
+# --------------------------------------------------------------------------- full-size workloads
+_CACHE = {}
+
+
+def cached(key, make):
+    """Compute make() once per test session (the workload cases and the oracle outputs of their longest
+    sequences are shared by the layer-path and stack-path tests)."""
+    if key not in _CACHE:
+        _CACHE[key] = make()
+    return _CACHE[key]
+
+
+def workload_case(name):
+    from hstu_sequential_transduction_attn_amd import configs as C
+    return cached(("case", name), getattr(C, name))
+
+
+def workload_sequences(case, shortest: int = 2):
+    """The `shortest` shortest sequences and the longest one (stable order of their lengths)."""
+    order = np.argsort(case.jagged.lengths, kind="stable")
+    return sorted({int(s) for s in order[:shortest]} | {int(order[-1])})
+
+
+def oracle_stack_sequence(name, case, seq):
+    """The float64 oracle of the whole stack on one sequence of a workload (jagged independence: a
+    sequence's output depends on its own tokens only)."""
+    from oracle import hstu_oracle as O
+
+    def make():
+        jag, idx = sub_jagged(case.jagged, [seq])
+        return O.stack_fwd(case.x.values[idx], oracle_jag(jag), oracle_layers(case), case.num_heads, case.head_dim)
+    return cached(("oracle", name, seq), make)

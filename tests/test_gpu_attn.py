@@ -140,24 +140,58 @@ def test_time_bucket_probe(dtype):
         assert (ind == want).all(), f"idx={idx}"
 
 
-def test_L8192_sampled_rows():
-    """The full L=8192 attention workload (8 x 8192, H=4, Dh=128, P=Tb=256), sampled rows vs the oracle."""
-    print("\n[case] attn_L8192 sampled rows", flush=True)
-    case = C.attn_L8192()
-    out = gpu_attn(case)
-    got = host(out)
+_L8192 = {}
+
+
+def _l8192_gpu():
+    """The full L=8192 attention workload (8 x 8192, H=4, Dh=128, P=Tb=256) and its bf16 output, computed
+    once per test session with the launch the benchmark times."""
+    if not _L8192:
+        case = C.attn_L8192()
+        out = gpu_attn(case)
+        torch.cuda.synchronize()
+        _L8192.update(case=case, out=out, got=host(out))
+    return _L8192["case"], _L8192["out"], _L8192["got"]
+
+
+def test_L8192_every_query_block():
+    """Every 128-row query block of every (sequence, head) of the L=8192 workload: its first and last row
+    and one random row inside it, against the oracle at the workload bar; plus fixed rows at the
+    64-key tile edges.  A second call is bitwise identical."""
+    print("\n[case] attn_L8192 every query block", flush=True)
+    case, out, got = _l8192_gpu()
     rng = np.random.default_rng(3)
-    rows = {b: np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 255, 256, 4095, 8190, 8191],
-                                         rng.integers(0, 8192, size=8)])) for b in range(8)}
+    n = 8192
+    rows = {}
+    for b in range(8):
+        blocks = np.arange(0, n, 128)
+        pick = np.concatenate([blocks, blocks + 127, blocks + rng.integers(1, 127, size=len(blocks)),
+                               [63, 64, 255, 256, 4095, 4096]])
+        rows[b] = np.unique(pick)
     want = _oracle(case, row_sample=rows)
     offs = case.jagged.seq_offsets
     g = np.concatenate([got[offs[b] + rows[b], h] for b in range(8) for h in range(4)])
     w = np.concatenate([want[(b, h)] for b in range(8) for h in range(4)])
-    r, m = assert_close(g, w, "bf16", "L8192 sampled")
-    print(f"  rel_l2={r:.3e} max_abs={m:.3e}")
-    # determinism: a second call is bitwise identical
+    r, m = assert_close(g, w, "bf16", "L8192 every query block")
+    print(f"  {sum(len(v) for v in rows.values()) * 4} rows: rel_l2={r:.3e} max_abs={m:.3e}")
     out2 = gpu_attn(case)
     assert torch.equal(out, out2)
+
+
+def test_L8192_one_full_sequence_head():
+    """All 8192 rows of one (sequence, head) of the L=8192 workload against the oracle."""
+    print("\n[case] attn_L8192 full (sequence 5, head 2)", flush=True)
+    case, _, got = _l8192_gpu()
+    b, h = 5, 2
+    j = case.jagged
+    jag = dict(seq_offsets=j.seq_offsets.astype(np.int64), timestamps=j.timestamps, mask=j.mask,
+               num_candidates=None, attn_scale=None)
+    sl = slice(h, h + 1)
+    want = O.attn_fwd(jag, case.q.values[:, sl], case.k.values[:, sl], case.v.values[:, sl], case.rab.pos_bias,
+                      case.rab.time_bias, row_sample={b: np.arange(8192)})[(b, 0)]
+    o0 = int(j.seq_offsets[b])
+    r, m = assert_close(got[o0:o0 + 8192, h], want, "bf16", "L8192 full sequence head")
+    print(f"  rel_l2={r:.3e} max_abs={m:.3e}")
 
 
 def test_empty_batch_and_empty_sequences():

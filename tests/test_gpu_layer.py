@@ -6,7 +6,8 @@ from hstu_sequential_transduction_attn_amd import configs as C
 from hstu_sequential_transduction_attn_amd import inputs as I
 from oracle import hstu_oracle as O
 
-from _util import assert_close, gpu_layer_stack, gather_input, host, dev, oracle_jag, oracle_layers, sub_jagged
+from _util import (assert_close, gpu_layer_stack, gather_input, host, dev, oracle_jag, oracle_layers,
+                   oracle_stack_sequence, sub_jagged, workload_case, workload_sequences)
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -91,28 +92,28 @@ def test_gather_rows_exact():
     assert np.array_equal(host(out), O.gather_rows(table.values, ids))
 
 
-def test_stack8_full_size_sampled_sequences():
-    """The 8-layer stack workload at full size on the GPU; the two shortest sequences vs the oracle."""
-    print("\n[case] stack8_bf16 (config 4), full batch, sampled sequences", flush=True)
-    case = C.stack8_bf16()
-    y = gpu_layer_stack(case, use_gather=True, residual_f32=True, act_split=True)
-    # the gathered input equals the case's x exactly
-    lengths = case.jagged.lengths
-    seqs = list(np.argsort(lengths, kind="stable")[:2])
-    _, idx = sub_jagged(case.jagged, seqs)
-    got = host(y)[idx]
-    r, m = assert_close(got, _oracle_stack(case, seqs), "bf16", "stack8 sampled")
-    print(f"  seqs={seqs} lengths={[int(lengths[s]) for s in seqs]} rel_l2={r:.3e} max_abs={m:.3e}")
+def _check_sequences(name, case, y, what):
+    offs = case.jagged.seq_offsets
+    for seq in workload_sequences(case):
+        print(f"  {what}: sequence {seq} (n = {int(case.jagged.lengths[seq])})", flush=True)
+        got = y[int(offs[seq]):int(offs[seq + 1])]
+        r, m = assert_close(got, oracle_stack_sequence(name, case, seq), "bf16", f"{what} sequence {seq}")
+        print(f"    rel_l2={r:.3e} max_abs={m:.3e}", flush=True)
 
 
-def test_mfalcon_full_size_sampled_user():
-    """The candidate-masked 3-layer workload at full size; the shortest user vs the oracle."""
-    print("\n[case] mfalcon_bf16 (config 5), full batch, sampled user", flush=True)
-    case = C.mfalcon_bf16()
-    y = gpu_layer_stack(case, use_gather=True, residual_f32=True)
-    lengths = case.jagged.lengths
-    seqs = [int(np.argmin(lengths))]
-    _, idx = sub_jagged(case.jagged, seqs)
-    got = host(y)[idx]
-    r, m = assert_close(got, _oracle_stack(case, seqs), "bf16", "mfalcon sampled")
-    print(f"  user={seqs} n={int(lengths[seqs[0]])} rel_l2={r:.3e} max_abs={m:.3e}")
+def test_stack8_full_size_shortest_and_longest_sequences():
+    """The 8-layer stack workload at full size (T = 145,051), one hstu_layer_fwd call per layer after the
+    gather; the two shortest sequences and the longest (4016 tokens through 8 layers) vs the oracle."""
+    print("\n[case] stack8_bf16 (config 4), full batch, layer by layer", flush=True)
+    case = workload_case("stack8_bf16")
+    y = host(gpu_layer_stack(case, use_gather=True, residual_f32=True, act_split=True))
+    _check_sequences("stack8_bf16", case, y, "stack8 layer path")
+
+
+def test_mfalcon_full_size_shortest_and_longest_users():
+    """The candidate-masked 3-layer workload at full size; the two shortest users and the longest (its
+    history and 1024 candidates) vs the oracle."""
+    print("\n[case] mfalcon_bf16 (config 5), full batch, layer by layer", flush=True)
+    case = workload_case("mfalcon_bf16")
+    y = host(gpu_layer_stack(case, use_gather=True, residual_f32=True))
+    _check_sequences("mfalcon_bf16", case, y, "mfalcon layer path")

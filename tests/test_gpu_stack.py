@@ -4,7 +4,7 @@ The oracle is the composition of its own pinned pieces: gather_rows, then stack_
 LayerNorm between layers).  Cases: a small stack that takes the unfused path (gather, then one layer
 call at a time), ragged batches large enough for the fused path (gather inside layer 0's GEMMs,
 LayerNorm applied inside the next layer's GEMMs), identity rows (no ids), split activations, the
-candidate mask, and the 8-layer and candidate workloads at full size on sampled sequences.
+candidate mask, and the 8-layer and candidate workloads at full size (shortest and longest sequences).
 """
 import numpy as np
 import pytest
@@ -13,7 +13,8 @@ from hstu_sequential_transduction_attn_amd import configs as C
 from hstu_sequential_transduction_attn_amd import inputs as I
 from oracle import hstu_oracle as O
 
-from _util import assert_close, dev, host, jag_dev, oracle_jag, oracle_layers, sub_jagged
+from _util import (assert_close, dev, host, jag_dev, oracle_jag, oracle_layers, oracle_stack_sequence,
+                   sub_jagged, workload_case, workload_sequences)
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -124,30 +125,33 @@ def _workload_table(case):
     return case.table_values, pos.astype(np.int64)
 
 
-def test_stack8_fused_full_size_sampled_sequences():
+def _check_sequences(name, case, y, what):
+    offs = case.jagged.seq_offsets
+    for seq in workload_sequences(case):
+        print(f"  {what}: sequence {seq} (n = {int(case.jagged.lengths[seq])})", flush=True)
+        got = y[int(offs[seq]):int(offs[seq + 1])]
+        r, m = assert_close(got, oracle_stack_sequence(name, case, seq), "bf16", f"{what} sequence {seq}")
+        print(f"    rel_l2={r:.3e} max_abs={m:.3e}", flush=True)
+
+
+def test_stack8_fused_full_size_shortest_and_longest_sequences():
     """The 8-layer stack workload (T = 145,051, D = 1024, H = 8 x 128) through hstu_stack_fwd with split
-    activations and an fp32 output; the two shortest sequences against the oracle."""
-    print("\n[case] stack8_bf16 fused, full batch, sampled sequences", flush=True)
-    case = C.stack8_bf16()
+    activations and an fp32 output; the two shortest sequences and the longest vs the oracle."""
+    print("\n[case] stack8_bf16 fused, full batch", flush=True)
+    case = workload_case("stack8_bf16")
     table, ids = _workload_table(case)
     y = _gpu(case, table, ids, act_split=True, y_dtype=torch.float32)
-    lengths = case.jagged.lengths
-    seqs = list(np.argsort(lengths, kind="stable")[:2])
-    _, idx = sub_jagged(case.jagged, seqs)
-    r, m = assert_close(y[idx], _oracle(case, table, ids, seqs), "bf16", "stack8 fused sampled")
-    print(f"  seqs={seqs} lengths={[int(lengths[s]) for s in seqs]} rel_l2={r:.3e} max_abs={m:.3e}")
+    _check_sequences("stack8_bf16", case, y, "stack8 fused")
 
 
-def test_mfalcon_fused_full_size_sampled_user():
-    print("\n[case] mfalcon_bf16 fused, full batch, sampled user", flush=True)
-    case = C.mfalcon_bf16()
+def test_mfalcon_fused_full_size_shortest_and_longest_users():
+    """The candidate-masked 3-layer workload through hstu_stack_fwd; the two shortest users and the
+    longest vs the oracle."""
+    print("\n[case] mfalcon_bf16 fused, full batch", flush=True)
+    case = workload_case("mfalcon_bf16")
     table, ids = _workload_table(case)
     y = _gpu(case, table, ids, y_dtype=torch.float32)
-    lengths = case.jagged.lengths
-    seqs = [int(np.argmin(lengths))]
-    _, idx = sub_jagged(case.jagged, seqs)
-    r, m = assert_close(y[idx], _oracle(case, table, ids, seqs), "bf16", "mfalcon fused sampled")
-    print(f"  user={seqs} n={int(lengths[seqs[0]])} rel_l2={r:.3e} max_abs={m:.3e}")
+    _check_sequences("mfalcon_bf16", case, y, "mfalcon fused")
 
 
 def test_stack_fused_partial_statistics_tile():
