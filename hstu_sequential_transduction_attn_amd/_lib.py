@@ -83,6 +83,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_attn_fwd.restype = ctypes.c_int
     lib.hstu_attn_fwd.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT), ctypes.c_int, c_vp, c_vp, c_vp,
                                   c_vp, ctypes.c_int, c_vp, c_sz, c_vp]
+    lib.hstu_attn_fwd_noalloc.restype = ctypes.c_int
+    lib.hstu_attn_fwd_noalloc.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT), ctypes.c_int, c_vp, c_vp,
+                                          c_vp, c_vp, ctypes.c_int, c_vp]
     lib.hstu_attn_cached_workspace_bytes.restype = c_sz
     lib.hstu_attn_cached_workspace_bytes.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(JaggedT),
                                                      ctypes.POINTER(AttnDescT)]
@@ -186,6 +189,22 @@ def attn_fwd(seq_offsets, timestamps, q, k, v, pos_bias, time_bias, *, max_seq_l
     _check(lib.hstu_attn_fwd(ctypes.byref(jag), ctypes.byref(desc), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                              _dtype_code(out), _ptr(workspace), workspace.numel() if workspace is not None else 0,
                              _stream(stream)))
+    return out
+
+
+def attn_fwd_noalloc(seq_offsets, timestamps, q, k, v, pos_bias, time_bias, *, max_seq_len: int,
+                     mask: int = MASK_CAUSAL, num_candidates=None, attn_scale=None, out=None, out_dtype=None,
+                     stream=None):
+    """hstu_attn_fwd_noalloc(...): as attn_fwd, with the library's fixed device scratch instead of a
+    workspace; pass `out` to make the call allocate nothing on the Python side either."""
+    lib = load_library()
+    T, H, Dh = q.shape
+    if out is None:
+        out = torch.empty((T, H, Dh), dtype=out_dtype or q.dtype, device=q.device)
+    jag = make_jagged(seq_offsets, timestamps, max_seq_len, num_candidates, attn_scale)
+    desc = make_desc(H, Dh, pos_bias, time_bias, mask)
+    _check(lib.hstu_attn_fwd_noalloc(ctypes.byref(jag), ctypes.byref(desc), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(out), _dtype_code(out), _stream(stream)))
     return out
 
 

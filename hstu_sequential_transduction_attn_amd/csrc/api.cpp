@@ -12,6 +12,8 @@
 
 #include "kernels.h"
 
+static_assert(hstu::kNoallocScratchBytes == HSTU_NOALLOC_SCRATCH_BYTES, "scratch size of the header");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -125,6 +127,43 @@ LayerWs layer_ws(int64_t T, int64_t B, int64_t H, int64_t HD, int64_t D, hstu_dt
   return w;
 }
 
+// Everything hstu_attn_fwd and hstu_attn_fwd_noalloc check before a launch, except the scratch.
+hstu_status_t check_attn_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, hstu_dtype_t in_dtype,
+                             const void *q, const void *k, const void *v, const void *out, hstu_dtype_t out_dtype) {
+  hstu_status_t st = check_jagged_desc(jag, desc);
+  if (st != HSTU_OK) return st;
+  if (!valid_dtype(in_dtype)) return fail(HSTU_ERR_INVALID_ARGUMENT, "in_dtype = %d invalid", (int)in_dtype);
+  if (!valid_dtype(out_dtype)) return fail(HSTU_ERR_INVALID_ARGUMENT, "out_dtype = %d invalid", (int)out_dtype);
+  if (in_dtype == HSTU_F32 && out_dtype != HSTU_F32) return fail(HSTU_ERR_UNSUPPORTED, "f32 inputs need an f32 output");
+  const int64_t T = jag->total_tokens;
+  if (T == 0) return HSTU_OK;
+  if (!q || !k || !v || !out) return fail(HSTU_ERR_INVALID_ARGUMENT, "q/k/v/out is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(HSTU_ERR_INVALID_ARGUMENT, "q/k/v/out must be 16-byte aligned");
+  const size_t nin = (size_t)T * desc->num_heads * desc->head_dim * esize(in_dtype);
+  const size_t nout = (size_t)T * desc->num_heads * desc->head_dim * esize(out_dtype);
+  if (overlaps(out, nout, q, nin) || overlaps(out, nout, k, nin) || overlaps(out, nout, v, nin))
+    return fail(HSTU_ERR_INVALID_ARGUMENT, "out overlaps q, k or v");
+  return HSTU_OK;
+}
+
+// The forward's launch once every argument has been checked; `workspace` holds the timestamp ranges.
+hstu_status_t launch_attn_fwd_checked(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, hstu_dtype_t in_dtype,
+                                      const void *q, const void *k, const void *v, void *out, hstu_dtype_t out_dtype,
+                                      void *workspace, void *stream) {
+  hstu::AttnArgs a = attn_args(jag, desc);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.row_stride = (int64_t)desc->num_heads * desc->head_dim;
+  a.out_row_stride = a.row_stride;
+  a.in_dtype = in_dtype == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
+  a.out_dtype = out_dtype == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
+  a.tau_stats = (int64_t *)workspace;
+  return from_hip(hstu::launch_attn_fwd(a, (hipStream_t)stream), "attn_fwd launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -155,12 +194,8 @@ hstu_status_t hstu_attn_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *de
                             const void *q, const void *k, const void *v, void *out, hstu_dtype_t out_dtype,
                             void *workspace, size_t workspace_bytes, void *stream) {
   try {
-    hstu_status_t st = check_jagged_desc(jag, desc);
+    hstu_status_t st = check_attn_fwd(jag, desc, in_dtype, q, k, v, out, out_dtype);
     if (st != HSTU_OK) return st;
-    if (!valid_dtype(in_dtype)) return fail(HSTU_ERR_INVALID_ARGUMENT, "in_dtype = %d invalid", (int)in_dtype);
-    if (!valid_dtype(out_dtype)) return fail(HSTU_ERR_INVALID_ARGUMENT, "out_dtype = %d invalid", (int)out_dtype);
-    if (in_dtype == HSTU_F32 && out_dtype != HSTU_F32)
-      return fail(HSTU_ERR_UNSUPPORTED, "f32 inputs need an f32 output");
     const size_t need = hstu_attn_workspace_bytes(jag, desc, in_dtype);
     if (workspace_bytes < need)
       return fail(HSTU_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
@@ -168,29 +203,36 @@ hstu_status_t hstu_attn_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *de
     if (T == 0) return ok();
     if (!workspace) return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace is NULL");
     if (!aligned16(workspace)) return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-    if (!q || !k || !v || !out) return fail(HSTU_ERR_INVALID_ARGUMENT, "q/k/v/out is NULL");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-      return fail(HSTU_ERR_INVALID_ARGUMENT, "q/k/v/out must be 16-byte aligned");
     const size_t nin = (size_t)T * desc->num_heads * desc->head_dim * esize(in_dtype);
     const size_t nout = (size_t)T * desc->num_heads * desc->head_dim * esize(out_dtype);
-    if (overlaps(out, nout, q, nin) || overlaps(out, nout, k, nin) || overlaps(out, nout, v, nin))
-      return fail(HSTU_ERR_INVALID_ARGUMENT, "out overlaps q, k or v");
     if (overlaps(workspace, need, out, nout) || overlaps(workspace, need, q, nin) ||
         overlaps(workspace, need, k, nin) || overlaps(workspace, need, v, nin))
       return fail(HSTU_ERR_INVALID_ARGUMENT, "workspace overlaps q, k, v or out");
-    hstu::AttnArgs a = attn_args(jag, desc);
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.out = out;
-    a.row_stride = (int64_t)desc->num_heads * desc->head_dim;
-    a.out_row_stride = a.row_stride;
-    a.in_dtype = in_dtype == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
-    a.out_dtype = out_dtype == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
-    a.tau_stats = (int64_t *)workspace;
-    return from_hip(hstu::launch_attn_fwd(a, (hipStream_t)stream), "attn_fwd launch");
+    return launch_attn_fwd_checked(jag, desc, in_dtype, q, k, v, out, out_dtype, workspace, stream);
   } catch (...) {
     return fail(HSTU_ERR_DEVICE, "unexpected C++ exception in hstu_attn_fwd");
+  }
+}
+
+hstu_status_t hstu_attn_fwd_noalloc(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, hstu_dtype_t in_dtype,
+                                    const void *q, const void *k, const void *v, void *out, hstu_dtype_t out_dtype,
+                                    void *stream) {
+  try {
+    hstu_status_t st = check_attn_fwd(jag, desc, in_dtype, q, k, v, out, out_dtype);
+    if (st != HSTU_OK) return st;
+    const size_t need = hstu_attn_workspace_bytes(jag, desc, in_dtype);
+    if (need > hstu::kNoallocScratchBytes)
+      return fail(HSTU_ERR_WORKSPACE_TOO_SMALL,
+                  "this batch needs %zu bytes of scratch (total_tokens / 32 + num_seqs + 1 timestamp ranges of 16 "
+                  "bytes); the fixed device scratch of hstu_attn_fwd_noalloc holds %zu",
+                  need, (size_t)hstu::kNoallocScratchBytes);
+    if (jag->total_tokens == 0) return ok();
+    void *scratch = nullptr;
+    const hipError_t e = hstu::noalloc_scratch(&scratch);
+    if (e != hipSuccess) return from_hip(e, "device address of the fixed scratch");
+    return launch_attn_fwd_checked(jag, desc, in_dtype, q, k, v, out, out_dtype, scratch, stream);
+  } catch (...) {
+    return fail(HSTU_ERR_DEVICE, "unexpected C++ exception in hstu_attn_fwd_noalloc");
   }
 }
 

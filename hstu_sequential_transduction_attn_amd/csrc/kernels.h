@@ -62,6 +62,10 @@ int attn_cached_splits(int64_t num_seqs, int64_t num_heads, int64_t max_candidat
 
 // Workspace bytes of the per-32-token timestamp ranges the attention kernel classifies tiles with.
 size_t attn_tau_stats_bytes(int64_t total_tokens, int64_t num_seqs);
+// Allocation-free forward: bytes of the file-scope device scratch array (noalloc.hip), and its device
+// address on the current device (looked up once per device, then cached).
+constexpr size_t kNoallocScratchBytes = (size_t)1 << 20;
+hipError_t noalloc_scratch(void **ptr);
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream);
 // Candidates against a cached history: each candidate sees every history key of its user and itself.
 hipError_t launch_attn_cached(const AttnArgs &a, hipStream_t stream);

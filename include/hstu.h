@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 6
+#define HSTU_ABI_VERSION 7
 
 typedef enum {
   HSTU_OK = 0,
@@ -137,6 +137,28 @@ size_t hstu_attn_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc_
 hstu_status_t hstu_attn_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, hstu_dtype_t in_dtype,
                             const void *q, const void *k, const void *v, void *out, hstu_dtype_t out_dtype,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Scratch held by the allocation-free forward on each GPU (bytes): it serves every batch with
+ * total_tokens / 32 + num_seqs + 1 <= 65536. */
+#define HSTU_NOALLOC_SCRATCH_BYTES ((size_t)1 << 20)
+
+/*
+ * hstu_attn_fwd for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same kernels and bitwise the same result as
+ * hstu_attn_fwd; the scratch (the per-32-token timestamp ranges) comes from a fixed device array of
+ * HSTU_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until the process ends,
+ * instead of from a caller workspace.  The caller passes only inputs and outputs, exactly as for
+ * hstu_attn_fwd.  Nothing is allocated or freed (no hipMalloc, hipFree or allocating library call);
+ * the first call on a device looks the array's device address up, with that device current, and keeps
+ * it.  The scratch needs no clearing: each call writes every entry it later reads.  All calls on one GPU
+ * share that GPU's array, which keeps the last call's contents, so calls that can overlap in time on
+ * one GPU (several streams or host threads) race and must be serialised by the caller.
+ * Errors: as hstu_attn_fwd; a batch with total_tokens / 32 + num_seqs + 1 > 65536 needs more scratch
+ * than the array holds and is HSTU_ERR_WORKSPACE_TOO_SMALL, returned before anything is launched.
+ */
+hstu_status_t hstu_attn_fwd_noalloc(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, hstu_dtype_t in_dtype,
+                                    const void *q, const void *k, const void *v, void *out, hstu_dtype_t out_dtype,
+                                    void *stream);
 
 /*
  * Workspace needed by hstu_attn_fwd_cached (bytes; 0 is possible): the per-32-token timestamp ranges

@@ -39,7 +39,7 @@ def _attn(jag, desc, in_dt=L.HSTU_BF16, out_dt=L.HSTU_BF16, q=P16 + 0x10000, k=P
 
 def test_exports_every_declared_symbol():
     names = L.exported_functions_in_header()
-    assert len(names) == 19
+    assert len(names) == 20
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib()
-    assert lib.hstu_abi_version() == 6
+    assert lib.hstu_abi_version() == 7
     assert lib.hstu_status_string(OK) == b"HSTU_OK"
     assert lib.hstu_status_string(WS_SMALL) == b"HSTU_ERR_WORKSPACE_TOO_SMALL"
     assert lib.hstu_status_string(99) == b"HSTU_STATUS_UNKNOWN"
@@ -85,6 +85,39 @@ def test_attn_zero_tokens_is_a_no_op():
     assert _lib().hstu_attn_workspace_bytes(ctypes.byref(jag), ctypes.byref(_desc()), L.HSTU_BF16) == 0
     st, msg = _attn(jag, _desc(), q=None, k=None, v=None, out=None, ws=None, nws=0)
     assert st == OK and msg == ""
+
+
+def _noalloc(jag, desc, in_dt=L.HSTU_BF16, out_dt=L.HSTU_BF16, q=P16 + 0x10000, k=P16 + 0x20000000,
+             v=P16 + 0x40000000, out=P16 + 0x60000000):
+    lib = _lib()
+    st = lib.hstu_attn_fwd_noalloc(ctypes.byref(jag) if jag else None, ctypes.byref(desc) if desc else None, in_dt,
+                                   q, k, v, out, out_dt, None)
+    return st, lib.hstu_last_error().decode()
+
+
+def test_noalloc_checks_before_touching_the_device():
+    # the argument checks of hstu_attn_fwd, without a workspace
+    assert _noalloc(None, _desc())[0] == INVALID
+    st, msg = _noalloc(_jag(), _desc(Dh=48))
+    assert st == UNSUPPORTED and "head_dim" in msg
+    assert _noalloc(_jag(), _desc(), in_dt=L.HSTU_F32, out_dt=L.HSTU_BF16)[0] == UNSUPPORTED
+    assert _noalloc(_jag(), _desc(), q=None)[0] == INVALID
+    st, msg = _noalloc(_jag(), _desc(), out=P16 + 0x10000 + 64)
+    assert st == INVALID and "overlaps" in msg
+    # zero tokens: nothing to do, nothing looked up
+    jag = L.JaggedT(3, 0, 0, P16, None, None, None)
+    assert _noalloc(jag, _desc(), q=None, k=None, v=None, out=None) == (OK, "")
+    # the fixed scratch holds T/32 + B + 1 <= 65536 timestamp ranges: the largest batch that fits ...
+    B = 5
+    T_fit = (65536 - B - 1) * 32 + 31
+    big_q = 1 << 44
+    fit = L.JaggedT(B, T_fit, 1 << 20, P16, P16 + 0x1000, None, None)
+    need = _lib().hstu_attn_workspace_bytes(ctypes.byref(fit), ctypes.byref(_desc()), L.HSTU_BF16)
+    assert need == 1 << 20
+    # ... and one token more is refused before any launch, naming both sizes
+    over = L.JaggedT(B, T_fit + 1, 1 << 20, P16, P16 + 0x1000, None, None)
+    st, msg = _noalloc(over, _desc(), q=P16 + big_q, k=P16 + 2 * big_q, v=P16 + 3 * big_q, out=P16 + 4 * big_q)
+    assert st == WS_SMALL and str(1 << 20) in msg and str(need + 256) in msg
 
 
 def test_attn_workspace_checks():
