@@ -1,12 +1,15 @@
 """Benchmark of the HSTU attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--extended]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--no-cpu-baseline] [--extended]
     python bench.py --only {layers,cached,attn_bwd,layer_bwd,layer_bwd_call}
 
 A step is one hstu_attn_fwd call (QK^T, bias, SiLU, mask and AV of every allowed pair) over the
 L = 8192 workload: 8 sequences of 8192 events, 4 heads x 128, P = Tb = 256 bias buckets, causal,
 bf16 with fp32 accumulation; inputs are resident in HBM before the timed region.  The FLOP count
 covers allowed (causal, non-padded) pairs only: sum_b H * n_b (n_b + 1) / 2 * 4 * Dh.
+
+Before the W warm-up steps, untimed calls run for --settle-ms (300 ms by default) so that the chip has
+reached its sustained clock when the K timed steps start; `clock_settle` in the output says how many.
 
 Prints one JSON line.  `roofline` compares the kernel's average duration (HIP events on the stream
 it runs on) with the MI355X dense bf16 MFMA peak; `cpu_baseline` times the float64 oracle on a
@@ -56,39 +59,69 @@ def measured_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case, budget_s: float = 15.0):
-    """Time the float64 oracle on whole 1024-row query blocks of the workload until ~budget_s: every
-    (sequence, head) in turn, the last (longest) query blocks of each first."""
+def _oracle_unit(task):
+    """One worker of the CPU baseline: the float64 oracle on 128-row query blocks of one (sequence, head),
+    in the given order, until its time budget is spent.  Returns (FLOP, blocks done, seconds)."""
+    q, k, v, tau, wp, wt, blocks, budget_s = task
     from oracle import hstu_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas_threads = 1
-    j = case.jagged
-    jag = dict(seq_offsets=j.seq_offsets.astype(np.int64), timestamps=j.timestamps, mask=j.mask,
-               num_candidates=j.num_candidates, attn_scale=j.attn_scale)
-    q, k, v = case.q.values, case.k.values, case.v.values
-    flops, done, t0 = 0, [], time.perf_counter()
-    n = np.diff(j.seq_offsets)
-    blocks = [(b, h, r0) for b in range(j.num_seqs) for h in range(case.num_heads)
-              for r0 in range(((int(n[b]) - 1) // 1024) * 1024, -1, -1024)]
-    for b, h, r0 in blocks:
-        r1 = min(r0 + 1024, int(n[b]))
-        rows = {b: np.arange(r0, r1)}
-        O.attn_fwd(jag, q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], case.rab.pos_bias, case.rab.time_bias,
-                   row_sample=rows)
-        flops += int(sum(i + 1 for i in range(r0, r1))) * 4 * case.head_dim
-        done.append((b, h, r0, r1))
+    n, dh = q.shape
+    jag = dict(seq_offsets=np.array([0, n], np.int64), timestamps=tau, mask=0, num_candidates=None, attn_scale=None)
+    flop, done, t0 = 0, 0, time.perf_counter()
+    for r0 in blocks:
+        rows = np.arange(r0, min(r0 + 128, n))
+        O.attn_fwd(jag, q[:, None], k[:, None], v[:, None], wp, wt, row_sample={0: rows})
+        flop += int((rows + 1).sum()) * 4 * dh
+        done += 1
         if time.perf_counter() - t0 > budget_s:
             break
-    dt = time.perf_counter() - t0
-    pairs = sorted({(b, h) for b, h, _, _ in done})
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"float64 oracle, {len(done)} query blocks of up to 1024 rows (longest first) from "
-                      f"(sequence, head) pairs {pairs[0]}..{pairs[-1]}, each against all its causal keys "
-                      f"({flops:.3e} FLOP in {dt:.1f} s; BLAS matmuls on {blas_threads} threads, bucket and "
-                      f"SiLU work single-threaded)"}
+    return flop, done, time.perf_counter() - t0
+
+
+def cpu_baseline(case, budget_s: float = 15.0):
+    """Time the float64 oracle on the host: one single-threaded process per core (up to 16) over the
+    (sequence, head) units of the workload, each unit's 128-row query blocks in an order spread over the
+    sequence (bit-reversed block index), every block against all its causal keys; each unit stops after
+    its share of about budget_s, so a host too slow for the whole workload times a spread sample of it."""
+    import multiprocessing as mp
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    j = case.jagged
+    offs = j.seq_offsets.astype(np.int64)
+    units = [(b, h) for b in range(j.num_seqs) for h in range(case.num_heads)]
+    per_unit_s = budget_s / -(-len(units) // cores)
+    tasks = []
+    for b, h in units:
+        o0, o1 = int(offs[b]), int(offs[b + 1])
+        nblk = (o1 - o0 + 127) // 128
+        bits = max(1, (nblk - 1).bit_length())
+        order = sorted(range(nblk), key=lambda x: int(format(x, f"0{bits}b")[::-1], 2))
+        sl = slice(o0, o1)
+        tasks.append((case.q.values[sl, h], case.k.values[sl, h], case.v.values[sl, h], j.timestamps[sl],
+                      case.rab.pos_bias, case.rab.time_bias, [128 * x for x in order], per_unit_s))
+    env = {k_: os.environ.get(k_) for k_ in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k_ in env:
+        os.environ[k_] = "1"    # each worker is one core
+    try:
+        t0 = time.perf_counter()
+        with mp.get_context("spawn").Pool(cores) as pool:
+            t1 = time.perf_counter()
+            res = pool.map(_oracle_unit, tasks, chunksize=1)
+            wall = time.perf_counter() - t1
+        total = time.perf_counter() - t0
+    finally:
+        for k_, v_ in env.items():
+            if v_ is None:
+                os.environ.pop(k_, None)
+            else:
+                os.environ[k_] = v_
+    flop = sum(r[0] for r in res)
+    blocks = sum(r[1] for r in res)
+    nblk = sum((int(offs[b + 1] - offs[b]) + 127) // 128 for b, _ in units)
+    return {"value": flop / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 oracle in {cores} single-threaded processes (one per host core, "
+                      f"{len(os.sched_getaffinity(0))} available) over the {len(units)} (sequence, head) units: "
+                      f"{blocks} of the workload's {nblk} query blocks of 128 rows, spread over each sequence, "
+                      f"each against all its causal keys ({flop:.3e} FLOP in {wall:.1f} s; {total:.1f} s with "
+                      f"process start-up)"}
 
 
 def run(args):
@@ -113,9 +146,23 @@ def run(args):
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
-    def step():
-        ops.attn_fwd(offs, tau, q, k, v, wp, wt, max_seq_len=j.max_seq_len, out=out, stream=stream)
+    ws = torch.empty(max(ops.attn_workspace_bytes(offs, tau, q, wp, wt, max_seq_len=j.max_seq_len), 1),
+                     dtype=torch.uint8, device=dev)
 
+    def step():
+        ops.attn_fwd(offs, tau, q, k, v, wp, wt, max_seq_len=j.max_seq_len, out=out, workspace=ws, stream=stream)
+
+    # The chip's power management needs on the order of 100 ms of sustained load to reach its sustained
+    # clock; a timed region of a few milliseconds right after a few calls from idle measures that ramp
+    # (about 12% slower), not the kernel.  So untimed calls run for settle_ms first, then the W warm-up
+    # steps, then exactly K timed steps.
+    settle_calls, t_settle = 0, time.perf_counter()
+    while args.settle_ms > 0 and (time.perf_counter() - t_settle) * 1e3 < args.settle_ms and settle_calls < 5000:
+        for _ in range(25):
+            step()
+        torch.cuda.synchronize()
+        settle_calls += 25
+    settle_ms = (time.perf_counter() - t_settle) * 1e3 if settle_calls else 0.0
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -152,6 +199,8 @@ def run(args):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(), "kernel_ms": round(kernel_ms, 4)},
+        "clock_settle": {"calls": settle_calls, "ms": round(settle_ms, 1),
+                         "note": "untimed calls before the warm-up steps, so the timed steps run at the sustained clock"},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(case)
@@ -451,10 +500,10 @@ def cached_scoring(dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # 100 untimed calls (about 70 ms of sustained load) bring the chip to its steady clock; after 5 the
-    # timed calls still run about 12% slower
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed calls for about this long before the warm-up steps (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extended", action="store_true")
     ap.add_argument("--only", choices=["layers", "cached", "attn_bwd", "layer_bwd", "layer_bwd_call"],

@@ -172,6 +172,16 @@ def make_desc(num_heads: int, head_dim: int, pos_bias: torch.Tensor, time_bias: 
     return AttnDescT(num_heads, head_dim, P, Tb, R, _ptr(pos_bias), _ptr(time_bias), int(mask))
 
 
+def attn_workspace_bytes(seq_offsets, timestamps, q, pos_bias, time_bias, *, max_seq_len: int,
+                         mask: int = MASK_CAUSAL) -> int:
+    """hstu_attn_workspace_bytes for attn_fwd's arguments (q [T, H, Dh] sets H, Dh and the dtype)."""
+    lib = load_library()
+    T, H, Dh = q.shape
+    jag = make_jagged(seq_offsets, timestamps, max_seq_len)
+    desc = make_desc(H, Dh, pos_bias, time_bias, mask)
+    return int(lib.hstu_attn_workspace_bytes(ctypes.byref(jag), ctypes.byref(desc), _dtype_code(q)))
+
+
 def attn_fwd(seq_offsets, timestamps, q, k, v, pos_bias, time_bias, *, max_seq_len: int, mask: int = MASK_CAUSAL,
              num_candidates=None, attn_scale=None, out_dtype: Optional[torch.dtype] = None, out=None, workspace=None,
              stream=None):

@@ -22,7 +22,7 @@ constexpr float kNegLn2 = -0.6931471805599453f;
 static_assert(kWaves * 16 == kBN, "each wave stages 16 rows of a tile");
 
 // Tile classes.  A class code is body | (low time bucket << 8).
-enum Body : int { kNone = 0, kUniform = 1, kTwo = 2, kGen32 = 3, kGen64 = 4, kGen32M = 5, kGen64M = 6 };
+enum Body : int { kNone = 0, kUniform = 1, kTwo = 2, kGen32 = 3, kGen64 = 4, kGen32M = 5, kGen64M = 6, kTwoOrd = 7 };
 
 // Row order of K inside each 32-row block of LDS: row r holds key kperm(r) (an involution swapping
 // rows 4..7 with 8..11 and 20..23 with 24..27, i.e. bits 2 and 3 of r).  With it, accumulator element e
@@ -108,6 +108,7 @@ struct TileCtx {
   int P, Tb;
   int64_t my_tau;
   uint32_t qoff;       // (uint32)(my_tau - base) for the 32-bit modes
+  uint32_t qlo;        // low word of my_tau (two-bucket tiles whose keys are no later than their queries)
   uint32_t base_lo;    // low word of the tile's timestamp base
   uint32_t thr;        // two-bucket mode: |dt| >= thr selects bias_hi
   int blo;             // two-bucket mode: the lower time bucket (the upper one is blo + 1)
@@ -117,7 +118,7 @@ struct TileCtx {
   const HSTU_LDS char *stage;      // the tile's LDS stage
 };
 
-// Score of a pair outside the mask: SiLU of it is exactly 0 in silu_block (u = 1.4e30 is finite, 2^u
+// Score of a pair outside the mask: its folded SiLU u / (1 + 2^u) is exactly 0 (u = 1.4e30 is finite, 2^u
 // overflows to +inf, the reciprocal of 1 + inf is 0 and u * 0 = 0), and adding a finite q.k keeps it there.
 constexpr float kMaskedScore = -1.0e30f;
 
@@ -172,16 +173,6 @@ __device__ __forceinline__ void adjust_block(floatx16 &s, const TileCtx &c, int 
         s[e] = s[e] + bias;
       }
     }
-  }
-}
-
-// u / (1 + 2^u) for u = -log2(e) * (score + bias) of the 16 scores of one block (the bias is c1 for a
-// uniform tile, already inside the scores otherwise).
-__device__ __forceinline__ void silu_block(const floatx16 &s, float (&a)[16], float c1) {
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const float u = __builtin_fmaf(s[e], kNegLog2e, c1);
-    a[e] = u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u));
   }
 }
 

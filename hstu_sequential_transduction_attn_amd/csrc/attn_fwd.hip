@@ -45,12 +45,16 @@
 //   uniform   - every pair allowed, one position bucket and one time bucket: a single bias constant;
 //   two       - every pair allowed, one position bucket, the time bucket is one of two adjacent
 //               buckets and the timestamps span less than 2^32: |tau_i - tau_j| from 32-bit offsets
-//               (v_sad_u32), one compare and one select per score;
+//               (v_sad_u32), one compare and one select per score; when every key of the tile is no
+//               later than every query of the wave (ordered timestamps) the gap is the plain 32-bit
+//               difference of the low words, one instruction fewer;
 //   general   - per-score mask and bucket lookups in LDS (32-bit offsets when the span allows,
 //               exact 64-bit differences otherwise).
-// All classes share one tile body: the MFMA code and the SiLU are common, and the classes other than
-// uniform add their per-score bias (and the mask) to the score accumulators in place, in a branch of
-// their own, so that the output accumulators never change registers between classes.
+// All classes share one tile body: the MFMA code and the SiLU are common.  The scores of a block are
+// taken out of the MFMA accumulator as 16 separate floats before the classes other than uniform add
+// their per-score bias (and the mask) in a branch of their own: a branch that rewrote elements of the
+// 16-wide accumulator value would make the register allocator copy the whole block at the class merge,
+// on every path.  The output accumulators never change registers between classes.
 #include "attn_common.hpp"
 
 namespace hstu {
@@ -58,9 +62,88 @@ namespace {
 
 using namespace attn;
 
-// One key tile for one wave: both score blocks; for a non-uniform tile the per-score bias and mask
-// patched into them in place (so that every class shares the MFMA code and the accumulators stay in
-// the same registers); then SiLU and AV for each block.
+// |a - b| for uint32 a, b in one v_sad_u32
+__device__ __forceinline__ uint32_t absdiff_u32(uint32_t a, uint32_t b) {
+  uint32_t d;
+  asm("v_sad_u32 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
+// Per-score bias and mask of a non-uniform tile, added to the 16 scores of 32-key block kb (held as
+// separate floats, so that the adjusted values stay in the scores' registers); element e holds key
+// k0 + 32*kb + 16*(e/8) + 8*half + e%8.
+template <typename T, int DH, int MODE>
+__device__ __forceinline__ void adjust_scalar(float (&s)[16], const TileCtx &c, int kb, int half) {
+  using L = Layout<T, DH>;
+  constexpr bool kMasked = MODE == kGen32M || MODE == kGen64M;
+  constexpr bool k64 = MODE == kGen64 || MODE == kGen64M;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int jl0 = 32 * kb + 16 * g + 8 * half;   // tile-local key of element 8*g
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 w = *(const HSTU_LDS u32x4 *)(c.stage + L::tau_at(jl0 + 2 * q));
+      lo[2 * q] = w.x; hi[2 * q] = w.y; lo[2 * q + 1] = w.z; hi[2 * q + 1] = w.w;
+    }
+#pragma unroll
+    for (int e8 = 0; e8 < 8; ++e8) {
+      const int e = 8 * g + e8;
+      float bias;
+      if constexpr (MODE == kTwoOrd) {
+        // every key of the tile is no later than every query and the span is below 2^32: the 32-bit
+        // difference of the low words is the exact gap
+        bias = c.qlo - lo[e8] >= c.thr ? c.bias_hi : c.bias_lo;
+      } else if constexpr (MODE == kTwo) {
+        bias = absdiff_u32(c.qoff, lo[e8] - c.base_lo) >= c.thr ? c.bias_hi : c.bias_lo;
+      } else {
+        const int j = c.k0 + jl0 + e8;
+        const int pj = imin(j, c.pos_lim);
+        const uint32_t dp = absdiff_u32((uint32_t)c.my_pos, (uint32_t)pj);
+        const int bp = (int)(dp < (uint32_t)(c.P - 1) ? dp : (uint32_t)(c.P - 1));
+        int bt;
+        if constexpr (!k64) {
+          bt = bitlen_u32(absdiff_u32(c.qoff, lo[e8] - c.base_lo));
+        } else {
+          const int64_t tj = (int64_t)(((uint64_t)hi[e8] << 32) | lo[e8]);
+          bt = bitlen_absdiff(c.my_tau, tj);
+        }
+        bt = imin(bt, c.Tb - 1);
+        bias = c.wp[bp] + c.wt[bt];
+      }
+      if constexpr (kMasked) {
+        const int j = c.k0 + jl0 + e8;
+        const bool ok = (j <= c.key_lim) | (j == c.my_q);
+        s[e] = ok ? s[e] + bias : kMaskedScore;
+      } else {
+        s[e] = s[e] + bias;
+      }
+    }
+  }
+}
+
+template <typename T, int DH>
+__device__ __forceinline__ void adjust_any(float (&s)[16], const TileCtx &c, int body, int kb, int half) {
+  if (body == kTwoOrd) adjust_scalar<T, DH, kTwoOrd>(s, c, kb, half);
+  else if (body == kTwo) adjust_scalar<T, DH, kTwo>(s, c, kb, half);
+  else if (body == kGen32) adjust_scalar<T, DH, kGen32>(s, c, kb, half);
+  else if (body == kGen32M) adjust_scalar<T, DH, kGen32M>(s, c, kb, half);
+  else if (body == kGen64) adjust_scalar<T, DH, kGen64>(s, c, kb, half);
+  else adjust_scalar<T, DH, kGen64M>(s, c, kb, half);
+}
+
+__device__ __forceinline__ void silu_scalar(const float (&s)[16], float (&a)[16], float c1) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float u = __builtin_fmaf(s[e], kNegLog2e, c1);
+    a[e] = u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u));
+  }
+}
+
+// One key tile for one wave.  Each 32-key block: scores (MFMA), for a non-uniform tile the per-score
+// bias and mask added to the scores as separate floats (so the class branch changes no register
+// assignment), SiLU, then AV.  The second block's score MFMAs are issued before the first block's
+// SiLU, so that they run under it.
 template <typename T, int DH>
 __device__ __forceinline__ void tile_body(OAcc<Layout<T, DH>::kDB> &oacc,
                                           const typename QFrag<T>::type (&qf)[Layout<T, DH>::kQSteps],
@@ -70,25 +153,18 @@ __device__ __forceinline__ void tile_body(OAcc<Layout<T, DH>::kDB> &oacc,
   const HSTU_LDS char *lK = c.stage + L::kOffK;
   const HSTU_LDS char *lV = c.stage + L::kOffV;
   floatx16 s0, s1;
+  float x0[16], x1[16], a0[16], a1[16];
   score_block<T, DH>(s0, lK, 0, l32, half, qf);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) x0[e] = s0[e];
+  if (body != kUniform) adjust_any<T, DH>(x0, c, body, 0, half);
   score_block<T, DH>(s1, lK, 1, l32, half, qf);
-  if (body != kUniform) {
-    if (body == kTwo) {
-      adjust_block<T, DH, kTwo>(s0, c, 0, half); adjust_block<T, DH, kTwo>(s1, c, 1, half);
-    } else if (body == kGen32) {
-      adjust_block<T, DH, kGen32>(s0, c, 0, half); adjust_block<T, DH, kGen32>(s1, c, 1, half);
-    } else if (body == kGen32M) {
-      adjust_block<T, DH, kGen32M>(s0, c, 0, half); adjust_block<T, DH, kGen32M>(s1, c, 1, half);
-    } else if (body == kGen64) {
-      adjust_block<T, DH, kGen64>(s0, c, 0, half); adjust_block<T, DH, kGen64>(s1, c, 1, half);
-    } else {
-      adjust_block<T, DH, kGen64M>(s0, c, 0, half); adjust_block<T, DH, kGen64M>(s1, c, 1, half);
-    }
-  }
-  float a0[16], a1[16];
-  silu_block(s0, a0, c.c1);
+  silu_scalar(x0, a0, c.c1);
   av_block<T, DH>(oacc, a0, lV, 0, lane);
-  silu_block(s1, a1, c.c1);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) x1[e] = s1[e];
+  if (body != kUniform) adjust_any<T, DH>(x1, c, body, 1, half);
+  silu_scalar(x1, a1, c.c1);
   av_block<T, DH>(oacc, a1, lV, 1, lane);
 }
 
@@ -526,7 +602,8 @@ __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_
             code = kUniform | (blo << 8);   // the bucket is read only by the backward
             clo = kNegLog2e * (wpc + wt_lds[blo]);
           } else if (bhi == blo + 1 && span < (1ull << 32)) {
-            code = kTwo | (blo << 8);      // threshold 2^blo: |dt| >= 2^blo has bit length > blo
+            // threshold 2^blo: |dt| >= 2^blo has bit length > blo
+            code = (!BWD && kmax <= wmin ? kTwoOrd : kTwo) | (blo << 8);
             clo = wpc + wt_lds[blo];
             chi = wpc + wt_lds[bhi];
           }
@@ -598,6 +675,7 @@ __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_
       c.blo = (code >> 8) & 255;
       c.base_lo = (uint32_t)readlane_i((int)cls_base, li);
       c.qoff = (uint32_t)(uint64_t)my_tau - c.base_lo;
+      c.qlo = (uint32_t)(uint64_t)my_tau;
       if constexpr (BWD) bwd_tile_body<T, DH>(oacc, qf, gf, c, body, code, ln, gb);
       else tile_body<T, DH>(oacc, qf, c, body, lane);
     }
