@@ -121,3 +121,26 @@ def layer_fwd_loops(x, offsets, timestamps, w_uvqk, b_uvqk, w_out, b_out, pos_bi
             yt = _layer_norm_row(yt, eps)
         y.append(yt)
     return y
+
+
+def softmax_attn_loops(offsets, q, k, v):
+    """Causal softmax attention, one score at a time: O_i = sum_{j<=i} w_ij v_j with
+    w_ij = exp(s_ij - max_j s_ij) / sum_j exp(s_ij - max_j s_ij), s_ij = q_i . k_j / sqrt(Dh)."""
+    T, H, Dh = len(q), len(q[0]), len(q[0][0])
+    out = [[[0.0] * Dh for _ in range(H)] for _ in range(T)]
+    for b in range(len(offsets) - 1):
+        o0, o1 = int(offsets[b]), int(offsets[b + 1])
+        for h in range(H):
+            for i in range(o1 - o0):
+                s = []
+                for j in range(i + 1):
+                    acc = 0.0
+                    for d in range(Dh):
+                        acc += float(q[o0 + i][h][d]) * float(k[o0 + j][h][d])
+                    s.append(acc / math.sqrt(Dh))
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                z = sum(e)
+                for d in range(Dh):
+                    out[o0 + i][h][d] = sum(e[j] / z * float(v[o0 + j][h][d]) for j in range(i + 1))
+    return out

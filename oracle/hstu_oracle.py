@@ -433,3 +433,41 @@ def stack_fwd(x, jag, layers, num_heads, head_dim):
 def gather_rows(table, ids):
     """X0[t] = E[id_t] (embedding lookup, [DLRMv4] Model architecture)."""
     return np.asarray(table)[np.asarray(ids, np.int64)]
+
+
+# --------------------------------------------------------------------------- softmax attention (comparison)
+def softmax_attn_fwd(jag: dict, q, k, v, row_sample=None):
+    """Causal softmax attention over the same jagged batch, the comparison point of [HSTU] abstract
+    (HSTU against FlashAttention2-based Transformers at sequence length 8192; the pages give no more
+    about those models, so this is the textbook scaled dot-product attention):
+        O_i = sum_{j <= i} softmax_j(q_i . k_j / sqrt(Dh)) v_j   per sequence and head, float64,
+    written with the row maximum subtracted before the exponential.  Only the causal mask; no bias.
+    q, k, v: [T, H, Dh]; returns [T, H, Dh], or with row_sample (dict b -> local rows) a dict
+    (b, h) -> [rows, Dh]."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    offs = np.asarray(jag["seq_offsets"], np.int64)
+    T, H, Dh = q.shape
+    scale = 1.0 / np.sqrt(Dh)
+    out = {} if row_sample is not None else np.zeros((T, H, Dh), dtype=np.float64)
+    for b in range(len(offs) - 1):
+        o0, o1 = int(offs[b]), int(offs[b + 1])
+        n = o1 - o0
+        if n == 0 or (row_sample is not None and b not in row_sample):
+            continue
+        rows_all = np.arange(n) if row_sample is None else np.asarray(row_sample[b], np.int64)
+        for h in range(H):
+            res = np.zeros((len(rows_all), Dh), dtype=np.float64)
+            for s in range(0, len(rows_all), _ROW_BLOCK):
+                r = rows_all[s:s + _ROW_BLOCK]
+                scores = (q[o0 + r, h] @ k[o0:o1, h].T) * scale
+                scores = np.where(np.arange(n)[None, :] <= r[:, None], scores, -np.inf)
+                w = np.exp(scores - scores.max(axis=1, keepdims=True))
+                w = w / w.sum(axis=1, keepdims=True)
+                res[s:s + _ROW_BLOCK] = w @ v[o0:o1, h]
+            if row_sample is None:
+                out[o0:o1, h] = res
+            else:
+                out[(b, h)] = res
+    return out
