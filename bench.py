@@ -1,7 +1,7 @@
 """Benchmark of the HSTU attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--no-cpu-baseline] [--extended]
-    python bench.py --only {layers,cached,attn_bwd,layer_bwd,layer_bwd_call}
+    python bench.py --only {layers,cached,attn_bwd,layer_bwd,layer_bwd_call,softmax}
 
 A step is one hstu_attn_fwd call (QK^T, bias, SiLU, mask and AV of every allowed pair) over the
 L = 8192 workload: 8 sequences of 8192 events, 4 heads x 128, P = Tb = 256 bias buckets, causal,
@@ -308,6 +308,7 @@ def extended(args, dev, layers_only=False):
     cached_scoring(dev)
     attn_backward(dev)
     layer_backward(dev)
+    softmax_context(dev)
 
 
 def layer_backward(dev, train_step: bool = True):
@@ -497,6 +498,35 @@ def cached_scoring(dev):
     print(line, file=sys.stderr, flush=True)
 
 
+def softmax_context(dev):
+    """Context for the HSTU abstract's speed claim against FlashAttention2-based Transformers at length
+    8192 (stderr): the self-written causal softmax attention on the attn_L8192 inputs beside
+    hstu_attn_fwd, both timed at the steady clock.  Same causal FLOP count for both (QK^T and AV)."""
+    import torch
+    from hstu_sequential_transduction_attn_amd import configs as C
+    from hstu_sequential_transduction_attn_amd import _lib as ops
+    case = C.attn_L8192()
+    j = case.jagged
+
+    def t(x):
+        return torch.from_numpy(x.bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = t(case.q), t(case.k), t(case.v)
+    offs = torch.from_numpy(j.seq_offsets.astype(np.int32)).to(dev)
+    tau = torch.from_numpy(j.timestamps).to(dev)
+    wp = torch.from_numpy(case.rab.pos_bias).to(dev)
+    wt = torch.from_numpy(case.rab.time_bias).to(dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(max(ops.attn_workspace_bytes(offs, tau, q, wp, wt, max_seq_len=j.max_seq_len), 1),
+                     dtype=torch.uint8, device=dev)
+    flop = case.flops()
+    ms_h = steady_ms(lambda: ops.attn_fwd(offs, tau, q, k, v, wp, wt, max_seq_len=j.max_seq_len, out=out,
+                                          workspace=ws))
+    ms_s = steady_ms(lambda: ops.softmax_attn_fwd(offs, q, k, v, max_seq_len=j.max_seq_len, out=out))
+    print(f"[extended] softmax vs pointwise attention, attn_L8192 shapes: hstu_attn_fwd {ms_h:.3f} ms "
+          f"({flop / ms_h / 1e9:.1f} TFLOP/s), causal softmax attention {ms_s:.3f} ms "
+          f"({flop / ms_s / 1e9:.1f} TFLOP/s); ratio {ms_s / ms_h:.2f}", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -506,7 +536,7 @@ def main():
                     help="untimed calls for about this long before the warm-up steps (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extended", action="store_true")
-    ap.add_argument("--only", choices=["layers", "cached", "attn_bwd", "layer_bwd", "layer_bwd_call"],
+    ap.add_argument("--only", choices=["layers", "cached", "attn_bwd", "layer_bwd", "layer_bwd_call", "softmax"],
                     help="run only this informational leg of --extended (stderr), without the metric line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (torch copy_) five times, to scale "
@@ -526,7 +556,8 @@ def main():
         dev = torch.device("cuda:0")
         {"layers": lambda: extended(args, dev, layers_only=True), "cached": lambda: cached_scoring(dev),
          "attn_bwd": lambda: attn_backward(dev), "layer_bwd": lambda: layer_backward(dev),
-         "layer_bwd_call": lambda: layer_backward(dev, train_step=False)}[args.only]()
+         "layer_bwd_call": lambda: layer_backward(dev, train_step=False),
+         "softmax": lambda: softmax_context(dev)}[args.only]()
         return
     run(args)
 

@@ -86,6 +86,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hstu_attn_fwd_noalloc.restype = ctypes.c_int
     lib.hstu_attn_fwd_noalloc.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(AttnDescT), ctypes.c_int, c_vp, c_vp,
                                           c_vp, c_vp, ctypes.c_int, c_vp]
+    lib.hstu_softmax_attn_fwd.restype = ctypes.c_int
+    lib.hstu_softmax_attn_fwd.argtypes = [ctypes.POINTER(JaggedT), c_i32, c_i32, ctypes.c_int, c_vp, c_vp, c_vp, c_vp,
+                                          ctypes.c_int, c_vp]
     lib.hstu_attn_cached_workspace_bytes.restype = c_sz
     lib.hstu_attn_cached_workspace_bytes.argtypes = [ctypes.POINTER(JaggedT), ctypes.POINTER(JaggedT),
                                                      ctypes.POINTER(AttnDescT)]
@@ -215,6 +218,18 @@ def attn_fwd_noalloc(seq_offsets, timestamps, q, k, v, pos_bias, time_bias, *, m
     desc = make_desc(H, Dh, pos_bias, time_bias, mask)
     _check(lib.hstu_attn_fwd_noalloc(ctypes.byref(jag), ctypes.byref(desc), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
                                      _ptr(out), _dtype_code(out), _stream(stream)))
+    return out
+
+
+def softmax_attn_fwd(seq_offsets, q, k, v, *, max_seq_len: int, out_dtype=None, out=None, stream=None):
+    """O = hstu_softmax_attn_fwd(...): causal softmax attention, q, k, v [T, H, 128] bf16."""
+    lib = load_library()
+    T, H, Dh = q.shape
+    if out is None:
+        out = torch.empty((T, H, Dh), dtype=out_dtype or q.dtype, device=q.device)
+    jag = JaggedT(seq_offsets.numel() - 1, T, int(max_seq_len), _ptr(seq_offsets), None, None, None)
+    _check(lib.hstu_softmax_attn_fwd(ctypes.byref(jag), H, Dh, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                     _dtype_code(out), _stream(stream)))
     return out
 
 

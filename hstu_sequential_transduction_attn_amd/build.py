@@ -17,7 +17,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libhstu.so")
-SOURCES = ["api.cpp", "attn_fwd.hip", "attn_bwd.hip", "gemm.hip", "rows.hip", "layer_bwd.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "attn_fwd.hip", "attn_bwd.hip", "gemm.hip", "rows.hip", "layer_bwd.hip", "noalloc.hip", "softmax_attn.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -236,6 +236,55 @@ hstu_status_t hstu_attn_fwd_noalloc(const hstu_jagged_t *jag, const hstu_attn_de
   }
 }
 
+hstu_status_t hstu_softmax_attn_fwd(const hstu_jagged_t *jag, int32_t num_heads, int32_t head_dim,
+                                    hstu_dtype_t in_dtype, const void *q, const void *k, const void *v, void *out,
+                                    hstu_dtype_t out_dtype, void *stream) {
+  try {
+    if (!jag) return fail(HSTU_ERR_INVALID_ARGUMENT, "jag is NULL");
+    if (jag->num_seqs < 0 || jag->total_tokens < 0)
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "num_seqs = %d, total_tokens = %d", jag->num_seqs, jag->total_tokens);
+    if (jag->max_seq_len < 0 || jag->max_seq_len > jag->total_tokens)
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "max_seq_len = %d outside [0, total_tokens = %d]", jag->max_seq_len,
+                  jag->total_tokens);
+    if (jag->num_seqs > 0 && !jag->seq_offsets) return fail(HSTU_ERR_INVALID_ARGUMENT, "seq_offsets is NULL");
+    if (jag->num_seqs == 0 && jag->total_tokens != 0)
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "num_seqs = 0 but total_tokens = %d", jag->total_tokens);
+    if (num_heads < 1) return fail(HSTU_ERR_INVALID_ARGUMENT, "num_heads = %d < 1", num_heads);
+    if (head_dim != 128) return fail(HSTU_ERR_UNSUPPORTED, "head_dim = %d (only 128)", head_dim);
+    if (in_dtype != HSTU_BF16) return fail(HSTU_ERR_UNSUPPORTED, "in_dtype must be HSTU_BF16");
+    if (!valid_dtype(out_dtype)) return fail(HSTU_ERR_INVALID_ARGUMENT, "out_dtype = %d invalid", (int)out_dtype);
+    const long long blocks = ((long long)jag->max_seq_len + 127) / 128 * num_heads * jag->num_seqs;
+    if (blocks > 0x7fffffffLL) return fail(HSTU_ERR_UNSUPPORTED, "launch too large (%lld workgroups)", blocks);
+    const int64_t T = jag->total_tokens;
+    if (T == 0) return ok();
+    if (!q || !k || !v || !out) return fail(HSTU_ERR_INVALID_ARGUMENT, "q/k/v/out is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "q/k/v/out must be 16-byte aligned");
+    const size_t nin = (size_t)T * num_heads * head_dim * 2;
+    const size_t nout = (size_t)T * num_heads * head_dim * esize(out_dtype);
+    if (overlaps(out, nout, q, nin) || overlaps(out, nout, k, nin) || overlaps(out, nout, v, nin))
+      return fail(HSTU_ERR_INVALID_ARGUMENT, "out overlaps q, k or v");
+    hstu::AttnArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.row_stride = (int64_t)num_heads * head_dim;
+    a.out_row_stride = a.row_stride;
+    a.seq_offsets = jag->seq_offsets;
+    a.num_seqs = jag->num_seqs;
+    a.num_heads = num_heads;
+    a.head_dim = head_dim;
+    a.max_seq_len = jag->max_seq_len;
+    a.num_rows_total = T;
+    a.in_dtype = hstu::kBF16;
+    a.out_dtype = out_dtype == HSTU_BF16 ? hstu::kBF16 : hstu::kF32;
+    return from_hip(hstu::launch_softmax_attn(a, (hipStream_t)stream), "softmax_attn launch");
+  } catch (...) {
+    return fail(HSTU_ERR_DEVICE, "unexpected C++ exception in hstu_softmax_attn_fwd");
+  }
+}
+
 namespace {
 // Cached-scoring workspace: timestamp ranges of the candidates and of the history, then (with key
 // splits) the partial sums [kv_splits][T_c][H][Dh] fp32; each region 256-byte aligned.

@@ -67,6 +67,9 @@ size_t attn_tau_stats_bytes(int64_t total_tokens, int64_t num_seqs);
 constexpr size_t kNoallocScratchBytes = (size_t)1 << 20;
 hipError_t noalloc_scratch(void **ptr);
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream);
+// Causal softmax attention (bf16 inputs, Dh = 128), the comparison point of the pointwise forward:
+// q, k, v, out, row strides, seq_offsets, num_seqs, num_heads, max_seq_len, out_dtype are read.
+hipError_t launch_softmax_attn(const AttnArgs &a, hipStream_t stream);
 // Candidates against a cached history: each candidate sees every history key of its user and itself.
 hipError_t launch_attn_cached(const AttnArgs &a, hipStream_t stream);
 

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 7
+#define HSTU_ABI_VERSION 8
 
 typedef enum {
   HSTU_OK = 0,
@@ -159,6 +159,24 @@ hstu_status_t hstu_attn_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *de
 hstu_status_t hstu_attn_fwd_noalloc(const hstu_jagged_t *jag, const hstu_attn_desc_t *desc, hstu_dtype_t in_dtype,
                                     const void *q, const void *k, const void *v, void *out, hstu_dtype_t out_dtype,
                                     void *stream);
+
+/*
+ * Causal softmax attention over the same jagged batch, for comparison with the pointwise attention:
+ * "Actions Speak Louder than Words ...", abstract, measures HSTU against FlashAttention2-based
+ * Transformers at sequence length 8192; this is the textbook attention of such a Transformer, timed on
+ * the same shapes and hardware.  It is not a step of the HSTU layer.
+ *   out[t][h][:] = sum_{j <= i} softmax_j(q_t . k_j / sqrt(Dh)) v_j     (sequence-local i, j; causal)
+ * jag: num_seqs, total_tokens, max_seq_len and seq_offsets are read (timestamps, num_candidates and
+ * attn_scale are not).  q, k, v: [T][num_heads][head_dim] bf16, row-major, 16-byte aligned (device).
+ * out: [T][num_heads][head_dim], out_dtype HSTU_BF16 or HSTU_F32; may not overlap an input.
+ * bf16 MFMA with fp32 accumulation; the online (running-maximum) softmax in fp32; the probabilities are
+ * rounded to bf16 as the AV operand.  No workspace; nothing is allocated or synchronised.
+ * Errors: HSTU_ERR_UNSUPPORTED unless in_dtype is HSTU_BF16 and head_dim is 128; the argument checks
+ * of hstu_attn_fwd otherwise (HSTU_ERR_INVALID_ARGUMENT).
+ */
+hstu_status_t hstu_softmax_attn_fwd(const hstu_jagged_t *jag, int32_t num_heads, int32_t head_dim,
+                                    hstu_dtype_t in_dtype, const void *q, const void *k, const void *v, void *out,
+                                    hstu_dtype_t out_dtype, void *stream);
 
 /*
  * Workspace needed by hstu_attn_fwd_cached (bytes; 0 is possible): the per-32-token timestamp ranges

@@ -39,7 +39,7 @@ def _attn(jag, desc, in_dt=L.HSTU_BF16, out_dt=L.HSTU_BF16, q=P16 + 0x10000, k=P
 
 def test_exports_every_declared_symbol():
     names = L.exported_functions_in_header()
-    assert len(names) == 20
+    assert len(names) == 21
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib()
-    assert lib.hstu_abi_version() == 7
+    assert lib.hstu_abi_version() == 8
     assert lib.hstu_status_string(OK) == b"HSTU_OK"
     assert lib.hstu_status_string(WS_SMALL) == b"HSTU_ERR_WORKSPACE_TOO_SMALL"
     assert lib.hstu_status_string(99) == b"HSTU_STATUS_UNKNOWN"
@@ -420,3 +420,21 @@ def test_layer_saved_sizes_and_errors():
     assert st == WS_SMALL
     st, msg = bwd(saved=P16 + 0x40000000 + 256)      # saved on top of the workspace
     assert st == INVALID and "overlap" in msg
+
+
+def test_softmax_attn_argument_checks():
+    lib = _lib()
+
+    def call(jag, H=4, Dh=128, in_dt=L.HSTU_BF16, out_dt=L.HSTU_BF16, q=P16 + 0x10000, k=P16 + 0x20000000,
+             v=P16 + 0x40000000, out=P16 + 0x60000000):
+        st = lib.hstu_softmax_attn_fwd(ctypes.byref(jag) if jag else None, H, Dh, in_dt, q, k, v, out, out_dt, None)
+        return st, lib.hstu_last_error().decode()
+    assert call(None)[0] == INVALID
+    assert call(_jag(), Dh=64)[0] == UNSUPPORTED
+    assert call(_jag(), in_dt=L.HSTU_F32)[0] == UNSUPPORTED
+    assert call(_jag(), H=0)[0] == INVALID
+    assert call(_jag(), out_dt=9)[0] == INVALID
+    assert call(_jag(), q=None)[0] == INVALID
+    st, msg = call(_jag(), out=P16 + 0x10000 + 64)
+    assert st == INVALID and "overlaps" in msg
+    assert call(L.JaggedT(3, 0, 0, P16, None, None, None), q=None, k=None, v=None, out=None) == (OK, "")
