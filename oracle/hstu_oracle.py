@@ -367,13 +367,25 @@ def layer_norm_bwd(x, eps, dy):
     return rstd * (dy - dy.mean(axis=-1, keepdims=True) - xh * (dy * xh).mean(axis=-1, keepdims=True))
 
 
+def round_bf16(a) -> np.ndarray:
+    """Each value rounded to the nearest bfloat16 (8 significant bits, ties to even), returned as
+    float64: the float32 value of the input keeps its top 16 bits after rounding."""
+    f = np.asarray(a, np.float64).astype(np.float32)
+    b = f.view(np.uint32).astype(np.uint64)
+    r = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def layer_bwd(x, jag, w_uvqk, b_uvqk, w_out, b_out, pos_bias, time_bias, num_heads, head_dim,
-              ln_eps, ln_output, dy, return_sq=False):
+              ln_eps, ln_output, dy, return_sq=False, bf16_attention=False):
     """Gradients of layer_fwd for an upstream gradient dy of its output y (the layer is trained:
     [DLRMv4] describes a training benchmark).  Returns a dict of float64 arrays:
         dx [T, D], d_w_uvqk [4*H*Dh, D], d_b_uvqk [4*H*Dh], d_w_out [D, H*Dh], d_b_out [D],
         d_pos_bias [R, P], d_time_bias [R, Tb]
     (with return_sq also d_pos_bias_sq, d_time_bias_sq: attn_bwd's per-bin sums of squares).
+    bf16_attention: the attention's operands q, k, v (forward and backward) and do (backward) are
+    rounded to bf16 first, the precision in which a bf16 layer stores them; every other step stays
+    float64.
     The chain, from the output back (r = x + g W2^T + b2 is the pre-LayerNorm sum, g = LN(o) * U):
         dr = layer_norm_bwd(r, dy) if ln_output else dy
         d_b_out = sum_t dr;  d_w_out = dr^T g;  dg = dr W2
@@ -392,6 +404,8 @@ def layer_bwd(x, jag, w_uvqk, b_uvqk, w_out, b_out, pos_bias, time_bias, num_hea
         z = z + np.asarray(b_uvqk, np.float64)
     s = silu(z)
     u, v, q, k = (s[:, c * hd:(c + 1) * hd].reshape(T, num_heads, head_dim) for c in range(4))
+    if bf16_attention:
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
     o = attn_fwd(jag, q, k, v, pos_bias, time_bias).reshape(T, hd)
     on = layer_norm(o, ln_eps)
     uf = u.reshape(T, hd)
@@ -409,6 +423,8 @@ def layer_bwd(x, jag, w_uvqk, b_uvqk, w_out, b_out, pos_bias, time_bias, num_hea
     dg = dr @ w2
     du = dg * on
     do = layer_norm_bwd(o, ln_eps, dg * uf)
+    if bf16_attention:
+        do = round_bf16(do)
     res = attn_bwd(jag, q, k, v, pos_bias, time_bias, do.reshape(T, num_heads, head_dim), return_sq=return_sq)
     dq, dk, dv, dwp, dwt = res[:5]
     ds = np.concatenate([du, dv.reshape(T, hd), dq.reshape(T, hd), dk.reshape(T, hd)], axis=1)

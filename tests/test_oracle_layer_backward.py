@@ -116,3 +116,42 @@ def test_zero_output_weights_pass_the_gradient_straight_through():
     for name in ("d_w_uvqk", "d_b_uvqk", "d_pos_bias", "d_time_bias"):
         assert not np.any(got[name]), name
     np.testing.assert_allclose(got["d_b_out"], dy.sum(axis=0), rtol=1e-14)
+
+
+def test_round_bf16_matches_the_bit_pattern_definition():
+    # values exactly representable stay; halfway cases go to the even neighbour; the result has 8
+    # significant bits: round(x) * 2^k is x to within half a unit of its 8th bit
+    import numpy as np
+    from oracle import hstu_oracle as O
+    one_ulp = 2.0 ** -7
+    assert O.round_bf16(np.array([1.0]))[0] == 1.0
+    assert O.round_bf16(np.array([1.0 + one_ulp / 2]))[0] == 1.0                 # tie -> even (1.0)
+    assert O.round_bf16(np.array([1.0 + 3 * one_ulp / 2]))[0] == 1.0 + 2 * one_ulp   # tie -> even
+    assert O.round_bf16(np.array([1.0 + 0.6 * one_ulp]))[0] == 1.0 + one_ulp
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(10000) * 10.0 ** rng.integers(-3, 4, 10000)
+    r = O.round_bf16(x)
+    m, e = np.frexp(r)                                 # r = m 2^e, 0.5 <= |m| < 1
+    assert np.all(m * 256 == np.round(m * 256))        # 8 significant bits
+    _, ex = np.frexp(x)                                # x = mx 2^ex: one ulp of 8 bits is 2^(ex - 8)
+    assert np.all(np.abs(r - x) <= 2.0 ** (ex - 9) * (1 + 2.0 ** -15))   # within half an ulp
+
+
+def test_bf16_attention_reading_changes_only_through_the_rounded_operands():
+    # with every attention operand already a bf16 value the rounded and the exact backward agree
+    # bit for bit; otherwise they differ by the rounding's effect, of order 2^-8 relative
+    import numpy as np
+    from hstu_sequential_transduction_attn_amd import inputs as I
+    from oracle import hstu_oracle as O
+    case = I.jagged_layer_case("rb", 4401, [5, 9], D=16, H=2, Dh=8, P=8, Tb=8, dtype="bf16", bias_std=0.1)
+    L = case.layers[0]
+    jag = dict(seq_offsets=case.jagged.seq_offsets, timestamps=case.jagged.timestamps, mask=0,
+               num_candidates=None, attn_scale=None)
+    dy = np.random.default_rng(2).standard_normal(case.x.shape)
+    args = (case.x.values, jag, L.w_uvqk.values, L.b_uvqk.values, L.w_out.values, L.b_out.values,
+            L.rab.pos_bias, L.rab.time_bias, 2, 8, L.ln_eps, True, dy)
+    a = O.layer_bwd(*args)
+    b = O.layer_bwd(*args, bf16_attention=True)
+    for key in a:
+        rel = np.linalg.norm(a[key] - b[key]) / np.linalg.norm(a[key])
+        assert 0 < rel < 2e-2, (key, rel)
