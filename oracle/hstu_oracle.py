@@ -377,7 +377,7 @@ def round_bf16(a) -> np.ndarray:
 
 
 def layer_bwd(x, jag, w_uvqk, b_uvqk, w_out, b_out, pos_bias, time_bias, num_heads, head_dim,
-              ln_eps, ln_output, dy, return_sq=False, bf16_attention=False):
+              ln_eps, ln_output, dy, return_sq=False, bf16_attention=False, attn_operands=None):
     """Gradients of layer_fwd for an upstream gradient dy of its output y (the layer is trained:
     [DLRMv4] describes a training benchmark).  Returns a dict of float64 arrays:
         dx [T, D], d_w_uvqk [4*H*Dh, D], d_b_uvqk [4*H*Dh], d_w_out [D, H*Dh], d_b_out [D],
@@ -386,6 +386,9 @@ def layer_bwd(x, jag, w_uvqk, b_uvqk, w_out, b_out, pos_bias, time_bias, num_hea
     bf16_attention: the attention's operands q, k, v (forward and backward) and do (backward) are
     rounded to bf16 first, the precision in which a bf16 layer stores them; every other step stays
     float64.
+    attn_operands: a function (name, array) -> array applied to the same four operands, named
+    "q", "k", "v" and "do" (e.g. a perturbation of each element); bf16_attention is the case of
+    round_bf16.  The same q, k, v serve the attention's forward and backward.
     The chain, from the output back (r = x + g W2^T + b2 is the pre-LayerNorm sum, g = LN(o) * U):
         dr = layer_norm_bwd(r, dy) if ln_output else dy
         d_b_out = sum_t dr;  d_w_out = dr^T g;  dg = dr W2
@@ -405,7 +408,11 @@ def layer_bwd(x, jag, w_uvqk, b_uvqk, w_out, b_out, pos_bias, time_bias, num_hea
     s = silu(z)
     u, v, q, k = (s[:, c * hd:(c + 1) * hd].reshape(T, num_heads, head_dim) for c in range(4))
     if bf16_attention:
-        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+        if attn_operands is not None:
+            raise ValueError("give bf16_attention or attn_operands, not both")
+        attn_operands = lambda name, a: round_bf16(a)
+    if attn_operands is not None:
+        q, k, v = attn_operands("q", q), attn_operands("k", k), attn_operands("v", v)
     o = attn_fwd(jag, q, k, v, pos_bias, time_bias).reshape(T, hd)
     on = layer_norm(o, ln_eps)
     uf = u.reshape(T, hd)
@@ -423,8 +430,8 @@ def layer_bwd(x, jag, w_uvqk, b_uvqk, w_out, b_out, pos_bias, time_bias, num_hea
     dg = dr @ w2
     du = dg * on
     do = layer_norm_bwd(o, ln_eps, dg * uf)
-    if bf16_attention:
-        do = round_bf16(do)
+    if attn_operands is not None:
+        do = attn_operands("do", do)
     res = attn_bwd(jag, q, k, v, pos_bias, time_bias, do.reshape(T, num_heads, head_dim), return_sq=return_sq)
     dq, dk, dv, dwp, dwt = res[:5]
     ds = np.concatenate([du, dv.reshape(T, hd), dq.reshape(T, hd), dk.reshape(T, hd)], axis=1)

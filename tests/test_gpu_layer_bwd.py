@@ -5,6 +5,8 @@ The oracle's layer gradients are pinned to finite differences of the forward ora
 nonzero biases, ragged batches with empty and one-token sequences, odd model widths (plain GEMM
 tails), batches large enough for the large-tile and split-K weight-gradient GEMMs, the candidate
 mask, an fp32 gradient stream with fp32 activations, an empty batch, and bitwise determinism.
+bf16 cases are held to the kernels' own bar plus 8 sigma of the noise that the bf16 storage of the
+attention's q, k, v and dO puts on each gradient element (see _check and tests/_noise.py).
 """
 import numpy as np
 import pytest
@@ -12,6 +14,7 @@ import pytest
 from hstu_sequential_transduction_attn_amd import inputs as I
 from oracle import hstu_oracle as O
 
+from _noise import operand_noise
 from _util import dev, host, jag_dev, max_abs, oracle_jag, rel_l2
 
 pytestmark = pytest.mark.gpu
@@ -40,42 +43,56 @@ def _gpu(case, dy, ln_output, x_f32=False, act_split=False):
     return {k: host(v) for k, v in out.items()}
 
 
-def _oracle(case, dy, ln_output):
+def _oracle(case, dy, ln_output, noise_samples=0, seed=0):
+    """The exact float64 gradients and, with noise_samples, the per-element sigma of the noise that
+    the bf16 storage of the attention's q, k, v and dO puts on them (tests/_noise.py)."""
     L = case.layers[0]
-    return O.layer_bwd(case.x.values, oracle_jag(case.jagged), L.w_uvqk.values,
-                       None if L.b_uvqk is None else L.b_uvqk.values, L.w_out.values,
-                       None if L.b_out is None else L.b_out.values, L.rab.pos_bias, L.rab.time_bias,
-                       case.num_heads, case.head_dim, L.ln_eps, ln_output, dy.values, return_sq=True)
+
+    def run(f):
+        return O.layer_bwd(case.x.values, oracle_jag(case.jagged), L.w_uvqk.values,
+                           None if L.b_uvqk is None else L.b_uvqk.values, L.w_out.values,
+                           None if L.b_out is None else L.b_out.values, L.rab.pos_bias, L.rab.time_bias,
+                           case.num_heads, case.head_dim, L.ln_eps, ln_output, dy.values, return_sq=True,
+                           attn_operands=f)
+    if not noise_samples:
+        return run(None), None
+    return operand_noise(run, samples=noise_samples, seed=seed)
 
 
-def _check(got, want, dtype, what):
-    """Norm-wise bar, as for the attention gradients: rel-L2 5e-3 (bf16) or 1e-5 (fp32) and, for bf16,
-    max-abs within 2e-2 + 2^-7 max|want| (every product's operands carry a bf16 rounding, 2^-9
-    relative, and the weight gradients are sums over all tokens).
-    The bias-table gradients sum dS over every pair of a bin, with cancellation; in the layer the
-    attention's inputs q, k, v and dO are themselves bf16 roundings of values the oracle keeps in
-    float64, so each summed term carries its own rounding error.  Their bar adds the noise of
-    independent 2^-8 relative errors per term, 2^-8 sqrt(sum of dS^2) per bin: norm-wise
-    ||err|| <= 5e-3 ||want|| + 2^-8 ||s||, elementwise |err| <= 2e-2 + 2^-7 (max|want| + s)."""
+def _check(got, want_sigma, dtype, what):
+    """fp32: rel-L2 <= 1e-5 on every gradient.
+    bf16: the bar the kernels meet with exact operands, plus 8 sigma of the noise of the attention's
+    bf16 operands (q, k, v, dO: independent relative errors up to 2^-8 per element, carried through
+    the float64 oracle, so that the correlation of one token's errors over all its pairs is kept):
+      dx, weight and bias-vector gradients: |err| <= 2e-2 + 2^-7 max|want| + 8 sigma elementwise and
+        rel-L2 <= 5e-3 + 3 ||sigma|| / ||want||;
+      bias-table gradients, per bin: |err| <= 4 * 2^-7 sqrt(sum dS^2) + 2^-7 |want| + 1e-6 + 8 sigma
+        (the attention-level bin bar: each bin sums many dS terms with their own roundings)."""
+    want, sigma = want_sigma
     for name in NAMES:
-        x, y = got[name], want[name]
+        x, y = np.asarray(got[name], np.float64), want[name]
         assert np.all(np.isfinite(x)), f"{what} {name}: non-finite"
         r, m = rel_l2(x, y), max_abs(x, y)
-        print(f"  {name:12s} rel_l2={r:.3e} max_abs={m:.3e} max|want|={float(np.abs(y).max()):.3e}")
         if dtype != "bf16":
+            print(f"  {name:12s} rel_l2={r:.3e} max_abs={m:.3e}")
             assert r <= 1e-5, f"{what} {name}: rel_l2={r:.3e} max_abs={m:.3e}"
             continue
-        ymax = float(np.abs(y).max() if y.size else 0.0)
+        err = np.abs(x - y)
+        sg = sigma[name]
         if name in ("d_pos_bias", "d_time_bias"):
-            sq = np.sqrt(want[name + "_sq"])
-            err = np.abs(np.asarray(x, np.float64) - y)
-            norm_bound = 5e-3 * np.linalg.norm(y) + 2.0 ** -8 * np.linalg.norm(sq)
-            assert np.linalg.norm(err) <= norm_bound, f"{what} {name}: ||err||={np.linalg.norm(err):.3e} > {norm_bound:.3e}"
-            excess = err - (2e-2 + 2.0 ** -7 * (ymax + sq))
-            assert excess.max() <= 0, f"{what} {name}: elementwise bound exceeded by {excess.max():.3e}"
+            bound = 4 * 2.0 ** -7 * np.sqrt(want[name + "_sq"]) + 2.0 ** -7 * np.abs(y) + 1e-6 + 8 * sg
+            rbar = None
         else:
-            bound = 2e-2 + 2.0 ** -7 * ymax
-            assert r <= 5e-3 and m <= bound, f"{what} {name}: rel_l2={r:.3e} max_abs={m:.3e} (bound {bound:.3e})"
+            ymax = float(np.abs(y).max() if y.size else 0.0)
+            bound = 2e-2 + 2.0 ** -7 * ymax + 8 * sg
+            ny = float(np.linalg.norm(y))
+            rbar = 5e-3 + 3 * float(np.linalg.norm(sg)) / (ny if ny > 0 else 1.0)
+        use = float((err / bound).max()) if err.size else 0.0
+        print(f"  {name:12s} rel_l2={r:.3e} max_abs={m:.3e} max|err|/bar={use:.3f} "
+              f"max 8sigma={8 * float(sg.max()) if sg.size else 0.0:.3e}")
+        assert use <= 1.0, f"{what} {name}: max|err|/bar={use:.3f} rel_l2={r:.3e} max_abs={m:.3e}"
+        if rbar is not None:
+            assert r <= rbar, f"{what} {name}: rel_l2={r:.3e} > {rbar:.3e}"
 
 
 @pytest.mark.parametrize("ln_output", [False, True])
@@ -94,7 +111,7 @@ def test_layer_bwd_bf16_ragged_odd_width(ln_output):
     case = I.jagged_layer_case("lbwd", 1310, [1, 0, 129, 64, 200, 31], D=72, H=3, Dh=64, P=50, Tb=30, dtype="bf16",
                                bias_std=0.3)
     dy = _dy(case, 1311, "bf16")
-    _check(_gpu(case, dy, ln_output), _oracle(case, dy, ln_output), "bf16", "bf16 ragged")
+    _check(_gpu(case, dy, ln_output), _oracle(case, dy, ln_output, 24, 1312), "bf16", "bf16 ragged")
 
 
 def test_layer_bwd_bf16_large_tiles_split_k():
@@ -107,7 +124,7 @@ def test_layer_bwd_bf16_large_tiles_split_k():
                                bias_std=0.1)
     print(f"  T={sum(lengths)}", flush=True)
     dy = _dy(case, 1321, "bf16")
-    _check(_gpu(case, dy, True), _oracle(case, dy, True), "bf16", "bf16 large")
+    _check(_gpu(case, dy, True), _oracle(case, dy, True, 8, 1322), "bf16", "bf16 large")
 
 
 def test_layer_bwd_candidates():
@@ -117,7 +134,7 @@ def test_layer_bwd_candidates():
     case.jagged.mask = I.CAUSAL_CANDIDATES
     case.jagged.num_candidates = np.array([50, 1, 100, 1], np.int32)
     dy = _dy(case, 1331, "bf16")
-    _check(_gpu(case, dy, False), _oracle(case, dy, False), "bf16", "candidates")
+    _check(_gpu(case, dy, False), _oracle(case, dy, False, 24, 1332), "bf16", "candidates")
 
 
 @pytest.mark.parametrize("act_split", [False, True])
@@ -128,7 +145,8 @@ def test_layer_bwd_fp32_gradient_stream(act_split):
                                bias_std=0.2)
     case.x = I.Tensor.make(case.x.values, "f32")   # the oracle reads the same fp32 x
     dy = _dy(case, 1341, "f32")
-    _check(_gpu(case, dy, True, x_f32=True, act_split=act_split), _oracle(case, dy, True), "bf16", "fp32 stream")
+    _check(_gpu(case, dy, True, x_f32=True, act_split=act_split), _oracle(case, dy, True, 24, 1342), "bf16",
+           "fp32 stream")
 
 
 def test_layer_bwd_empty_batch_zeroes_every_gradient():
@@ -219,22 +237,20 @@ def test_layer_bwd_f32_random_shapes(seed):
     _check(_gpu(case, dy, ln_output), _oracle(case, dy, ln_output), "f32", f"random {seed}")
 
 
-@pytest.mark.parametrize("seed", [7101, 7102, 7103, 7104, 7105])
+@pytest.mark.parametrize("seed", list(range(7101, 7111)))
 def test_layer_bwd_bf16_random_shapes(seed):
-    """bf16 layers on seeded random shapes (odd widths, candidates, biases, the output LayerNorm, fp32
-    streams with and without split activations), kept to tables of at least 30 buckets and sequences
-    of at least 8 tokens (with a few huge bins or 1-token sums, bf16 roundings of q, k, v do not
-    average out).  The next seed of this generator, 7106 (lengths 921 and 270, P = 185), is left out:
-    its position-bias gradient exceeds the bin bound by 11%, the clamped bin pooling most pairs of
-    the 921-token sequence, whose per-token roundings are correlated, as that bound does not model."""
+    """bf16 layers on seeded random shapes: every one of the generator's first ten seeds (tables from 1
+    bucket, sequences from 1 token, odd widths, candidates, biases, the output LayerNorm, fp32 streams
+    with and without split activations), at the bar of _check: the kernels' own bar plus 8 sigma of
+    the noise of the attention's bf16 operands."""
     rng = np.random.default_rng(seed)
     B = int(rng.integers(1, 6))
-    lengths = [int(x) for x in rng.integers(8, 300, B)]
+    lengths = [int(x) for x in rng.integers(1, 300, B)]
     if rng.random() < 0.3:
         lengths[0] = int(rng.integers(300, 1100))
     D = int(rng.choice([64, 72, 96, 128, 200, 256, 512]))
     H, Dh = int(rng.integers(1, 4)), int(rng.choice([32, 64, 128]))
-    P, Tb = int(rng.integers(30, 200)), int(rng.integers(30, 70))
+    P, Tb = int(rng.integers(1, 200)), int(rng.integers(1, 70))
     ln_output = bool(rng.random() < 0.5)
     case = I.jagged_layer_case("lrndb", seed, lengths, D=D, H=H, Dh=Dh, P=P, Tb=Tb, dtype="bf16",
                                bias_std=float(rng.choice([0.0, 0.2])))
@@ -249,5 +265,5 @@ def test_layer_bwd_bf16_random_shapes(seed):
           f"ln_output={ln_output} candidates={case.jagged.num_candidates is not None} x_f32={x_f32} "
           f"split={act_split}", flush=True)
     dy = _dy(case, seed + 1, "f32" if x_f32 else "bf16")
-    _check(_gpu(case, dy, ln_output, x_f32=x_f32, act_split=act_split), _oracle(case, dy, ln_output), "bf16",
-           f"random {seed}")
+    got = _gpu(case, dy, ln_output, x_f32=x_f32, act_split=act_split)
+    _check(got, _oracle(case, dy, ln_output, 24, seed + 2), "bf16", f"random {seed}")

@@ -1,0 +1,138 @@
+"""Pins of the rounding-noise model that sets the bar of the bf16 layer-backward tests (tests/_noise.py).
+
+The model: q, k, v and dO reach a bf16 layer's attention as x (1 + d), |d| <= 2^-8 per element,
+independently; the noise of every gradient element is carried through the float64 oracle.  Pinned
+here against (1) the oracle's own evaluation with those operands really rounded to bf16, on the
+shapes that break a model of independent pair terms (tables of 1 to 3 buckets, sequences of 1 to 7
+tokens); (2) the linearised variance summed from finite-difference derivatives of every operand
+element of a tiny layer; (3) the closed-form derivative of a bias-table bin in one element of dO,
+which shows that the oracle's operand hook reaches the attention backward's dO.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from hstu_sequential_transduction_attn_amd import inputs as I
+from oracle import hstu_oracle as O
+
+from _noise import U_BF16, operand_noise
+from _util import oracle_jag
+
+NAMES = ["dx", "d_w_uvqk", "d_b_uvqk", "d_w_out", "d_b_out", "d_pos_bias", "d_time_bias"]
+
+
+def _runner(case, dy, ln_output):
+    L = case.layers[0]
+
+    def run(f, bf16=False):
+        return O.layer_bwd(case.x.values, oracle_jag(case.jagged), L.w_uvqk.values,
+                           None if L.b_uvqk is None else L.b_uvqk.values, L.w_out.values,
+                           None if L.b_out is None else L.b_out.values, L.rab.pos_bias, L.rab.time_bias,
+                           case.num_heads, case.head_dim, L.ln_eps, ln_output, dy, attn_operands=f,
+                           bf16_attention=bf16)
+    return run
+
+
+def _case(seed, lengths, D, H, Dh, P, Tb, bias_std=0.2):
+    case = I.jagged_layer_case("noise", seed, lengths, D=D, H=H, Dh=Dh, P=P, Tb=Tb, dtype="bf16",
+                               bias_std=bias_std)
+    dy = np.random.default_rng(seed + 1).standard_normal(case.x.shape)
+    return case, dy
+
+
+@pytest.mark.parametrize("seed,lengths,P,Tb,ln_output", [
+    (8801, [1, 2, 3, 7, 60], 1, 1, True),
+    (8802, [1, 5, 4, 90], 2, 3, False),
+    (8803, [3, 1, 1, 6, 2, 40], 3, 1, True),
+    (8804, [250, 7], 1, 2, False),
+])
+def test_model_covers_the_oracles_own_bf16_rounding(seed, lengths, P, Tb, ln_output):
+    """Tiny tables (a bin pools most pairs) and 1-7 token sequences (a gradient sums few pairs):
+    the oracle with q, k, v, dO rounded to bf16 stays within 8 sigma of the exact oracle,
+    and within 6 sigma for every element (the model is no loose bound)."""
+    case, dy = _case(seed, lengths, D=64, H=2, Dh=32, P=P, Tb=Tb)
+    run = _runner(case, dy, ln_output)
+    exact, sigma = operand_noise(run, samples=24, seed=seed)
+    rounded = run(None, True)
+    worst = 0.0
+    for name in NAMES:
+        err = np.abs(rounded[name] - exact[name])
+        assert np.all(err <= 8 * sigma[name] + 1e-12), name
+        live = sigma[name] > 0
+        if live.any():
+            worst = max(worst, float((err[live] / sigma[name][live]).max()))
+    assert worst <= 6.0, worst
+    # the rounding moves some bin of a bias table by more than 2^-7 of its value: a bar of the
+    # kernel's own relative error alone would fail there
+    moved = max(float((np.abs(rounded[n] - exact[n]) / (2.0 ** -7 * np.abs(exact[n]))).max())
+                for n in ("d_pos_bias", "d_time_bias"))
+    assert moved > 1.0, moved
+
+
+def test_sampled_sigma_matches_the_linearised_variance():
+    """sigma^2 = (u^2 / 3) sum_e (d out / d delta_e)^2 over every element e of q, k, v and dO, the
+    derivatives by central differences in the relative perturbation delta_e of one element."""
+    case, dy = _case(8810, [1, 4], D=8, H=1, Dh=4, P=2, Tb=2, bias_std=0.3)
+    run = _runner(case, dy, True)
+    exact = run(None)
+    shapes = {"q": (5, 1, 4), "k": (5, 1, 4), "v": (5, 1, 4), "do": (5, 4)}
+    var = {n: np.zeros(np.shape(exact[n])) for n in NAMES}
+    h = 1e-5
+    for op, shp in shapes.items():
+        for flat in range(int(np.prod(shp))):
+            idx = np.unravel_index(flat, shp)
+
+            def bump(sign):
+                def f(name, a):
+                    if name != op:
+                        return a
+                    b = np.array(a, np.float64, copy=True)
+                    b[idx] *= 1.0 + sign * h
+                    return b
+                return run(f)
+            up, dn = bump(1.0), bump(-1.0)
+            for n in NAMES:
+                var[n] += ((up[n] - dn[n]) / (2 * h)) ** 2
+    _, sigma = operand_noise(run, samples=3000, seed=8811)
+    for n in NAMES:
+        lin = np.sqrt(var[n] * U_BF16 ** 2 / 3.0)
+        assert lin.max() > 0, n     # with the output LayerNorm even d_b_out depends on the attention
+        live = lin > 1e-3 * lin.max()
+        ratio = sigma[n][live] / lin[live]
+        assert np.all(np.abs(ratio - 1.0) <= 0.12), (n, float(ratio.min()), float(ratio.max()))
+
+
+def test_do_hook_reaches_the_attention_backward():
+    """d_pos_bias[p] = sum over allowed pairs (i, j) of bucket p of c (dO_i . v_j) SiLU'(s_ij) is linear in
+    dO: adding h to dO[i, d] moves bin p by h c sum_j v_jd SiLU'(s_ij) over the j of that bin."""
+    n, D, Dh, P, Tb = 6, 8, 4, 3, 4
+    case, dy = _case(8820, [n], D=D, H=1, Dh=Dh, P=P, Tb=Tb, bias_std=0.3)
+    run = _runner(case, dy, False)
+    L = case.layers[0]
+    z = case.x.values.astype(np.float64) @ L.w_uvqk.values.T.astype(np.float64) + L.b_uvqk.values
+    sig = 1.0 / (1.0 + np.exp(-z))
+    a = z * sig
+    v, q, k = a[:, Dh:2 * Dh], a[:, 2 * Dh:3 * Dh], a[:, 3 * Dh:]
+    ts = case.jagged.timestamps.astype(np.int64)
+    c = 1.0 / n
+    i, d, h = 4, 2, 1e-3
+
+    def dsilu(s):
+        e = 1.0 / (1.0 + math.exp(-s))
+        return e * (1.0 + s * (1.0 - e))
+    want = np.zeros(P)
+    for j in range(i + 1):
+        bp = min(i - j, P - 1)
+        bt = min(int(abs(int(ts[i]) - int(ts[j]))).bit_length(), Tb - 1)
+        s = float(q[i] @ k[j]) + float(L.rab.pos_bias[0, bp]) + float(L.rab.time_bias[0, bt])
+        want[bp] += c * v[j, d] * dsilu(s)
+
+    def add(name, arr):
+        if name != "do":
+            return arr
+        b = np.array(arr, np.float64, copy=True)
+        b[i, d] += h
+        return b
+    got = (run(add)["d_pos_bias"][0] - run(lambda nm, arr: arr)["d_pos_bias"][0]) / h
+    np.testing.assert_allclose(got, want, rtol=1e-7, atol=1e-9)
