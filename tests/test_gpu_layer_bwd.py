@@ -267,3 +267,26 @@ def test_layer_bwd_bf16_random_shapes(seed):
     dy = _dy(case, seed + 1, "f32" if x_f32 else "bf16")
     got = _gpu(case, dy, ln_output, x_f32=x_f32, act_split=act_split)
     _check(got, _oracle(case, dy, ln_output, 24, seed + 2), "bf16", f"random {seed}")
+
+
+@pytest.mark.parametrize("P,Tb,ln_output,x_f32,act_split", [
+    (1, 1, True, False, False),
+    (2, 3, False, True, True),
+    (3, 1, True, True, False),
+])
+def test_layer_bwd_bf16_tiny_tables_and_short_sequences(P, Tb, ln_output, x_f32, act_split):
+    """The shapes that break a bar built on independent pair terms: tables of 1 to 3 buckets (one bin
+    pools most pairs of every sequence) and sequences of 1 to 7 tokens (each gradient sums few pairs),
+    beside one longer sequence, with candidates; held to the same bar as every bf16 case."""
+    lengths = [1, 2, 3, 4, 5, 6, 7, 1, 150]
+    seed = 7150 + 10 * P + Tb
+    case = I.jagged_layer_case("ltiny", seed, lengths, D=128, H=2, Dh=64, P=P, Tb=Tb, dtype="bf16", bias_std=0.2)
+    case.jagged.mask = I.CAUSAL_CANDIDATES
+    case.jagged.num_candidates = np.array([0, 1, 1, 2, 0, 3, 2, 0, 20], np.int32)
+    if x_f32:
+        case.x = I.Tensor.make(case.x.values, "f32")
+    print(f"\n[case] layer bwd bf16 tiny tables P={P} Tb={Tb} ln_output={ln_output} x_f32={x_f32} split={act_split}",
+          flush=True)
+    dy = _dy(case, seed + 1, "f32" if x_f32 else "bf16")
+    got = _gpu(case, dy, ln_output, x_f32=x_f32, act_split=act_split)
+    _check(got, _oracle(case, dy, ln_output, 24, seed + 2), "bf16", f"tiny tables P={P} Tb={Tb}")
