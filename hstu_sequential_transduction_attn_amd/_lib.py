@@ -133,6 +133,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                          c_vp, c_vp, ctypes.POINTER(LayerGradsT), c_vp, c_sz, c_vp, c_sz, c_vp]
     lib.hstu_gather_rows.restype = ctypes.c_int
     lib.hstu_gather_rows.argtypes = [c_vp, c_i64, c_i32, ctypes.c_int, c_vp, c_i32, c_vp, c_vp]
+    lib.hstu_id_errors.restype = ctypes.c_int
+    lib.hstu_id_errors.argtypes = [ctypes.POINTER(ctypes.c_uint32), c_i32, c_vp]
     if path is None:
         _lib = lib
     return lib
@@ -441,6 +443,15 @@ def gather_rows(table: torch.Tensor, ids: torch.Tensor, out=None, stream=None):
         out = torch.empty((T, d), dtype=table.dtype, device=table.device)
     _check(lib.hstu_gather_rows(_ptr(table), rows, d, _dtype_code(table), _ptr(ids), T, _ptr(out), _stream(stream)))
     return out
+
+
+def id_errors(reset: bool = True, stream=None) -> int:
+    """Out-of-range row ids met by the gathers on the current device since the last reset: 0, or the
+    number of clamped reads (hstu_id_errors; waits for the stream)."""
+    lib = load_library()
+    n = ctypes.c_uint32(0)
+    _check(lib.hstu_id_errors(ctypes.byref(n), 1 if reset else 0, _stream(stream)))
+    return int(n.value)
 
 
 def abi_version() -> int:

@@ -974,6 +974,29 @@ hstu_status_t hstu_gather_rows(const void *table, int64_t table_rows, int32_t d,
   }
 }
 
+hstu_status_t hstu_id_errors(uint32_t *count, int32_t reset, void *stream) {
+  try {
+    if (!count) return fail(HSTU_ERR_INVALID_ARGUMENT, "count is NULL");
+    unsigned int *word = nullptr;
+    hipError_t e = hstu::id_error_word(&word);
+    if (e != hipSuccess) return from_hip(e, "id-error word lookup");
+    e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return from_hip(e, "stream synchronize");
+    unsigned int v = 0;
+    e = hipMemcpy(&v, word, sizeof v, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return from_hip(e, "id-error word read");
+    if (reset) {
+      const unsigned int zero = 0;
+      e = hipMemcpy(word, &zero, sizeof zero, hipMemcpyHostToDevice);
+      if (e != hipSuccess) return from_hip(e, "id-error word reset");
+    }
+    *count = v;
+    return ok();
+  } catch (...) {
+    return fail(HSTU_ERR_DEVICE, "unexpected C++ exception in hstu_id_errors");
+  }
+}
+
 namespace {
 
 // Stack workspace.  Fused path (bf16, large-tile shapes): U (fp32), V, Q, K (bf16), O (fp32) and its
@@ -1111,6 +1134,11 @@ hstu_status_t hstu_stack_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
     }
 
     hipError_t e;
+    unsigned int *id_err = nullptr;
+    if (ids) {
+      e = hstu::id_error_word(&id_err);
+      if (e != hipSuccess) return from_hip(e, "id-error word lookup");
+    }
     for (int l = 0; l < L; ++l) {
       const hstu_layer_weights_t &w = weights[l];
       const bool last = l == L - 1;
@@ -1118,7 +1146,7 @@ hstu_status_t hstu_stack_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
       hstu::GemmStackProjArgs g1{};
       g1.a_mode = l == 0 ? (ids ? 1 : 0) : 2;
       g1.a = l == 0 ? table : (const void *)(wsb + ws.r32[prev]);
-      g1.ids = ids;
+      g1.ids = ids; g1.id_rows = table_rows; g1.id_err = id_err;
       g1.a_rowstat = (const float *)(wsb + ws.rowstat[prev]);
       g1.w = w.w_uvqk; g1.bias = w.b_uvqk;
       g1.u = (float *)(wsb + ws.u); g1.v = wsb + ws.v; g1.q = wsb + ws.q; g1.k = wsb + ws.k;
@@ -1140,7 +1168,8 @@ hstu_status_t hstu_stack_fwd(const hstu_jagged_t *jag, const hstu_attn_desc_t *d
       g2.row_stats = (const float *)(wsb + ws.ostat);
       g2.heads = (int32_t)H; g2.head_dim = descs[0].head_dim; g2.eps = w.ln_eps;
       g2.w = w.w_out; g2.bias = w.b_out;
-      g2.resid_mode = g1.a_mode; g2.resid = g1.a; g2.ids = ids; g2.resid_rowstat = g1.a_rowstat;
+      g2.resid_mode = g1.a_mode; g2.resid = g1.a; g2.ids = ids; g2.id_rows = table_rows; g2.id_err = id_err;
+      g2.resid_rowstat = g1.a_rowstat;
       g2.y32 = last ? nullptr : (float *)(wsb + ws.r32[l % 2]);
       g2.out_stats = last ? nullptr : (float *)(wsb + ws.tstats);
       g2.y = last ? y : nullptr; g2.y_f32 = y_dtype == HSTU_F32;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "row_ids.hpp"
+
 namespace hstu {
 
 #define HSTU_LDS __attribute__((address_space(3)))
@@ -47,6 +49,16 @@ __device__ __forceinline__ floatx16 mfma32(float a, float b, floatx16 c) {
 __device__ __forceinline__ float silu_f32(float s) {
   const float e = __builtin_amdgcn_exp2f(s * -1.4426950408889634f);
   return s * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// A gathered row id clamped into [0, rows); each clamped read adds 1 to *err, the library's
+// per-device id-error word (a vector atomic: the branch is taken only for a bad id).
+__device__ __forceinline__ int64_t checked_row_id(int64_t id, int64_t rows, unsigned int *err) {
+  if (!row_id_in_range(id, rows)) {
+    atomicAdd(err, 1u);
+    id = clamp_row_id(id, rows);
+  }
+  return id;
 }
 
 // Number of significant bits of |a - b| for int64 a, b (exact; the difference fits in uint64).

@@ -85,6 +85,8 @@ struct GemmParams {
   // large-tile kernel only:
   const int64_t *ids;      // gathered rows: A row m (kAkGather) and residual row m (resid_mode 1) are row
                            // ids[m] of a [rows][K] (A) or [rows][N] (residual) bf16 table
+  int64_t id_rows;         // the table's row count: ids are clamped into [0, id_rows)
+  unsigned int *id_err;    // id-error word: +1 per clamped read
   const float *a_rowstat;  // kAkLn: [M][2] (mean, rstd) of A's rows
   int resid_mode;          // 0: resid [M][N]; 1: bf16 table rows resid[ids[m]]; 2: LN of fp32 resid rows
   const float *resid_rowstat;  // resid_mode 2: [M][2] (mean, rstd)
@@ -440,7 +442,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
 #pragma unroll
     for (int t = 0; t < C::kDA; ++t) {
       const int q = wave + t * C::kWaves, g = q / (BM / 16), r = (q % (BM / 16)) * 16 + lrow;
-      const int64_t row = p.ids[m0 + imin(r, a_rows - 1)];
+      const int64_t row = checked_row_id(p.ids[m0 + imin(r, a_rows - 1)], p.id_rows, p.id_err);
       aptr[t] = (const char *)p.a + row * (int64_t)a_rb + (int64_t)kt0 * BK * 2 + g * 64 + lpiece;
     }
   }
@@ -590,7 +592,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
       for (int e = 0; e < 16; ++e) {
         const int m = imin(m0 + wm + 32 * i + 8 * (e / 4) + 4 * half + (e % 4), p.M - 1);
         if (p.resid_mode == 1) {
-          const uint64_t row = (uint64_t)p.ids[m];
+          const uint64_t row = (uint64_t)checked_row_id(p.ids[m], p.id_rows, p.id_err);
           rp0[i][e] = (uint32_t)row;
           rp1[i][e] = (uint32_t)(row >> 32);
         } else if (p.resid_mode == 2) {
@@ -867,7 +869,7 @@ hipError_t launch_gemm_stack_proj(const GemmStackProjArgs &a, hipStream_t s) {
   p.out0 = a.u; p.out1 = a.v; p.out2 = a.q; p.out3 = a.k; p.out32 = nullptr; p.zout = nullptr;
   p.M = a.M; p.N = 4 * a.HD; p.K = a.K; p.HD = a.HD;
   p.splits = 1;
-  p.ids = a.ids; p.a_rowstat = a.a_rowstat;
+  p.ids = a.ids; p.id_rows = a.id_rows; p.id_err = a.id_err; p.a_rowstat = a.a_rowstat;
   if (a.a_mode == 1) return launch_big<CfgGather, kEpiUvqk>(p, s);
   if (a.a_mode == 2) return a.split ? launch_big<CfgLnSplit, kEpiUvqk>(p, s) : launch_big<CfgLn, kEpiUvqk>(p, s);
   return launch_big<CfgBf16, kEpiUvqk>(p, s);
@@ -881,7 +883,8 @@ hipError_t launch_gemm_stack_out(const GemmStackOutArgs &a, hipStream_t s) {
   p.resid_f32 = 0; p.y_f32 = a.y_f32;
   p.gate_u = a.u; p.row_stats = a.row_stats; p.heads = a.heads; p.head_dim = a.head_dim; p.eps = a.eps;
   p.splits = 1;
-  p.resid_mode = a.resid_mode; p.ids = a.ids; p.resid_rowstat = a.resid_rowstat;
+  p.resid_mode = a.resid_mode; p.ids = a.ids; p.id_rows = a.id_rows; p.id_err = a.id_err;
+  p.resid_rowstat = a.resid_rowstat;
   p.out_stats = a.y32 ? a.out_stats : nullptr;
   return a.split ? launch_big<CfgGateSplit, kEpiOutStack>(p, s) : launch_big<CfgGate, kEpiOutStack>(p, s);
 }

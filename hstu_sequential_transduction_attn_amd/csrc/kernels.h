@@ -66,6 +66,9 @@ size_t attn_tau_stats_bytes(int64_t total_tokens, int64_t num_seqs);
 // address on the current device (looked up once per device, then cached).
 constexpr size_t kNoallocScratchBytes = (size_t)1 << 20;
 hipError_t noalloc_scratch(void **ptr);
+// Device address of the current device's id-error word: gathers add 1 for each read whose row id lies
+// outside [0, table_rows) (the read is clamped to the nearest row).
+hipError_t id_error_word(unsigned int **ptr);
 hipError_t launch_attn_fwd(const AttnArgs &a, hipStream_t stream);
 // Causal softmax attention (bf16 inputs, Dh = 128), the comparison point of the pointwise forward:
 // q, k, v, out, row strides, seq_offsets, num_seqs, num_heads, max_seq_len, out_dtype are read.
@@ -149,7 +152,9 @@ int gemm_plain_splits(int64_t M, int64_t N, int64_t K, int dtype, int a_f32);
 struct GemmStackProjArgs {
   int32_t a_mode;
   const void *a;
-  const int64_t *ids;
+  const int64_t *ids;      // a_mode 1: row ids, clamped into [0, id_rows) (each clamp counted in id_err)
+  int64_t id_rows;
+  unsigned int *id_err;
   const float *a_rowstat;
   const void *w, *bias;
   float *u;
@@ -168,7 +173,9 @@ struct GemmStackOutArgs {
   const void *w, *bias;
   int32_t resid_mode;
   const void *resid;
-  const int64_t *ids;
+  const int64_t *ids;      // resid_mode 1: row ids, clamped into [0, id_rows) (each clamp counted in id_err)
+  int64_t id_rows;
+  unsigned int *id_err;
   const float *resid_rowstat;
   float *y32, *out_stats;
   void *y;

@@ -1,10 +1,14 @@
 // Row-wise, HBM-bound kernels of the HSTU layer on gfx950.
 //
 //  * row_layernorm:  y_t = LN(y32_t) between stacked layers (LayerNorm with biased variance, no affine).
-//  * gather_rows:    x_t = E[id_t], the embedding lookup that stages the first layer's input.
+//  * gather_rows:    x_t = E[id_t], the embedding lookup that stages the first layer's input.  An id
+//                    outside [0, table_rows) is clamped to the nearest row and counted in the
+//                    per-device id-error word (read back through hstu_id_errors).
 //
 // One wave per row; each lane keeps its slice of the row in registers, so the row is read from HBM
 // exactly once and the statistics take two passes over registers (mean, then centred squares).
+#include <mutex>
+
 #include "device_common.hpp"
 #include "kernels.h"
 
@@ -65,13 +69,14 @@ __global__ void __launch_bounds__(256) row_ln_kernel(const float *__restrict__ i
 }
 
 __global__ void __launch_bounds__(256) gather_kernel(const u32x4 *__restrict__ table, const int64_t *__restrict__ ids,
-                                                     u32x4 *__restrict__ out, int T, int chunks_per_row) {
+                                                     u32x4 *__restrict__ out, int T, int chunks_per_row, int64_t rows,
+                                                     unsigned int *__restrict__ err) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)T * chunks_per_row;
   if (i >= total) return;
   const int64_t t = i / chunks_per_row;
   const int c = (int)(i % chunks_per_row);
-  out[i] = table[ids[t] * chunks_per_row + c];
+  out[i] = table[checked_row_id(ids[t], rows, err) * chunks_per_row + c];
 }
 
 // Chan's pairwise combination of per-tile (mean, M2) in tile order; one thread per row.
@@ -121,13 +126,42 @@ hipError_t launch_row_stats_combine(const float *tile_stats, float *rowstat, int
 
 hipError_t launch_gather_rows(const void *table, int64_t table_rows, int32_t row_bytes, const int64_t *ids, int32_t T,
                               void *out, hipStream_t s) {
-  (void)table_rows;
   if (T == 0) return hipSuccess;
+  unsigned int *err = nullptr;
+  hipError_t e = id_error_word(&err);
+  if (e != hipSuccess) return e;
   const int cpr = row_bytes / 16;
   const int64_t total = (int64_t)T * cpr;
   const dim3 grid((unsigned)((total + 255) / 256));
-  hipLaunchKernelGGL(gather_kernel, grid, dim3(256), 0, s, (const u32x4 *)table, ids, (u32x4 *)out, T, cpr);
+  hipLaunchKernelGGL(gather_kernel, grid, dim3(256), 0, s, (const u32x4 *)table, ids, (u32x4 *)out, T, cpr,
+                     table_rows, err);
   return hipGetLastError();
+}
+
+// The per-device id-error word: a file-scope device variable whose device address is looked up once
+// per device (with that device current) and kept; host code never passes the variable's own name.
+namespace {
+static __device__ __align__(256) unsigned int id_errors;
+constexpr int kMaxIdDevices = 64;
+std::once_flag g_id_once[kMaxIdDevices];
+unsigned int *g_id_ptr[kMaxIdDevices];
+hipError_t g_id_err[kMaxIdDevices];
+}  // namespace
+
+hipError_t id_error_word(unsigned int **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxIdDevices) return hipErrorInvalidDevice;
+  std::call_once(g_id_once[dev], [dev] {
+    void *p = nullptr;
+    g_id_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(id_errors));
+    g_id_ptr[dev] = g_id_err[dev] == hipSuccess ? (unsigned int *)p : nullptr;
+  });
+  if (g_id_err[dev] != hipSuccess) return g_id_err[dev];
+  if (!g_id_ptr[dev]) return hipErrorInvalidSymbol;
+  *ptr = g_id_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace hstu

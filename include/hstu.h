@@ -38,7 +38,7 @@
  *    returns HSTU_ERR_DEVICE with the HIP error text.
  *  - Device-resident content is the caller's contract and is not validated on the hot path:
  *    offsets must be non-decreasing from 0 to total_tokens, 0 <= num_candidates[b] <= n_b,
- *    and ids must be < table_rows.
+ *    and ids must be in [0, table_rows) (an id outside is clamped and counted: hstu_id_errors).
  *  - Outputs are bitwise deterministic for identical inputs on one device (no float atomics).
  */
 #ifndef HSTU_H_
@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 8
+#define HSTU_ABI_VERSION 9
 
 typedef enum {
   HSTU_OK = 0,
@@ -287,7 +287,8 @@ size_t hstu_stack_workspace_bytes(const hstu_jagged_t *jag, const hstu_attn_desc
  *   x_{l+1} = LN(x_l + branch_l(x_l)) for l < num_layers - 1,   y = x_L-1 + branch_L-1(x_L-1),
  * with branch_l the layer of hstu_layer_fwd (weights[l], descs[l]; weights[l].ln_output is not read).
  * Every layer has the same jag, d_model, num_heads, head_dim and mask; tables and weights are per layer.
- * table: [table_rows][D] dtype (device); ids: [T] int64 in [0, table_rows) (device) or NULL (then
+ * table: [table_rows][D] dtype (device); ids: [T] int64 in [0, table_rows) (device; an id outside is
+ * clamped to the nearest row and counted, as in hstu_gather_rows) or NULL (then
  * table_rows >= T); y: [T][D], y_dtype in {HSTU_F32, dtype} (device), may not overlap the table.
  * bf16 with large-tile shapes: the gather is done by layer 0's projection and output GEMMs while they
  * load their operands (x_0 is never stored); each output GEMM before a LayerNorm writes its fp32 sum
@@ -383,9 +384,23 @@ hstu_status_t hstu_layer_bwd_saved(const hstu_jagged_t *jag, const hstu_attn_des
  * 約560GBへ拡大" -- the tables those ids index (512-wide rows in the benchmark).
  * table: [table_rows][d] (device); ids: [T] int64 (device), each in [0, table_rows);
  * out: [T][d] (device).  Element type `dtype`; d * element size must be a multiple of 16 bytes.
+ * An id outside [0, table_rows) reads the nearest row (0 or table_rows - 1) instead of memory past the
+ * table, and the read is counted in the device's id-error word (hstu_id_errors).
  */
 hstu_status_t hstu_gather_rows(const void *table, int64_t table_rows, int32_t d, hstu_dtype_t dtype,
                                const int64_t *ids, int32_t T, void *out, void *stream);
+
+/*
+ * Out-of-range row ids met by the gathers (hstu_gather_rows, and hstu_stack_fwd with ids) on the
+ * current device since the library was loaded or last reset.  Not an operation of the method: the
+ * gathers run asynchronously and cannot return an error for a bad id, so each read whose id lies
+ * outside [0, table_rows) is clamped to the nearest row and adds 1 to a per-device word, which the
+ * caller reads here when convenient.  *count (host) receives the word: 0 means no bad id; otherwise
+ * the number of clamped reads (one bad id may be read several times).  Waits for `stream` first;
+ * with reset != 0 the word is set back to 0.  Calls that gather concurrently on the device add to the
+ * same word.  Errors: count NULL -> HSTU_ERR_INVALID_ARGUMENT; a failing HIP call -> HSTU_ERR_DEVICE.
+ */
+hstu_status_t hstu_id_errors(uint32_t *count, int32_t reset, void *stream);
 
 #ifdef __cplusplus
 }

@@ -39,7 +39,7 @@ def _attn(jag, desc, in_dt=L.HSTU_BF16, out_dt=L.HSTU_BF16, q=P16 + 0x10000, k=P
 
 def test_exports_every_declared_symbol():
     names = L.exported_functions_in_header()
-    assert len(names) == 21
+    assert len(names) == 22
     lib = ctypes.CDLL(L.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib()
-    assert lib.hstu_abi_version() == 8
+    assert lib.hstu_abi_version() == 9
     assert lib.hstu_status_string(OK) == b"HSTU_OK"
     assert lib.hstu_status_string(WS_SMALL) == b"HSTU_ERR_WORKSPACE_TOO_SMALL"
     assert lib.hstu_status_string(99) == b"HSTU_STATUS_UNKNOWN"
@@ -438,3 +438,9 @@ def test_softmax_attn_argument_checks():
     st, msg = call(_jag(), out=P16 + 0x10000 + 64)
     assert st == INVALID and "overlaps" in msg
     assert call(L.JaggedT(3, 0, 0, P16, None, None, None), q=None, k=None, v=None, out=None) == (OK, "")
+
+
+def test_id_errors_rejects_a_null_count_before_touching_the_device():
+    lib = _lib()
+    assert lib.hstu_id_errors(None, 1, None) == INVALID
+    assert "count" in lib.hstu_last_error().decode()
