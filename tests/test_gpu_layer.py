@@ -26,7 +26,8 @@ def test_tiny_layer_f32_full():
     print("\n[case] tiny_layer_f32 (config 1)", flush=True)
     case = C.tiny_layer_f32()
     got = host(gpu_layer_stack(case))
-    assert_close(got, _oracle_stack(case), "f32", "tiny layer f32")
+    r, m = assert_close(got, _oracle_stack(case), "f32", "tiny layer f32")
+    print(f"  rel_l2={r:.3e} max_abs={m:.3e}")
 
 
 def test_layer_bf16_full():
