@@ -15,6 +15,7 @@ constexpr int kBM = kWaves * kQW;        // queries per workgroup
 constexpr int kBN = 64;                  // keys per LDS tile
 constexpr int kThreads = kWaves * kWave;
 constexpr int kTimeTab = 65;             // a 64-bit gap has bit length 0..64
+constexpr int kPosPad = 8;               // forward: position-table entries past P - 1 (copies of w_p[P-1])
 constexpr int kChunk = 32;               // tokens per timestamp-range chunk
 constexpr int kRingBudget = 68 * 1024;   // LDS for the stage ring: two workgroups per CU
 constexpr float kNegLog2e = -1.4426950408889634f;

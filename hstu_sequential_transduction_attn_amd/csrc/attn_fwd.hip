@@ -72,6 +72,13 @@ __device__ __forceinline__ uint32_t absdiff_u32(uint32_t a, uint32_t b) {
 // Per-score bias and mask of a non-uniform tile, added to the 16 scores of 32-key block kb (held as
 // separate floats, so that the adjusted values stay in the scores' registers); element e holds key
 // k0 + 32*kb + 16*(e/8) + 8*half + e%8.
+// The forward's tables are padded so that no bucket needs a clamp: wp[d] = w_p[min(d, P-1)] for
+// d < P + kPosPad and wt[b] = w_t[min(b, Tb-1)] for every bit length b <= 64.  In a tile whose keys
+// are all allowed, all history and no later than the query's position, the 8 keys of a lane's group
+// have position distances d0 - e8 (d0 = my_pos - first key), so their biases are the 8 consecutive
+// entries wp[d0 - 7 .. d0]; with d0 capped at P + 6 the window stays in the table and, past P - 1,
+// reads w_p[P-1] for every key, as the clamp would.  In a masked tile the same holds for every allowed
+// key but a candidate's own (distance 0).
 template <typename T, int DH, int MODE>
 __device__ __forceinline__ void adjust_scalar(float (&s)[16], const TileCtx &c, int kb, int half) {
   using L = Layout<T, DH>;
@@ -86,6 +93,7 @@ __device__ __forceinline__ void adjust_scalar(float (&s)[16], const TileCtx &c, 
       const u32x4 w = *(const HSTU_LDS u32x4 *)(c.stage + L::tau_at(jl0 + 2 * q));
       lo[2 * q] = w.x; hi[2 * q] = w.y; lo[2 * q + 1] = w.z; hi[2 * q + 1] = w.w;
     }
+    const HSTU_LDS float *wpw = c.wp + (imin(c.my_pos - (c.k0 + jl0), c.P + kPosPad - 2) - 7);
 #pragma unroll
     for (int e8 = 0; e8 < 8; ++e8) {
       const int e = 8 * g + e8;
@@ -97,10 +105,14 @@ __device__ __forceinline__ void adjust_scalar(float (&s)[16], const TileCtx &c, 
       } else if constexpr (MODE == kTwo) {
         bias = absdiff_u32(c.qoff, lo[e8] - c.base_lo) >= c.thr ? c.bias_hi : c.bias_lo;
       } else {
-        const int j = c.k0 + jl0 + e8;
-        const int pj = imin(j, c.pos_lim);
-        const uint32_t dp = absdiff_u32((uint32_t)c.my_pos, (uint32_t)pj);
-        const int bp = (int)(dp < (uint32_t)(c.P - 1) ? dp : (uint32_t)(c.P - 1));
+        float wpv = wpw[7 - e8];
+        if constexpr (kMasked) {
+          // an allowed key other than the query itself is a history key no later than the query's
+          // position, where the window holds; a candidate's own key has distance 0 (both at n_h); the
+          // window's value for a masked key is never used (its window may start below the table, inside
+          // the stage ring)
+          if (c.k0 + jl0 + e8 == c.my_q) wpv = c.wp[0];
+        }
         int bt;
         if constexpr (!k64) {
           bt = bitlen_u32(absdiff_u32(c.qoff, lo[e8] - c.base_lo));
@@ -108,8 +120,7 @@ __device__ __forceinline__ void adjust_scalar(float (&s)[16], const TileCtx &c, 
           const int64_t tj = (int64_t)(((uint64_t)hi[e8] << 32) | lo[e8]);
           bt = bitlen_absdiff(c.my_tau, tj);
         }
-        bt = imin(bt, c.Tb - 1);
-        bias = c.wp[bp] + c.wt[bt];
+        bias = wpv + c.wt[bt];
       }
       if constexpr (kMasked) {
         const int j = c.k0 + jl0 + e8;
@@ -462,11 +473,12 @@ __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_
   const int half = lane >> 5;
 
   // ---- bias tables into LDS (after the stage ring)
+  // forward: both tables padded with their last entry (no bucket clamp in the per-score bias, see
+  // adjust_scalar); the dQ pass reads entries below P and Tb only
   HSTU_LDS float *wp_lds = (HSTU_LDS float *)(smem + L::kStages * L::kStageBytes);
-  HSTU_LDS float *wt_lds = wp_lds + P;
-  for (int i = tid; i < P; i += kThreads) wp_lds[i] = p.pos_bias[(int64_t)rr * P + i];
-  const int nt_tab = imin(Tb, kTimeTab);
-  for (int i = tid; i < nt_tab; i += kThreads) wt_lds[i] = p.time_bias[(int64_t)rr * Tb + i];
+  HSTU_LDS float *wt_lds = wp_lds + P + (BWD ? 0 : kPosPad);
+  for (int i = tid; i < P + (BWD ? 0 : kPosPad); i += kThreads) wp_lds[i] = p.pos_bias[(int64_t)rr * P + imin(i, P - 1)];
+  for (int i = tid; i < kTimeTab; i += kThreads) wt_lds[i] = p.time_bias[(int64_t)rr * Tb + imin(i, Tb - 1)];
 
   // ---- this wave's queries
   const int qr = q0 + wave * kQW;                 // first query row of the wave (a multiple of 32)
@@ -842,7 +854,7 @@ attn_bwd_dq_kernel(const AttnArgs p, const int n_qblocks) {
 template <typename T, int DH, bool BWD>
 size_t attn_lds_bytes(int num_pos_buckets) {
   using L = Layout<T, DH>;
-  const size_t tables = (size_t)(num_pos_buckets + kTimeTab) * sizeof(float);
+  const size_t tables = (size_t)(num_pos_buckets + (BWD ? 0 : kPosPad) + kTimeTab) * sizeof(float);
   return (size_t)L::kStages * L::kStageBytes + tables * (BWD ? 1 + kWaves : 1);
 }
 
