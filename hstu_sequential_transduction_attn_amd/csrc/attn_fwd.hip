@@ -93,7 +93,10 @@ __device__ __forceinline__ void adjust_scalar(float (&s)[16], const TileCtx &c, 
       const u32x4 w = *(const HSTU_LDS u32x4 *)(c.stage + L::tau_at(jl0 + 2 * q));
       lo[2 * q] = w.x; hi[2 * q] = w.y; lo[2 * q + 1] = w.z; hi[2 * q + 1] = w.w;
     }
-    const HSTU_LDS float *wpw = c.wp + (imin(c.my_pos - (c.k0 + jl0), c.P + kPosPad - 2) - 7);
+    // masked tiles: a group whose keys are all past the position reads its (unused) window from just
+    // below the table, inside the stage ring, wherever the position is
+    const int d0 = imin(c.my_pos - (c.k0 + jl0), c.P + kPosPad - 2);
+    const HSTU_LDS float *wpw = c.wp + (kMasked ? imax(d0, -1) : d0) - 7;
 #pragma unroll
     for (int e8 = 0; e8 < 8; ++e8) {
       const int e = 8 * g + e8;
@@ -109,8 +112,7 @@ __device__ __forceinline__ void adjust_scalar(float (&s)[16], const TileCtx &c, 
         if constexpr (kMasked) {
           // an allowed key other than the query itself is a history key no later than the query's
           // position, where the window holds; a candidate's own key has distance 0 (both at n_h); the
-          // window's value for a masked key is never used (its window may start below the table, inside
-          // the stage ring)
+          // window's value for a masked key is never used
           if (c.k0 + jl0 + e8 == c.my_q) wpv = c.wp[0];
         }
         int bt;

@@ -686,9 +686,10 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
   if constexpr (EPI == kEpiOutStack) {
     if (p.out_stats) {
       constexpr int kParts = C::WN * 32;
-      static_assert(BM * (kParts + 1) * 4 <= C::kLds, "row statistics fit in the LDS ring");
-      HSTU_LDS float *red = (HSTU_LDS float *)smem;    // [BM][kParts]
-      HSTU_LDS float *rmean = red + BM * kParts;       // [BM]
+      constexpr int kStride = kParts + 1;   // a padded row: the per-row sums below read down a column
+      static_assert(BM * (kStride + 1) * 4 <= C::kLds, "row statistics fit in the LDS ring");
+      HSTU_LDS float *red = (HSTU_LDS float *)smem;    // [BM][kStride]
+      HSTU_LDS float *rmean = red + BM * kStride;      // [BM]
       const int cnt = imin(BN, p.N - n0);
       const int wn_i = wave % C::WN;
       float mean_r[FM][16];
@@ -706,12 +707,12 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
               const float d = pass == 0 ? acc[i][j][e] : acc[i][j][e] - mean_r[i][e];
               v += ok ? (pass == 0 ? d : d * d) : 0.0f;
             }
-            red[row * kParts + wn_i * 32 + l32] = v;
+            red[row * kStride + wn_i * 32 + l32] = v;
           }
         __syncthreads();
         if (tid < BM) {
           float sum = 0.0f;
-          for (int q = 0; q < kParts; ++q) sum += red[tid * kParts + q];
+          for (int q = 0; q < kParts; ++q) sum += red[tid * kStride + q];
           if (pass == 0) {
             rmean[tid] = sum / (float)cnt;
           } else {
