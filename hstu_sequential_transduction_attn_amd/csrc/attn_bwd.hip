@@ -381,13 +381,9 @@ hipError_t launch_dkdv_typed(const AttnArgs &a, hipStream_t stream) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const size_t lds = dkdv_lds_bytes<T, DH>(a.num_pos_buckets);
   if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)attn_bwd_dkdv_kernel<T, DH>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static LdsLimit lim;
+  hipError_t e = lim.raise((const void *)attn_bwd_dkdv_kernel<T, DH>, 160 * 1024);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DH>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a, n_kblocks);
   return hipGetLastError();
 }

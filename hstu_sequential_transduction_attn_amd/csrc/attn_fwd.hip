@@ -903,12 +903,11 @@ hipError_t launch_typed(const AttnArgs &a, hipStream_t stream) {
     }
     return hipSuccess;
   }
-  static bool attr_set = false;
-  if (!attr_set) {
+  static LdsLimit lim;
+  {
     const void *fn = BWD ? (const void *)attn_bwd_dq_kernel<T, DH> : (const void *)attn_fwd_kernel<T, DH, TO, CACHED>;
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipError_t e = lim.raise(fn, 160 * 1024);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   launch_tau_stats(a.seq_offsets, a.timestamps, a.tau_stats, a.num_seqs, a.num_rows_total, stream);
   if constexpr (CACHED)

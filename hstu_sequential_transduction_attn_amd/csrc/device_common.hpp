@@ -5,9 +5,27 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "row_ids.hpp"
 
 namespace hstu {
+
+// Host side: a kernel's dynamic-LDS limit, raised once per device (function attributes are kept per
+// device) and safely when several host threads launch at once.  One static instance per kernel.
+struct LdsLimit {
+  static constexpr int kMaxDevices = 64;
+  std::once_flag once[kMaxDevices];
+  hipError_t err[kMaxDevices] = {};
+  hipError_t raise(const void *fn, int bytes) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(once[dev], [&] { err[dev] = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes); });
+    return err[dev];
+  }
+};
 
 #define HSTU_LDS __attribute__((address_space(3)))
 

@@ -740,12 +740,10 @@ __global__ void __launch_bounds__(C::kThreads, C::kOcc) gemm_big_kernel(const Ge
 template <class C, int EPI>
 hipError_t launch_big(const GemmParams &p0, hipStream_t s) {
   if (p0.M == 0 || p0.N == 0) return hipSuccess;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_big_kernel<C, EPI>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+  static LdsLimit lim;
+  {
+    hipError_t e = lim.raise((const void *)gemm_big_kernel<C, EPI>, C::kLds);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   GemmParams p = p0;
   p.splits = p.splits > 1 ? p.splits : 1;

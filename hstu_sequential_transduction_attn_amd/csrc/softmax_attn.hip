@@ -162,12 +162,10 @@ hipError_t launch_softmax_typed(const AttnArgs &a, hipStream_t stream) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (grid == 0) return hipSuccess;
   const size_t lds = 2 * (size_t)Layout<__bf16, 128>::kStageBytes;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)softmax_attn_kernel<TO>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  static LdsLimit lim;
+  {
+    hipError_t e = lim.raise((const void *)softmax_attn_kernel<TO>, 160 * 1024);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   hipLaunchKernelGGL(softmax_attn_kernel<TO>, dim3((unsigned)grid), dim3(kThreads), lds, stream, a, n_qblocks);
   return hipGetLastError();
