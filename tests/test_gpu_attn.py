@@ -212,3 +212,27 @@ def test_tiny_bias_tables(P, Tb):
     cc = I.attn_case("tinyc", 1510 + P + Tb, [400, 90], H=2, Dh=64, P=P, Tb=Tb, dtype="bf16",
                      num_candidates=[70, 30])
     assert_close(host(gpu_attn(cc)), _oracle(cc), "bf16", f"candidates P={P} Tb={Tb}", magnitude_aware=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_candidate_block_far_longer_than_its_history(dtype):
+    """Users whose candidate block is much longer than their history (up to 20,000 candidates after 300
+    history events), with small tables: a candidate's diagonal tile then sits thousands of positions past
+    its own position n_h, where the per-score position bias of the masked tiles is read from a window
+    that starts far below the table.  Sampled candidate rows (every 97th, the first and the last) and
+    all history rows against the oracle."""
+    print(f"\n[case] long candidate blocks {dtype}", flush=True)
+    lengths = [300 + 20000, 1 + 5000, 2048 + 64]
+    cands = [20000, 5000, 64]
+    case = I.attn_case("longcand", 1520, lengths, H=2, Dh=64, P=4, Tb=8, dtype=dtype, num_candidates=cands)
+    got = host(gpu_attn(case, out_dtype=torch.float32))
+    rows = {}
+    for b, (n, m) in enumerate(zip(lengths, cands)):
+        nh = n - m
+        rows[b] = np.unique(np.concatenate([np.arange(nh), np.arange(nh, n, 97), [nh, n - 1]]))
+    want = _oracle(case, row_sample=rows)
+    offs = case.jagged.seq_offsets
+    g = np.concatenate([got[offs[b] + rows[b], h] for b in range(len(lengths)) for h in range(2)])
+    w = np.concatenate([want[(b, h)] for b in range(len(lengths)) for h in range(2)])
+    r, mx = assert_close(g, w, dtype, f"long candidate blocks {dtype}", magnitude_aware=dtype == "bf16")
+    print(f"  {len(g)} rows: rel_l2={r:.3e} max_abs={mx:.3e}")
