@@ -789,6 +789,9 @@ using CfgGateSplit = BigCfg<64, 256, 32, 2, 2, 2, kAkGate, 2, 4, 2>;
 using CfgGather = BigCfg<128, 256, 32, 2, 2, 2, kAkGather, 1, 4, 2>;
 using CfgLn = BigCfg<128, 256, 32, 2, 2, 2, kAkLn, 1, 8, 2>;
 using CfgLnSplit = BigCfg<128, 256, 32, 2, 2, 2, kAkLn, 2, 8, 2>;
+// bf16 operands on a small problem (fewer than 1024 tiles of 128 x 256, about two rounds of the 512
+// workgroup slots): narrower tiles, twice as many workgroups (config-2 projection: 60 -> 49 us)
+using CfgBf16N = BigCfg<128, 128, 32, 2, 2, 2, kAkBf16, 1, 4, 2>;
 
 // The large-tile kernel needs K to be a whole number of k-tiles, per-lane source offsets (row within
 // the tile times the row's bytes) that fit 32 bits, and enough tiles to fill the chip.
@@ -803,6 +806,11 @@ bool big_fits(const GemmParams &p) {
   return p.K % C::BK == 0 && tiles >= 256 && offsets_fit<C>(p.K);
 }
 
+template <class C>
+long long big_tiles(const GemmParams &p) {
+  return (long long)((p.N + C::BN - 1) / C::BN) * ((p.M + C::BM - 1) / C::BM);
+}
+
 template <int EPI, bool GATE>
 hipError_t dispatch(const GemmParams &p, int dtype, int a_f32, int split, hipStream_t s) {
   if (dtype == kF32) return launch<float, float, 1, EPI, GATE>(p, s);
@@ -812,6 +820,7 @@ hipError_t dispatch(const GemmParams &p, int dtype, int a_f32, int split, hipStr
   } else {
     if (a_f32 && split && big_fits<CfgF32Split>(p)) return launch_big<CfgF32Split, EPI>(p, s);
     if (a_f32 && !split && big_fits<CfgF32>(p)) return launch_big<CfgF32, EPI>(p, s);
+    if (!a_f32 && big_tiles<CfgBf16>(p) < 1024 && big_fits<CfgBf16N>(p)) return launch_big<CfgBf16N, EPI>(p, s);
     if (!a_f32 && big_fits<CfgBf16>(p)) return launch_big<CfgBf16, EPI>(p, s);
   }
   if constexpr (!GATE) {
