@@ -37,7 +37,7 @@ METRIC = "HSTU attn fwd TFLOP/s (causal, jagged) at L=8192 bf16; % MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_L8192_traffic.json")
 # every source the attention forward kernel is compiled from (its traffic figure is void once any changes)
 KERNEL_SOURCES = [os.path.join(ROOT, "hstu_sequential_transduction_attn_amd", "csrc", f)
-                  for f in ("attn_fwd.hip", "attn_common.hpp", "device_common.hpp", "row_ids.hpp", "kernels.h")]
+                  for f in ("attn_fwd.hip", "attn_common.hpp", "device_common.hpp", "row_ids.hpp", "work_order.hpp", "kernels.h")]
 
 
 def kernel_source_hash() -> str:

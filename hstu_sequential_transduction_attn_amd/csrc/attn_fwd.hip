@@ -56,6 +56,7 @@
 // 16-wide accumulator value would make the register allocator copy the whole block at the class merge,
 // on every path.  The output accumulators never change registers between classes.
 #include "attn_common.hpp"
+#include "work_order.hpp"
 
 namespace hstu {
 namespace {
@@ -424,7 +425,8 @@ __global__ void __launch_bounds__(256) attn_split_reduce_kernel(const AttnArgs p
 // adds them in split order.
 //
 // BWD: the dQ pass of the backward (bwd_tile_body); out is dQ (fp32) and each workgroup writes its
-// bias-gradient bins (times c_b) to row blockIdx.x of `partial`.
+// bias-gradient bins (times c_b) to row canonical_item(...) of `partial` (the item's place in query-block-major
+// order, whatever order the items run in).
 template <typename T, int DH, typename TO, bool CACHED, bool BWD>
 __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_qblocks) {
   using L = Layout<T, DH>;
@@ -433,13 +435,16 @@ __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_
   HSTU_LDS char *smem = (HSTU_LDS char *)smem_raw;
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
-  // ---- work item: query block major (longest first), then (sequence, head); cached: key split fastest
+  // ---- work item: the XCD-local order of work_order.hpp; cached: query block major (longest first),
+  // then (sequence, head), key split fastest
   const int HB = p.num_heads * p.num_seqs;
   const int split = CACHED ? (int)(blockIdx.x % (unsigned)p.kv_splits) : 0;
   const int item = CACHED ? (int)(blockIdx.x / (unsigned)p.kv_splits) : (int)blockIdx.x;
-  const int qblk = n_qblocks - 1 - item / HB;
-  const int b = (item % HB) / p.num_heads;
-  const int h = (item % HB) % p.num_heads;
+  const WorkItem wi = CACHED ? WorkItem{n_qblocks - 1 - item / HB, item % HB} : work_item(item, HB, n_qblocks);
+  const int qblk = wi.qblk;
+  const int b = wi.pair / p.num_heads;
+  const int h = wi.pair % p.num_heads;
+  [[maybe_unused]] const int64_t bins_row = canonical_item(wi, HB, n_qblocks);   // backward: its row of `partial`
   // o0/nq: first row and count of this sequence's query rows; ho/nh: first key row and history length;
   // vq0: local (virtual-sequence) index of query row 0; n: virtual sequence length
   const int o0 = p.seq_offsets[b];
@@ -448,7 +453,7 @@ __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_
   const int nbins = p.num_pos_buckets + kTimeTab;  // backward: bias-gradient bins per wave
   if (q0 >= nq) {        // uniform over the workgroup
     if constexpr (BWD)
-      for (int i = threadIdx.x; i < nbins; i += kThreads) p.partial[(int64_t)blockIdx.x * nbins + i] = 0.0f;
+      for (int i = threadIdx.x; i < nbins; i += kThreads) p.partial[bins_row * nbins + i] = 0.0f;
     return;
   }
   const bool cand = CACHED || p.mask == kCausalCandidates;
@@ -756,7 +761,7 @@ __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_
     const HSTU_LDS float *h0 = wt_lds + kTimeTab;
     for (int i = tid; i < nbins; i += kThreads) {
       const float v = ((h0[i] + h0[nbins + i]) + h0[2 * nbins + i]) + h0[3 * nbins + i];
-      p.partial[(int64_t)blockIdx.x * nbins + i] = v * cb;
+      p.partial[bins_row * nbins + i] = v * cb;
     }
     return;
   }
