@@ -21,6 +21,7 @@
 // 256 registers, and the loop keeps nothing else across tiles that can be rebuilt (see KeyCtx), so
 // nothing spills (a reload from scratch would also wait for the next tile's direct-to-LDS prefetch).
 #include "attn_common.hpp"
+#include "work_order.hpp"
 
 namespace hstu {
 namespace {
@@ -163,12 +164,13 @@ attn_bwd_dkdv_kernel(const AttnArgs p, const int n_kblocks) {
   HSTU_LDS char *smem = (HSTU_LDS char *)smem_raw;
   const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
-  // ---- work item: key block (first keys first: they see the most queries), then (sequence, head)
+  // ---- work item: the XCD-local order of work_order.hpp; rank 0 is the first key block (it sees the
+  // most queries)
   const int HB = p.num_heads * p.num_seqs;
-  const int item = blockIdx.x;
-  const int kblk = item / HB;
-  const int b = (item % HB) / p.num_heads;
-  const int h = (item % HB) % p.num_heads;
+  const WorkItem wi = work_item((int)blockIdx.x, HB, n_kblocks);
+  const int kblk = wi.rank;
+  const int b = wi.pair / p.num_heads;
+  const int h = wi.pair % p.num_heads;
   const int o0 = p.seq_offsets[b];
   const int n = p.seq_offsets[b + 1] - o0;
   const int k0 = kblk * kBM;

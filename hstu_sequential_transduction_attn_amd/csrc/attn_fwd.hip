@@ -440,11 +440,11 @@ __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_
   const int HB = p.num_heads * p.num_seqs;
   const int split = CACHED ? (int)(blockIdx.x % (unsigned)p.kv_splits) : 0;
   const int item = CACHED ? (int)(blockIdx.x / (unsigned)p.kv_splits) : (int)blockIdx.x;
-  const WorkItem wi = CACHED ? WorkItem{n_qblocks - 1 - item / HB, item % HB} : work_item(item, HB, n_qblocks);
-  const int qblk = wi.qblk;
+  const WorkItem wi = CACHED ? WorkItem{item / HB, item % HB} : work_item(item, HB, n_qblocks);
+  const int qblk = n_qblocks - 1 - wi.rank;
   const int b = wi.pair / p.num_heads;
   const int h = wi.pair % p.num_heads;
-  [[maybe_unused]] const int64_t bins_row = canonical_item(wi, HB, n_qblocks);   // backward: its row of `partial`
+  [[maybe_unused]] const int64_t bins_row = canonical_item(wi, HB);   // backward: its row of `partial`
   // o0/nq: first row and count of this sequence's query rows; ho/nh: first key row and history length;
   // vq0: local (virtual-sequence) index of query row 0; n: virtual sequence length
   const int o0 = p.seq_offsets[b];
