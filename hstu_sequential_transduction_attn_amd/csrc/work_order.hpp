@@ -10,11 +10,13 @@
 // at a time, the more of those reads its L2 serves.  When the pairs divide evenly among the XCDs
 // (HB = 8 PX), XCD x takes pairs x, x + 8, ..., x + 8 (PX - 1) and runs them in groups, longest block
 // first (rank order) inside each group:
-//   - the first two pairs together and the last two pairs together: a lone pair's longest blocks would
-//     start late at the end (and set the kernel's end) and leave the XCD half filled at the start;
+//   - its first g pairs together and its last g pairs together, g = max(2, ceil(128 / nb)) for nb blocks
+//     per pair: the groups at the ends fill the XCD's 64 workgroup slots at the start and let the last
+//     long blocks start early enough at the end (a lone last pair's longest blocks would set the
+//     kernel's end); the fewer blocks a pair has, the more pairs that takes;
 //   - every pair in between alone.
-// With PX <= 3 the XCD runs all its pairs as one group, and when HB is not a multiple of 8 the items
-// go rank major over all pairs: both are the order of a single group.
+// With fewer than 2 g pairs per XCD, or pairs that do not divide by 8, the items go rank major over all
+// pairs: the order of a single group.
 #pragma once
 
 namespace hstu {
@@ -28,19 +30,20 @@ struct WorkItem {
 // item in [0, HB * nb); HB = number of (sequence, head) pairs, nb = blocks per pair
 constexpr WorkItem work_item(int item, int HB, int nb) {
   const int PX = HB >> 3;
-  if ((HB & 7) != 0 || PX <= 3) return WorkItem{item / HB, item % HB};
+  const int g = (128 + nb - 1) / nb < 2 ? 2 : (128 + nb - 1) / nb;   // pairs in each end group
+  if ((HB & 7) != 0 || PX < 2 * g) return WorkItem{item / HB, item % HB};
   const int x = item & 7, j = item >> 3;
-  const int e0 = 2 * nb, e1 = (PX - 2) * nb;   // end of the first group, start of the last
+  const int e0 = g * nb, e1 = (PX - g) * nb;   // end of the first group, start of the last
   int rank = 0, pr = 0;
   if (j < e0) {
-    rank = j / 2;
-    pr = j % 2;
+    rank = j / g;
+    pr = j % g;
   } else if (j < e1) {
-    pr = 2 + (j - e0) / nb;
+    pr = g + (j - e0) / nb;
     rank = (j - e0) % nb;
   } else {
-    rank = (j - e1) / 2;
-    pr = PX - 2 + (j - e1) % 2;
+    rank = (j - e1) / g;
+    pr = PX - g + (j - e1) % g;
   }
   return WorkItem{rank, x + 8 * pr};
 }

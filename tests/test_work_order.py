@@ -70,18 +70,29 @@ def _order(exe, HB, nqb):
     return [tuple(int(v) for v in ln.split()) for ln in lines if ln.strip()]
 
 
-def test_groups_listed(exe):
-    """HB = 40 pairs (5 per XCD), 3 blocks each: XCD 3 runs pairs 3, 11 interleaved (rank 0, the longest
-    block, first), then 19 alone, then 27 and 35 interleaved."""
-    order = _order(exe, 40, 3)
-    xcd3 = [(r, p) for i, r, p in order if i % 8 == 3]
-    assert xcd3 == [(0, 3), (0, 11), (1, 3), (1, 11), (2, 3), (2, 11),
-                    (0, 19), (1, 19), (2, 19),
-                    (0, 27), (0, 35), (1, 27), (1, 35), (2, 27), (2, 35)]
+def _expected_xcd_order(x, PX, nb):
+    """The groups the header describes, for XCD x: g = max(2, ceil(128 / nb)) pairs at each end run together
+    (rank by rank, the group's pairs in turn), every pair in between alone (rank by rank)."""
+    g = max(2, -(-128 // nb))
+    if PX < 2 * g:
+        groups = [list(range(PX))]
+    else:
+        groups = [list(range(g))] + [[p] for p in range(g, PX - g)] + [list(range(PX - g, PX))]
+    return [(r, x + 8 * p) for grp in groups for r in range(nb) for p in grp]
+
+
+@pytest.mark.parametrize("PX,nb", [(5, 64), (9, 32), (40, 8), (7, 3), (4, 64), (64, 72)])
+def test_groups_listed(exe, PX, nb):
+    """Each XCD's list of items follows the end-group rule (e.g. 5 pairs of 64 blocks: the first two
+    interleaved, the middle one alone, the last two interleaved; 9 pairs of 32 blocks: groups of 4)."""
+    order = _order(exe, 8 * PX, nb)
+    for x in (0, 3, 7):
+        assert [(r, p) for i, r, p in order if i % 8 == x] == _expected_xcd_order(x, PX, nb), (PX, nb, x)
 
 
 def test_few_pairs_keep_rank_major(exe):
-    """HB not a multiple of 8, or at most 3 pairs per XCD: rank major (longest block first) over all pairs."""
-    for HB, nqb in ((7, 4), (24, 5), (12, 3)):
+    """HB not a multiple of 8, or fewer than 2 g pairs per XCD: rank major (longest block first) over all
+    pairs."""
+    for HB, nqb in ((7, 4), (24, 5), (12, 3), (24, 64), (128, 8)):
         order = _order(exe, HB, nqb)
         assert [(r, p) for _, r, p in order] == [(i // HB, i % HB) for i in range(HB * nqb)]
