@@ -10,10 +10,13 @@
 // at a time, the more of those reads its L2 serves.  When the pairs divide evenly among the XCDs
 // (HB = 8 PX), XCD x takes pairs x, x + 8, ..., x + 8 (PX - 1) and runs them in groups, longest block
 // first (rank order) inside each group:
-//   - its first g pairs together and its last g pairs together, g = max(2, ceil(128 / nb)) for nb blocks
-//     per pair: the groups at the ends fill the XCD's 64 workgroup slots at the start and let the last
-//     long blocks start early enough at the end (a lone last pair's longest blocks would set the
-//     kernel's end); the fewer blocks a pair has, the more pairs that takes;
+//   - its first g pairs together and its last g pairs together: the groups at the ends fill the XCD's 64
+//     workgroup slots at the start and let the last long blocks start early enough at the end (a lone
+//     last pair's longest blocks would set the kernel's end).  With nb blocks per pair (the longest
+//     2 nb key tiles, a pair about nb^2), an XCD's 64 slots each hold about PX nb / 128 longest blocks
+//     of work: at 8 or more (PX nb >= 1024) the end is short against the whole and g = 2 keeps the most
+//     locality; below that g = max(2, ceil(128 / nb)), so that the last group alone holds one longest
+//     block's time of work per slot;
 //   - every pair in between alone.
 // With fewer than 2 g pairs per XCD, or pairs that do not divide by 8, the items go rank major over all
 // pairs: the order of a single group.
@@ -30,7 +33,8 @@ struct WorkItem {
 // item in [0, HB * nb); HB = number of (sequence, head) pairs, nb = blocks per pair
 constexpr WorkItem work_item(int item, int HB, int nb) {
   const int PX = HB >> 3;
-  const int g = (128 + nb - 1) / nb < 2 ? 2 : (128 + nb - 1) / nb;   // pairs in each end group
+  const int gt = (128 + nb - 1) / nb;
+  const int g = (PX * nb >= 1024 || gt < 2) ? 2 : gt;   // pairs in each end group
   if ((HB & 7) != 0 || PX < 2 * g) return WorkItem{item / HB, item % HB};
   const int x = item & 7, j = item >> 3;
   const int e0 = g * nb, e1 = (PX - g) * nb;   // end of the first group, start of the last

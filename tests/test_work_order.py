@@ -71,9 +71,10 @@ def _order(exe, HB, nqb):
 
 
 def _expected_xcd_order(x, PX, nb):
-    """The groups the header describes, for XCD x: g = max(2, ceil(128 / nb)) pairs at each end run together
-    (rank by rank, the group's pairs in turn), every pair in between alone (rank by rank)."""
-    g = max(2, -(-128 // nb))
+    """The groups the header describes, for XCD x: g pairs at each end run together (rank by rank, the
+    group's pairs in turn), every pair in between alone (rank by rank); g = 2 when PX nb >= 1024, else
+    max(2, ceil(128 / nb))."""
+    g = 2 if PX * nb >= 1024 else max(2, -(-128 // nb))
     if PX < 2 * g:
         groups = [list(range(PX))]
     else:
@@ -81,10 +82,11 @@ def _expected_xcd_order(x, PX, nb):
     return [(r, x + 8 * p) for grp in groups for r in range(nb) for p in grp]
 
 
-@pytest.mark.parametrize("PX,nb", [(5, 64), (9, 32), (40, 8), (7, 3), (4, 64), (64, 72)])
+@pytest.mark.parametrize("PX,nb", [(5, 64), (9, 32), (40, 8), (7, 3), (4, 64), (64, 72), (64, 32), (16, 64), (128, 8)])
 def test_groups_listed(exe, PX, nb):
     """Each XCD's list of items follows the end-group rule (e.g. 5 pairs of 64 blocks: the first two
-    interleaved, the middle one alone, the last two interleaved; 9 pairs of 32 blocks: groups of 4)."""
+    interleaved, the middle one alone, the last two interleaved; 9 pairs of 32 blocks: groups of 4;
+    64 pairs of 32 blocks, deep enough for groups of 2)."""
     order = _order(exe, 8 * PX, nb)
     for x in (0, 3, 7):
         assert [(r, p) for i, r, p in order if i % 8 == x] == _expected_xcd_order(x, PX, nb), (PX, nb, x)
@@ -93,6 +95,6 @@ def test_groups_listed(exe, PX, nb):
 def test_few_pairs_keep_rank_major(exe):
     """HB not a multiple of 8, or fewer than 2 g pairs per XCD: rank major (longest block first) over all
     pairs."""
-    for HB, nqb in ((7, 4), (24, 5), (12, 3), (24, 64), (128, 8)):
+    for HB, nqb in ((7, 4), (24, 5), (12, 3), (24, 64), (128, 8), (504, 4)):
         order = _order(exe, HB, nqb)
         assert [(r, p) for _, r, p in order] == [(i // HB, i % HB) for i in range(HB * nqb)]
