@@ -10,7 +10,7 @@ import pytest
 from hstu_sequential_transduction_attn_amd import inputs as I
 from oracle import hstu_oracle as O
 
-from _util import dev, host, jag_dev, max_abs, oracle_jag, rel_l2
+from _util import assert_close, dev, host, jag_dev, max_abs, oracle_jag, rel_l2
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -117,6 +117,37 @@ def test_bwd_deterministic_and_bins_consistent():
         assert np.array_equal(x, y), f"{name} differs between runs"
     # every allowed pair lands in one position bin and one time bin
     np.testing.assert_allclose(a[3].sum(axis=1), a[4].sum(axis=1), rtol=1e-4, atol=1e-5)
+
+
+def test_bwd_xcd_grouped_work_order():
+    """A batch whose (sequence, head) pairs take the XCD-local work order with all three segments:
+    256 sequences x 2 heads = 512 pairs (64 per XCD), at most 8 query blocks per pair, so each XCD runs
+    its first 16 pairs together, the next 32 one at a time and its last 16 together (csrc/work_order.hpp).
+    Both passes run in that order, and the dQ pass stores each workgroup's bias-gradient bins at its
+    query-block-major row: every gradient, the bias tables' included, against the whole oracle, the
+    forward as well, and two runs bitwise equal."""
+    print("\n[case] bwd and fwd in the XCD-grouped work order (256 x 2 pairs)", flush=True)
+    rng = np.random.default_rng(1180)
+    lengths = [int(v) for v in rng.integers(1, 80, size=256)]
+    for i in rng.choice(256, size=10, replace=False):
+        lengths[int(i)] = int(rng.integers(900, 1025))
+    lengths[int(rng.integers(0, 256))] = 1024            # the longest: 8 query blocks per pair
+    case = I.attn_case("bwdx", 1180, lengths, H=2, Dh=32, P=64, Tb=32, dtype="bf16", with_u=False)
+    g = _grad_out(case, 1181)
+    got = _gpu(case, g)
+    _check(got, _oracle(case, g), "bf16", "grouped order")
+    again = _gpu(case, g)
+    for x, y, name in zip(got, again, NAMES):
+        assert np.array_equal(x, y), f"{name} differs between runs"
+    from hstu_sequential_transduction_attn_amd import _lib as ops
+    jd = jag_dev(case.jagged)
+    o = host(ops.attn_fwd(jd["seq_offsets"], jd["timestamps"], dev(case.q), dev(case.k), dev(case.v),
+                          dev(case.rab.pos_bias), dev(case.rab.time_bias), max_seq_len=jd["max_seq_len"]))
+    want = O.attn_fwd(oracle_jag(case.jagged), case.q.values, case.k.values, case.v.values, case.rab.pos_bias,
+                      case.rab.time_bias)
+    # an ad-hoc batch: sequences of 1 to 80 tokens have c_b up to 1 and outputs up to about 20, so the
+    # elementwise bar grows with the value (two bf16 roundings, 2^-7 |want|)
+    assert_close(o, want, "bf16", "forward, grouped order", magnitude_aware=True)
 
 
 def test_bwd_empty_batch_zeroes_the_bias_gradients():

@@ -1,4 +1,4 @@
-"""GPU parity of hstu_layer_fwd (and the gather + stack driver) against the float64 oracle."""
+"""GPU parity of hstu_layer_fwd (and the gather followed by layer-by-layer stacks) against the float64 oracle."""
 import numpy as np
 import pytest
 
