@@ -15,6 +15,7 @@ constexpr int kBM = kWaves * kQW;        // queries per workgroup
 constexpr int kBN = 64;                  // keys per LDS tile
 constexpr int kThreads = kWaves * kWave;
 constexpr int kTimeTab = 65;             // a 64-bit gap has bit length 0..64
+constexpr int kTimeRev = 34;             // forward: the time table by leading-zero count of a 32-bit gap
 constexpr int kPosPad = 8;               // forward: position-table entries past P - 1 (copies of w_p[P-1])
 constexpr int kChunk = 32;               // tokens per timestamp-range chunk
 constexpr int kRingBudget = 68 * 1024;   // LDS for the stage ring: two workgroups per CU
@@ -116,6 +117,7 @@ struct TileCtx {
   float c1;            // -log2(e) * bias of a uniform tile, 0 otherwise
   float bias_lo, bias_hi;          // two-bucket mode: the two biases
   const HSTU_LDS float *wp, *wt;   // bias tables
+  const HSTU_LDS float *wtr;       // forward: wtr[z] = time bias of a 32-bit gap with v_ffbh_u32 = z (-1 for 0)
   const HSTU_LDS char *stage;      // the tile's LDS stage
 };
 

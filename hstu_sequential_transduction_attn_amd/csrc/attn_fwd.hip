@@ -63,6 +63,14 @@ namespace {
 
 using namespace attn;
 
+// Leading zeros of a uint32 in one v_ffbh_u32: 0..31, and -1 (all bits set) for 0, so that a 32-bit gap d
+// has bit length 32 - ffbh(d) for d > 0 and 0 for d = 0
+__device__ __forceinline__ int ffbh_u32(uint32_t d) {
+  int r;
+  asm("v_ffbh_u32 %0, %1" : "=v"(r) : "v"(d));
+  return r;
+}
+
 // |a - b| for uint32 a, b in one v_sad_u32
 __device__ __forceinline__ uint32_t absdiff_u32(uint32_t a, uint32_t b) {
   uint32_t d;
@@ -74,7 +82,8 @@ __device__ __forceinline__ uint32_t absdiff_u32(uint32_t a, uint32_t b) {
 // separate floats, so that the adjusted values stay in the scores' registers); element e holds key
 // k0 + 32*kb + 16*(e/8) + 8*half + e%8.
 // The forward's tables are padded so that no bucket needs a clamp: wp[d] = w_p[min(d, P-1)] for
-// d < P + kPosPad and wt[b] = w_t[min(b, Tb-1)] for every bit length b <= 64.  In a tile whose keys
+// d < P + kPosPad and wt[b] = w_t[min(b, Tb-1)] for every bit length b <= 64; a 32-bit gap reads a second
+// copy of the time table (wtr) by its leading-zero count, which saves the bit length's two instructions.  In a tile whose keys
 // are all allowed, all history and no later than the query's position, the 8 keys of a lane's group
 // have position distances d0 - e8 (d0 = my_pos - first key), so their biases are the 8 consecutive
 // entries wp[d0 - 7 .. d0]; with d0 capped at P + 6 the window stays in the table and, past P - 1,
@@ -116,14 +125,13 @@ __device__ __forceinline__ void adjust_scalar(float (&s)[16], const TileCtx &c, 
           // window's value for a masked key is never used
           if (c.k0 + jl0 + e8 == c.my_q) wpv = c.wp[0];
         }
-        int bt;
         if constexpr (!k64) {
-          bt = bitlen_u32(absdiff_u32(c.qoff, lo[e8] - c.base_lo));
+          // the reversed table takes the leading-zero count directly (no bit length, no clamp)
+          bias = wpv + c.wtr[ffbh_u32(absdiff_u32(c.qoff, lo[e8] - c.base_lo))];
         } else {
           const int64_t tj = (int64_t)(((uint64_t)hi[e8] << 32) | lo[e8]);
-          bt = bitlen_absdiff(c.my_tau, tj);
+          bias = wpv + c.wt[bitlen_absdiff(c.my_tau, tj)];
         }
-        bias = wpv + c.wt[bt];
       }
       if constexpr (kMasked) {
         const int j = c.k0 + jl0 + e8;
@@ -486,6 +494,11 @@ __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_
   HSTU_LDS float *wt_lds = wp_lds + P + (BWD ? 0 : kPosPad);
   for (int i = tid; i < P + (BWD ? 0 : kPosPad); i += kThreads) wp_lds[i] = p.pos_bias[(int64_t)rr * P + imin(i, P - 1)];
   for (int i = tid; i < kTimeTab; i += kThreads) wt_lds[i] = p.time_bias[(int64_t)rr * Tb + imin(i, Tb - 1)];
+  // forward: the time table once more, by leading-zero count of a 32-bit gap (entry 0: a gap of 0; entry
+  // z + 1: a gap with z leading zeros, bit length 32 - z)
+  HSTU_LDS float *wtr_lds = wt_lds + kTimeTab;
+  if constexpr (!BWD)
+    for (int i = tid; i < kTimeRev; i += kThreads) wtr_lds[i] = p.time_bias[(int64_t)rr * Tb + imin(i == 0 ? 0 : 33 - i, Tb - 1)];
 
   // ---- this wave's queries
   const int qr = q0 + wave * kQW;                 // first query row of the wave (a multiple of 32)
@@ -651,6 +664,7 @@ __device__ __forceinline__ void attn_query_major(const AttnArgs &p, const int n_
   c.my_tau = my_tau;
   c.wp = wp_lds;
   c.wt = wt_lds;
+  c.wtr = wtr_lds + 1;
 
   // backward: this wave's bias-gradient bins (after the bias tables), cleared by the wave itself
   GradBins gb{};
@@ -861,7 +875,7 @@ attn_bwd_dq_kernel(const AttnArgs p, const int n_qblocks) {
 template <typename T, int DH, bool BWD>
 size_t attn_lds_bytes(int num_pos_buckets) {
   using L = Layout<T, DH>;
-  const size_t tables = (size_t)(num_pos_buckets + (BWD ? 0 : kPosPad) + kTimeTab) * sizeof(float);
+  const size_t tables = (size_t)(num_pos_buckets + (BWD ? 0 : kPosPad + kTimeRev) + kTimeTab) * sizeof(float);
   return (size_t)L::kStages * L::kStageBytes + tables * (BWD ? 1 + kWaves : 1);
 }
 
