@@ -43,6 +43,8 @@ struct KeyCtx {
   const HSTU_LDS float *wp, *wt;
   const HSTU_LDS char *stage;
   uint32_t base_lo;    // 32-bit mode: low word of the tile's smallest timestamp (all within 2^32 of it)
+  uint32_t thr;        // two-bucket tiles: |dt| >= thr takes bias_hi
+  float bias_lo, bias_hi;
 };
 
 // Bias (and mask) of the 16 scores of 32-query block qb in place; element e holds query
@@ -88,8 +90,32 @@ __device__ __forceinline__ void adjust_block_keys(floatx16 &s, const KeyCtx &c, 
   }
 }
 
-// One 32-query block of a tile for one wave.  body: kUniform (bias c1 folded into the exponent),
-// kGen64 (per-score bias), kGen64M (per-score bias and mask).  Every class shares one copy of the MFMA
+// Bias of the 16 scores of 32-query block qb in a two-bucket tile: every pair is allowed and clamped to
+// position bucket P - 1, and |dt| falls in time bucket blo or blo + 1, told apart by |dt| >= 2^blo; the
+// gaps come from 32-bit offsets of the tile's smallest timestamp (one v_sad_u32 per score).
+template <typename T, int DH>
+__device__ __forceinline__ void adjust_block_keys_two(floatx16 &s, const KeyCtx &c, int qb, int lane) {
+  using L = Layout<T, DH>;
+  const int half = lane >> 5;
+  const uint32_t koff = (uint32_t)(uint64_t)c.ktau[lane & 31] - c.base_lo;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int il0 = 32 * qb + 16 * g + 8 * half;
+    uint32_t lo[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 w = *(const HSTU_LDS u32x4 *)(c.stage + L::tau_at(il0 + 2 * q));
+      lo[2 * q] = w.x;
+      lo[2 * q + 1] = w.z;
+    }
+#pragma unroll
+    for (int e8 = 0; e8 < 8; ++e8)
+      s[8 * g + e8] += __usad(koff, lo[e8] - c.base_lo, 0u) >= c.thr ? c.bias_hi : c.bias_lo;
+  }
+}
+
+// One 32-query block of a tile for one wave.  body: kUniform (bias c1 folded into the exponent), kTwo
+// (two time buckets), kGen32/kGen64 (per-score bias), kGen32M/kGen64M (per-score bias and mask).  Every class shares one copy of the MFMA
 // code, so the dK^T and dV^T accumulators stay in the same registers whatever the class.
 template <typename T, int DH>
 __device__ __forceinline__ void dkdv_block(OAcc<Layout<T, DH>::kDB> &dk, OAcc<Layout<T, DH>::kDB> &dv,
@@ -102,7 +128,8 @@ __device__ __forceinline__ void dkdv_block(OAcc<Layout<T, DH>::kDB> &dk, OAcc<La
   const HSTU_LDS char *lG = c.stage + L::kOffV;
   floatx16 s;
   score_block<T, DH>(s, lQ, qb, l32, half, kf);
-  if (body == kGen32) adjust_block_keys<T, DH, false, true>(s, c, qb, lane);
+  if (body == kTwo) adjust_block_keys_two<T, DH>(s, c, qb, lane);
+  else if (body == kGen32) adjust_block_keys<T, DH, false, true>(s, c, qb, lane);
   else if (body == kGen32M) adjust_block_keys<T, DH, true, true>(s, c, qb, lane);
   else if (body == kGen64) adjust_block_keys<T, DH, false, false>(s, c, qb, lane);
   else if (body == kGen64M) adjust_block_keys<T, DH, true, false>(s, c, qb, lane);
@@ -318,6 +345,12 @@ attn_bwd_dkdv_kernel(const AttnArgs p, const int n_kblocks) {
           if (blo == bhi) {
             body = kUniform;
             c1 = kNegLog2e * (wp_lds[P - 1] + wt_lds[blo]);
+          } else if (bhi == blo + 1 && k32) {
+            body = kTwo;
+            // wave-uniform values read from LDS: held in scalar registers
+            c.thr = 1u << blo;
+            c.bias_lo = readlane_f(wp_lds[P - 1] + wt_lds[blo], 0);
+            c.bias_hi = readlane_f(wp_lds[P - 1] + wt_lds[bhi], 0);
           }
         }
       }
